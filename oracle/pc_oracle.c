@@ -1,0 +1,460 @@
+/*
+ * pc_oracle.c -- plain, slow, fp64 CPU oracle for the paged KV-cache write and
+ * paged decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Tests, the smoke check and the benchmark's CPU
+ * baseline call it; the product library never links, loads or calls it, and it
+ * shares no code, header, table or helper with the GPU path.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  oracle_write   -- "Inside vLLM CUDA Kernels: KV-Cache Writes and Paged
+ *                    Attention", Part 2, sections "Decomposing a Slot into Block
+ *                    and Offset" (negative slot = no destination; block = slot / B,
+ *                    offset = slot % B) and "Why Layout and Quantization Scale
+ *                    Produce Two Copy Paths" (block/page/head strides form the
+ *                    address); "How vLLM CUDA Kernels Write and Read the Paged KV
+ *                    Cache", section "Writing K and V into the cache".  Values are
+ *                    copied as raw bits (the conversion is an identity when the
+ *                    input and cache formats match).
+ *
+ *  oracle_decode  -- per (sequence s, query head h): the dense decode attention of
+ *                    "vLLM 源码完全拆解（七）", section 先明确问题 (one query per (s,h),
+ *                    softmax over the L_s visible tokens, max subtracted for
+ *                    stability), with the head mapping of section 线程组织
+ *                    (kv_head = h / (Hq/Hkv)), and the logical-to-physical walk of
+ *                    "How vLLM CUDA Kernels Write and Read the Paged KV Cache",
+ *                    section "Reading logical blocks during attention"
+ *                    (physical block = block_table[t / B], offset = t % B).  The
+ *                    logical K/V rows are materialised first, then scores
+ *                    x_t = scale * q.k_t, m = max x, p_t = exp(x_t - m),
+ *                    out = sum p_t v_t / sum p_t, all in double.  No epsilon in the
+ *                    denominator; scale is the caller's float widened to double.
+ *
+ *  oracle_partials, oracle_merge -- the split-context form of "vLLM 源码完全拆解
+ *                    （七）", section V1与V2 (512-token partitions; a partition past
+ *                    seq_len does nothing) and the stable merge of "Inside vLLM CUDA
+ *                    Kernels", Part 3, section "How Each K/V Tile Contributes to the
+ *                    Output" (local states rescaled to a common maximum).  A
+ *                    partition stores its own max m_p, exp-sum l_p and normalised
+ *                    output o_p; the merge forms M = max m_p, w_p = l_p e^(m_p - M),
+ *                    out = sum w_p o_p / sum w_p.
+ *
+ * Storage formats: 0 = fp32, 1 = fp16, 2 = bf16 (raw bits in memory).
+ * Return codes: 0 ok, -1 invalid argument, -2 a data value points outside the
+ * pool (slot, block id or sequence length) -- the oracle refuses to read or write
+ * out of range, so a test that passes proves no such access was needed.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+#define OR_ERANGE (-2)
+
+static int esize_of(int fmt) {
+    return fmt == 0 ? 4 : (fmt == 1 || fmt == 2) ? 2 : 0;
+}
+
+/* IEEE binary16 -> double, from the format's definition. */
+static double half_to_double(uint16_t h) {
+    int sign = h >> 15;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of a binary32. */
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double load_elem(const void *base, int64_t idx, int fmt) {
+    if (fmt == 0) {
+        float f;
+        memcpy(&f, (const char *)base + idx * 4, 4);
+        return (double)f;
+    }
+    uint16_t b;
+    memcpy(&b, (const char *)base + idx * 2, 2);
+    return fmt == 1 ? half_to_double(b) : bf16_to_double(b);
+}
+
+/* ------------------------------------------------------------------------- */
+/* write                                                                      */
+/* ------------------------------------------------------------------------- */
+
+int oracle_write(void *k_pool, void *v_pool, int64_t pool_elems, int64_t num_blocks,
+                 int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                 const void *key, const void *value, int64_t key_row_stride, int64_t value_row_stride,
+                 const int64_t *slot_mapping, int64_t num_tokens,
+                 int num_kv_heads, int head_size, int block_size, int fmt) {
+    int es = esize_of(fmt);
+    if (!es || !k_pool || !v_pool || num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0)
+        return OR_EINVAL;
+    if (num_tokens > 0 && (!key || !value || !slot_mapping))
+        return OR_EINVAL;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0)
+            continue; /* padding: no destination */
+        int64_t blk = slot / block_size;
+        int64_t off = slot % block_size;
+        if (blk >= num_blocks)
+            return OR_ERANGE;
+        for (int h = 0; h < num_kv_heads; ++h) {
+            for (int d = 0; d < head_size; ++d) {
+                int64_t dst = blk * block_stride + off * token_stride + (int64_t)h * head_stride + d;
+                if (dst < 0 || dst >= pool_elems)
+                    return OR_ERANGE;
+                int64_t ks = t * key_row_stride + (int64_t)h * head_size + d;
+                int64_t vs = t * value_row_stride + (int64_t)h * head_size + d;
+                memcpy((char *)k_pool + dst * es, (const char *)key + ks * es, (size_t)es);
+                memcpy((char *)v_pool + dst * es, (const char *)value + vs * es, (size_t)es);
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* decode                                                                     */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+    const void *q, *k_pool, *v_pool;
+    int64_t pool_elems, num_blocks, block_stride, token_stride, head_stride;
+    const int32_t *block_tables;
+    int max_blocks_per_seq;
+    const int32_t *seq_lens;
+    int num_seqs, num_q_heads, num_kv_heads, head_size, block_size;
+    double scale;
+    int fmt;
+    int partition_size; /* 0: whole sequence (decode); > 0: partials */
+    int max_partitions;
+    /* outputs */
+    double *out;                                  /* decode: [S, Hq, D] */
+    double *tmp_out, *max_logits, *exp_sums;      /* partials: [S, Hq, P, D], [S, Hq, P] */
+    /* work split */
+    int64_t n_items;
+    int nthreads;
+    int status;
+    pthread_mutex_t lock;
+} job_t;
+
+typedef struct {
+    job_t *job;
+    int tid;
+} worker_arg_t;
+
+/* Materialise the logical rows [t0, t1) of sequence s, kv head kv, as doubles:
+ * block_table[s, t / B] gives the physical block, t % B the row inside it. */
+static int gather_rows(const job_t *j, int s, int kv, int t0, int t1, double *K, double *V) {
+    const int32_t *row = j->block_tables + (int64_t)s * j->max_blocks_per_seq;
+    for (int t = t0; t < t1; ++t) {
+        int lb = t / j->block_size;
+        int off = t % j->block_size;
+        if (lb >= j->max_blocks_per_seq)
+            return OR_ERANGE;
+        int64_t phys = row[lb];
+        if (phys < 0 || phys >= j->num_blocks)
+            return OR_ERANGE;
+        int64_t base = phys * j->block_stride + (int64_t)off * j->token_stride + (int64_t)kv * j->head_stride;
+        if (base < 0 || base + j->head_size > j->pool_elems)
+            return OR_ERANGE;
+        for (int d = 0; d < j->head_size; ++d) {
+            K[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->k_pool, base + d, j->fmt);
+            V[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->v_pool, base + d, j->fmt);
+        }
+    }
+    return OR_OK;
+}
+
+/* Dense softmax attention of one query over n materialised rows.
+ * Writes o[D] = sum p_t v_t / sum p_t, *m = max x_t, *l = sum p_t. */
+static void dense_attention(const double *qv, const double *K, const double *V, int n, int D, double scale,
+                            double *x, double *o, double *m_out, double *l_out) {
+    double m = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+            dot += qv[d] * K[(int64_t)t * D + d];
+        x[t] = scale * dot;
+        if (x[t] > m)
+            m = x[t];
+    }
+    double l = 0.0;
+    for (int t = 0; t < n; ++t) {
+        x[t] = exp(x[t] - m);
+        l += x[t];
+    }
+    for (int d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int t = 0; t < n; ++t)
+            acc += x[t] * V[(int64_t)t * D + d];
+        o[d] = acc / l;
+    }
+    *m_out = m;
+    *l_out = l;
+}
+
+/* One work item = one (s, h) for decode, one (s, h, p) for partials. */
+static int run_item(job_t *j, int64_t item, double *K, double *V, double *x, double *qv) {
+    int D = j->head_size;
+    int G = j->num_q_heads / j->num_kv_heads;
+    int s, h, p = 0;
+    if (j->partition_size > 0) {
+        p = (int)(item % j->max_partitions);
+        h = (int)((item / j->max_partitions) % j->num_q_heads);
+        s = (int)(item / ((int64_t)j->max_partitions * j->num_q_heads));
+    } else {
+        h = (int)(item % j->num_q_heads);
+        s = (int)(item / j->num_q_heads);
+    }
+    int kv = h / G;
+    int L = j->seq_lens[s];
+    if (L < 0 || (int64_t)L > (int64_t)j->max_blocks_per_seq * j->block_size)
+        return OR_ERANGE;
+    for (int d = 0; d < D; ++d)
+        qv[d] = load_elem(j->q, ((int64_t)s * j->num_q_heads + h) * D + d, j->fmt);
+
+    if (j->partition_size == 0) {
+        double *o = j->out + ((int64_t)s * j->num_q_heads + h) * D;
+        if (L == 0) { /* no visible token: defined as zeros */
+            for (int d = 0; d < D; ++d)
+                o[d] = 0.0;
+            return OR_OK;
+        }
+        int rc = gather_rows(j, s, kv, 0, L, K, V);
+        if (rc)
+            return rc;
+        double m, l;
+        dense_attention(qv, K, V, L, D, j->scale, x, o, &m, &l);
+        return OR_OK;
+    }
+
+    int t0 = p * j->partition_size;
+    if (t0 >= L)
+        return OR_OK; /* empty partition: writes nothing */
+    if ((int64_t)L > (int64_t)j->max_partitions * j->partition_size)
+        return OR_ERANGE;
+    int t1 = t0 + j->partition_size < L ? t0 + j->partition_size : L;
+    int rc = gather_rows(j, s, kv, t0, t1, K, V);
+    if (rc)
+        return rc;
+    int64_t sp = ((int64_t)s * j->num_q_heads + h) * j->max_partitions + p;
+    dense_attention(qv, K, V, t1 - t0, D, j->scale, x, j->tmp_out + sp * D, &j->max_logits[sp], &j->exp_sums[sp]);
+    return OR_OK;
+}
+
+static void *worker(void *argp) {
+    worker_arg_t *a = (worker_arg_t *)argp;
+    job_t *j = a->job;
+    /* rows of one materialised range: a partition, or the longest valid sequence */
+    int64_t rows = j->partition_size;
+    if (j->partition_size == 0) {
+        int64_t cap = (int64_t)j->max_blocks_per_seq * j->block_size;
+        rows = 1;
+        for (int s = 0; s < j->num_seqs; ++s)
+            if (j->seq_lens[s] > rows)
+                rows = j->seq_lens[s] < cap ? j->seq_lens[s] : cap;
+    }
+    double *K = (double *)malloc(sizeof(double) * (size_t)rows * (size_t)j->head_size + 8);
+    double *V = (double *)malloc(sizeof(double) * (size_t)rows * (size_t)j->head_size + 8);
+    double *x = (double *)malloc(sizeof(double) * (size_t)rows + 8);
+    double *qv = (double *)malloc(sizeof(double) * (size_t)j->head_size);
+    int rc = OR_OK;
+    if (!K || !V || !x || !qv)
+        rc = OR_EINVAL;
+    for (int64_t it = a->tid; rc == OR_OK && it < j->n_items; it += j->nthreads)
+        rc = run_item(j, it, K, V, x, qv);
+    if (rc) {
+        pthread_mutex_lock(&j->lock);
+        if (!j->status)
+            j->status = rc;
+        pthread_mutex_unlock(&j->lock);
+    }
+    free(K);
+    free(V);
+    free(x);
+    free(qv);
+    return NULL;
+}
+
+static int run_job(job_t *j, int nthreads) {
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    j->nthreads = nthreads;
+    j->status = OR_OK;
+    pthread_mutex_init(&j->lock, NULL);
+    pthread_t th[256];
+    worker_arg_t args[256];
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        args[i].job = j;
+        args[i].tid = i;
+        if (i == 0)
+            continue;
+        if (pthread_create(&th[i], NULL, worker, &args[i]) == 0)
+            started = i;
+        else
+            break;
+    }
+    if (started + 1 < nthreads) {
+        /* could not start every thread: let the caller's thread take every item */
+        for (int i = 1; i <= started; ++i)
+            pthread_join(th[i], NULL);
+        j->nthreads = 1;
+        args[0].tid = 0;
+        worker(&args[0]);
+    } else {
+        worker(&args[0]);
+        for (int i = 1; i < nthreads; ++i)
+            pthread_join(th[i], NULL);
+    }
+    pthread_mutex_destroy(&j->lock);
+    return j->status;
+}
+
+static int check_common(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_tables,
+                        const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
+                        int block_size, int max_blocks_per_seq, int fmt) {
+    if (!esize_of(fmt) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+        block_size <= 0 || max_blocks_per_seq < 0 || num_q_heads % num_kv_heads)
+        return OR_EINVAL;
+    if (num_seqs > 0 && (!q || !k_pool || !v_pool || !block_tables || !seq_lens))
+        return OR_EINVAL;
+    return OR_OK;
+}
+
+int oracle_decode(double *out, const void *q, const void *k_pool, const void *v_pool, int64_t pool_elems,
+                  int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                  const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_size, int block_size, float scale, int fmt,
+                  int nthreads) {
+    int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                          head_size, block_size, max_blocks_per_seq, fmt);
+    if (rc)
+        return rc;
+    if (num_seqs > 0 && !out)
+        return OR_EINVAL;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.q = q;
+    j.k_pool = k_pool;
+    j.v_pool = v_pool;
+    j.pool_elems = pool_elems;
+    j.num_blocks = num_blocks;
+    j.block_stride = block_stride;
+    j.token_stride = token_stride;
+    j.head_stride = head_stride;
+    j.block_tables = block_tables;
+    j.max_blocks_per_seq = max_blocks_per_seq;
+    j.seq_lens = seq_lens;
+    j.num_seqs = num_seqs;
+    j.num_q_heads = num_q_heads;
+    j.num_kv_heads = num_kv_heads;
+    j.head_size = head_size;
+    j.block_size = block_size;
+    j.scale = (double)scale;
+    j.fmt = fmt;
+    j.out = out;
+    j.n_items = (int64_t)num_seqs * num_q_heads;
+    return run_job(&j, nthreads);
+}
+
+int oracle_partials(double *tmp_out, double *max_logits, double *exp_sums, const void *q, const void *k_pool,
+                    const void *v_pool, int64_t pool_elems, int64_t num_blocks, int64_t block_stride,
+                    int64_t token_stride, int64_t head_stride, const int32_t *block_tables, int max_blocks_per_seq,
+                    const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
+                    int block_size, float scale, int partition_size, int max_partitions, int fmt, int nthreads) {
+    int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                          head_size, block_size, max_blocks_per_seq, fmt);
+    if (rc)
+        return rc;
+    if (partition_size <= 0 || max_partitions < 0 || (num_seqs > 0 && (!tmp_out || !max_logits || !exp_sums)))
+        return OR_EINVAL;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.q = q;
+    j.k_pool = k_pool;
+    j.v_pool = v_pool;
+    j.pool_elems = pool_elems;
+    j.num_blocks = num_blocks;
+    j.block_stride = block_stride;
+    j.token_stride = token_stride;
+    j.head_stride = head_stride;
+    j.block_tables = block_tables;
+    j.max_blocks_per_seq = max_blocks_per_seq;
+    j.seq_lens = seq_lens;
+    j.num_seqs = num_seqs;
+    j.num_q_heads = num_q_heads;
+    j.num_kv_heads = num_kv_heads;
+    j.head_size = head_size;
+    j.block_size = block_size;
+    j.scale = (double)scale;
+    j.fmt = fmt;
+    j.partition_size = partition_size;
+    j.max_partitions = max_partitions;
+    j.tmp_out = tmp_out;
+    j.max_logits = max_logits;
+    j.exp_sums = exp_sums;
+    j.n_items = (int64_t)num_seqs * num_q_heads * max_partitions;
+    return run_job(&j, nthreads);
+}
+
+/* Merge the partials of the ceil(L_s / partition_size) partitions that hold tokens.
+ * A sequence with no token gets zeros. */
+int oracle_merge(double *out, const double *tmp_out, const double *max_logits, const double *exp_sums,
+                 const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_size, int max_partitions,
+                 int partition_size) {
+    if (num_seqs < 0 || num_q_heads <= 0 || head_size <= 0 || max_partitions < 0 || partition_size <= 0)
+        return OR_EINVAL;
+    if (num_seqs > 0 && (!out || !tmp_out || !max_logits || !exp_sums || !seq_lens))
+        return OR_EINVAL;
+    for (int s = 0; s < num_seqs; ++s) {
+        int L = seq_lens[s];
+        if (L < 0)
+            return OR_ERANGE;
+        int np_ = (int)(((int64_t)L + partition_size - 1) / partition_size);
+        if (np_ > max_partitions)
+            return OR_ERANGE;
+        for (int h = 0; h < num_q_heads; ++h) {
+            int64_t sh = (int64_t)s * num_q_heads + h;
+            double *o = out + sh * head_size;
+            double M = -INFINITY;
+            for (int p = 0; p < np_; ++p)
+                if (max_logits[sh * max_partitions + p] > M)
+                    M = max_logits[sh * max_partitions + p];
+            double wsum = 0.0;
+            for (int d = 0; d < head_size; ++d)
+                o[d] = 0.0;
+            for (int p = 0; p < np_; ++p) {
+                double w = exp_sums[sh * max_partitions + p] * exp(max_logits[sh * max_partitions + p] - M);
+                wsum += w;
+                const double *op = tmp_out + (sh * max_partitions + p) * head_size;
+                for (int d = 0; d < head_size; ++d)
+                    o[d] += w * op[d];
+            }
+            if (np_ > 0)
+                for (int d = 0; d < head_size; ++d)
+                    o[d] /= wsum;
+        }
+    }
+    return OR_OK;
+}

@@ -1,0 +1,456 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``pin_*`` function raises ``AssertionError`` (or ``oracle.OracleError``) when
+the oracle disagrees with something it does not compute itself:
+
+* worked values printed on the pages (``tests/golden/*.json``, each cites its page);
+* closed forms (one visible token, q = 0, identical keys, two tokens, huge logits);
+* invariants (any physical placement of the blocks, unread memory, padding rows);
+* independent references (numpy and torch float64 dense attention on the contiguous
+  history, a tile-wise online softmax, a pure-Python per-token brute force);
+* the split identity (per-partition partials merged = the whole sequence).
+
+``tests/test_oracle_pins.py`` runs them; ``tests/test_oracle_mutants.py`` plants
+mistakes in copies of the oracle and requires some pin to fail for each.
+"""
+
+from __future__ import annotations
+
+import functools
+import json
+import math
+import os
+from types import SimpleNamespace
+
+import numpy as np
+
+import brute
+import oracle
+from helpers import GOLDEN, bits_to_f64, dense_numpy, f64_to_bits, online_tiles_numpy
+from workloads import custom, make_config, nan_bits
+
+B = 16
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+@functools.lru_cache(maxsize=None)
+def _cfg(idx, contents=True):
+    return make_config(idx, contents=contents)
+
+
+def hand_wl(dtype, Hq, Hkv, D, num_blocks, block_tables, seq_lens, q_f64):
+    """A hand-built HND workload ([num_blocks, Hkv, B, D] per buffer)."""
+    wl = SimpleNamespace(dtype=dtype, num_seqs=len(seq_lens), num_q_heads=Hq, num_kv_heads=Hkv, head_size=D,
+                         block_size=B, layout="hnd", num_blocks=num_blocks, block_stride=Hkv * B * D,
+                         token_stride=D, head_stride=B * D, v_offset=0, pool_elems=num_blocks * Hkv * B * D,
+                         seq_lens=np.asarray(seq_lens, np.int32),
+                         block_tables=np.asarray(block_tables, np.int32).reshape(len(seq_lens), -1),
+                         scale=np.float32(1.0 / math.sqrt(D)), q=f64_to_bits(np.asarray(q_f64), dtype))
+    bits = np.uint32 if dtype == "f32" else np.uint16
+    wl.nan_pool = lambda: np.full(wl.pool_elems, nan_bits(dtype), dtype=bits)
+    return wl
+
+
+def hand_pool(wl, K, V):
+    """Pool image from per-physical-slot rows K, V shaped [num_blocks, B, Hkv, D] (float64);
+    the HND buffer is [num_blocks, Hkv, B, D]."""
+    k = f64_to_bits(np.ascontiguousarray(np.transpose(K, (0, 2, 1, 3))), wl.dtype).reshape(-1)
+    v = f64_to_bits(np.ascontiguousarray(np.transpose(V, (0, 2, 1, 3))), wl.dtype).reshape(-1)
+    return oracle.Pool(k, v, 0, wl.pool_elems)
+
+
+def _rounded(x, dtype):
+    return bits_to_f64(f64_to_bits(x, dtype), dtype)
+
+
+# ---------------------------------------------------------------------------------
+# worked examples printed on the pages
+# ---------------------------------------------------------------------------------
+
+def pin_slot_write():
+    """Slot 36 of the worked example lands at physical block 2, offset 4, and nowhere else."""
+    g = _golden("slot_example.json")
+    Hkv, D = 2, 8
+    wl = hand_wl("f32", Hkv, Hkv, D, 10, [g["block_table"]], [g["position"] + 1], np.zeros((1, Hkv, D)))
+    pool = oracle.empty_pool(wl)
+    key = f64_to_bits(np.arange(1, Hkv * D + 1, dtype=float).reshape(1, Hkv, D), "f32")
+    value = f64_to_bits(-np.arange(1, Hkv * D + 1, dtype=float).reshape(1, Hkv, D), "f32")
+    oracle.write(wl, pool, key, value, np.array([g["slot"]], np.int64))
+    for arr, row in ((pool.k, key[0]), (pool.v, value[0])):
+        img = arr.reshape(10, Hkv, B, D)
+        assert np.array_equal(img[g["physical_block"], :, g["offset"], :], row)
+        rest = np.ones(img.shape, bool)
+        rest[g["physical_block"], :, g["offset"], :] = False
+        assert (img[rest] == nan_bits("f32")).all()
+
+
+def _saturating_read(g, position_key, length_key, target_block, target_offset, table):
+    """All keys zero except one physical slot whose key scores 50 against q: the output
+    is that slot's value row iff the read resolves the position to that slot."""
+    D = 8
+    rng = np.random.default_rng(1)
+    wl = hand_wl("f32", 1, 1, D, 10, [table], [g[length_key]], rng.standard_normal((1, 1, D)))
+    qv = bits_to_f64(wl.q, "f32")[0, 0]
+    scale = float(wl.scale)
+    K = np.zeros((10, B, 1, D))
+    V = _rounded(rng.standard_normal((10, B, 1, D)), "f32")
+    K[target_block, target_offset, 0] = qv * (50.0 / (scale * float(qv @ qv)))
+    pool = hand_pool(wl, K, V)
+    out = oracle.decode(wl, pool)[0, 0]
+    assert np.abs(out - V[target_block, target_offset, 0]).max() < 1e-12
+    # one token shorter: the target position is not visible, every score is 0, and the
+    # output is the plain mean of the rows the table maps positions 0..L-2 to
+    L = g[length_key] - 1
+    out2 = oracle.decode(wl, pool, seq_lens=np.array([L], np.int32))[0, 0]
+    rows = [V[table[t // B], t % B, 0] for t in range(L)]
+    assert np.abs(out2 - np.mean(rows, axis=0)).max() < 1e-13
+    assert np.abs(out2 - V[target_block, target_offset, 0]).max() > 1e-3
+
+
+def pin_slot_read():
+    """Position 20 under block_table [7, 2, 9] is read from physical block 2, offset 4."""
+    g = _golden("slot_example.json")
+    g = dict(g, seq_len=g["position"] + 1)
+    _saturating_read(g, "position", "seq_len", g["physical_block"], g["offset"], g["block_table"])
+
+
+def pin_invariant_line():
+    """seq_len 17 with block_table [7, 2]: logical token 16 is physical block 2, offset 0."""
+    g = _golden("invariant_example.json")
+    _saturating_read(g, "logical_token", "seq_len", g["physical_block"], g["offset"], g["block_table"])
+
+
+def pin_gqa_mapping():
+    """Query head h reads KV head h / (Hq / Hkv) (printed examples)."""
+    g = _golden("gqa_examples.json")
+    for case in g["cases"]:
+        Hq, Hkv, D = case["num_q_heads"], case["num_kv_heads"], 8
+        rng = np.random.default_rng(2)
+        wl = hand_wl("f32", Hq, Hkv, D, 2, [[1]], [5], rng.standard_normal((1, Hq, D)))
+        K = _rounded(rng.standard_normal((2, B, Hkv, D)), "f32")
+        V = np.zeros((2, B, Hkv, D))
+        for kv in range(Hkv):
+            V[:, :, kv, :] = kv + 1.0  # every value row of KV head kv is (kv + 1)
+        out = oracle.decode(wl, hand_pool(wl, K, V))[0]
+        for h, kv in case["pairs"]:
+            assert np.abs(out[h] - (kv + 1.0)).max() < 1e-14, (h, kv, out[h][:2])
+
+
+def pin_worked_decode():
+    """8 query heads / 2 KV heads, seq_len 35 over [7, 2, 9]: query head 5 reads KV head 1
+    and position 34 sits in physical block 9, offset 2."""
+    g = _golden("worked_decode.json")
+    Hq, Hkv, D = g["num_q_heads"], g["num_kv_heads"], g["head_size"]
+    rng = np.random.default_rng(3)
+    wl = hand_wl("bf16", Hq, Hkv, D, 10, [g["block_table"]], [g["seq_len"]], rng.standard_normal((1, Hq, D)))
+    q = bits_to_f64(wl.q, "bf16")[0]
+    K = np.zeros((10, B, Hkv, D))
+    V = _rounded(rng.standard_normal((10, B, Hkv, D)), "bf16")
+    pb = g["last_block_tokens"]["physical_block"]
+    off = g["last_block_tokens"]["offsets"][-1]
+    qh = q[g["query_head"]]
+    K[pb, off, g["kv_head"]] = _rounded(qh * (60.0 / (float(wl.scale) * float(qh @ qh))), "bf16")
+    out = oracle.decode(wl, hand_pool(wl, K, V))[0]
+    assert np.abs(out[g["query_head"]] - V[pb, off, g["kv_head"]]).max() < 1e-9
+    # heads of KV head 0 saw only zero keys: the plain mean of the 35 rows of KV head 0
+    rows = [V[g["block_table"][t // B], t % B, 0] for t in range(g["seq_len"])]
+    for h in range(Hq // Hkv):
+        assert np.abs(out[h] - np.mean(rows, axis=0)).max() < 1e-13
+
+
+def pin_combined_block_layout():
+    """tiny-vllm's combined block: V_OFFSET 16384 B, 32768 B blocks, 65536 blocks in 2 GiB,
+    128 blocks per 2048-token sequence; bytes land where its address rule says."""
+    g = _golden("combined_block_constants.json")
+    w = _cfg(2, contents=False)
+    assert w.v_offset * w.esize == g["v_offset_bytes"]
+    assert w.block_stride * w.esize == g["block_bytes"]
+    assert w.num_blocks == g["num_blocks"] == g["cache_bytes"] // g["block_bytes"]
+    assert w.block_tables.shape[1] == g["max_blocks_per_seq"] == g["max_seq_len"] // g["block_size"]
+    assert w.num_kv_heads * w.head_size == g["kv_dim"]
+    assert 2 * 16 * g["max_blocks_per_seq"] == g["block_table_entries_2_seqs_16_layers"]
+    small = custom(0, "bf16", 32, 8, 64, [5], layout="combined", pool_factor=3.0)
+    pool = oracle.empty_pool(small)
+    rng = np.random.default_rng(4)
+    key = f64_to_bits(rng.standard_normal((1, 8, 64)), "bf16")
+    value = f64_to_bits(rng.standard_normal((1, 8, 64)), "bf16")
+    blk, tok = 2, 3
+    oracle.write(small, pool, key, value, np.array([blk * B + tok], np.int64))
+    raw = pool.k.view(np.uint8)
+    for h in range(8):
+        for d in range(64):
+            a = blk * g["block_bytes"] + tok * g["kv_dim"] * 2 + h * g["head_dim"] * 2 + d * 2
+            assert raw[a:a + 2].view(np.uint16)[0] == key[0, h, d]
+            a += g["v_offset_bytes"]
+            assert raw[a:a + 2].view(np.uint16)[0] == value[0, h, d]
+
+
+# ---------------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------------
+
+def pin_one_token_exact():
+    """One visible token: the output is that token's value row, exactly."""
+    for dt in ("f32", "bf16", "f16"):
+        w = custom(3, dt, 4, 2, 64, [1, 1, 1])
+        out = oracle.decode(w, oracle.filled_pool(w))
+        for s in range(3):
+            for h in range(4):
+                assert np.array_equal(out[s, h], bits_to_f64(w.logical_v(s)[0, h // 2], dt)), (dt, s, h)
+
+
+def pin_special_values_exact():
+    """Format decoding: subnormals, zeros, the largest finite values and ordinary
+    normals come back exactly through a one-token read (a zero's sign is not kept:
+    the weighted sum starts from +0)."""
+    specials = {
+        "f16": [0x0001, 0x03FF, 0x0400, 0x8001, 0x8000, 0x7BFF, 0xFBFF, 0x3C00, 0x3555, 0xC800],
+        "bf16": [0x0001, 0x007F, 0x0080, 0x8001, 0x8000, 0x7F7F, 0xFF7F, 0x3F80, 0x3EAB, 0xC120],
+        "f32": [0x00000001, 0x007FFFFF, 0x00800000, 0x80000001, 0x80000000, 0x7F7FFFFF, 0xFF7FFFFF,
+                0x3F800000, 0x3EAAAAAB, 0xC1200000],
+    }
+    for dt, pats in specials.items():
+        D = 64
+        w = custom(20, dt, 1, 1, D, [1])
+        row = np.resize(np.array(pats, dtype=w.bits_dtype), D)
+        w.key[0, 0, :] = row
+        w.bank_v[w.logical_src[0][0], 0, :] = row
+        w.value[0, 0, :] = row
+        out = oracle.decode(w, oracle.filled_pool(w))[0, 0]
+        expect = bits_to_f64(row, dt)
+        assert np.array_equal(out, expect), dt
+
+
+def pin_zero_query_mean():
+    """q = 0: every score is 0 and the output is the mean of the visible value rows."""
+    w = custom(4, "bf16", 8, 2, 64, [1, 7, 33, 100])
+    out = oracle.decode(w, oracle.filled_pool(w), q=np.zeros_like(w.q))
+    for s in range(w.num_seqs):
+        V = bits_to_f64(w.logical_v(s), "bf16")
+        for h in range(8):
+            assert np.abs(out[s, h] - V[:, h // 4].mean(axis=0)).max() < 1e-13
+
+
+def pin_equal_keys_mean():
+    """All keys identical: uniform softmax, the output is the mean of the value rows."""
+    w = custom(5, "f16", 4, 4, 128, [3, 40, 64])
+    w.pre_key[:] = w.key[0]
+    w.key[:] = w.key[0]
+    out = oracle.decode(w, oracle.filled_pool(w))
+    for s in range(w.num_seqs):
+        V = bits_to_f64(w.logical_v(s), "f16")
+        for h in range(4):
+            assert np.abs(out[s, h] - V[:, h].mean(axis=0)).max() < 1e-13
+
+
+def _sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+def pin_two_tokens_sigmoid():
+    """Two tokens: out = sigma(x0 - x1) v0 + sigma(x1 - x0) v1, x_t = scale q.k_t."""
+    w = custom(6, "f32", 4, 2, 64, [2, 2])
+    out = oracle.decode(w, oracle.filled_pool(w))
+    sc = float(w.scale)
+    q = bits_to_f64(w.q, "f32")
+    for s in range(2):
+        K = bits_to_f64(w.logical_k(s), "f32")
+        V = bits_to_f64(w.logical_v(s), "f32")
+        for h in range(4):
+            kv = h // 2
+            x0 = sc * math.fsum(q[s, h] * K[0, kv])
+            x1 = sc * math.fsum(q[s, h] * K[1, kv])
+            exp = _sig(x0 - x1) * V[0, kv] + _sig(x1 - x0) * V[1, kv]
+            assert np.abs(out[s, h] - exp).max() < 1e-14
+
+
+def pin_huge_logits():
+    """Scores near 800 overflow exp() unless the running maximum is subtracted first."""
+    D = 8
+    q = np.zeros((1, 1, D))
+    q[0, 0, 0] = 1.0
+    wl = hand_wl("f32", 1, 1, D, 1, [[0]], [2], q)
+    K = np.zeros((1, B, 1, D))
+    K[0, 0, 0, 0] = 2262.75
+    K[0, 1, 0, 0] = 2234.5
+    rng = np.random.default_rng(5)
+    V = _rounded(rng.standard_normal((1, B, 1, D)), "f32")
+    out = oracle.decode(wl, hand_pool(wl, K, V))[0, 0]
+    sc = float(wl.scale)
+    x0, x1 = sc * 2262.75, sc * 2234.5
+    assert x0 > 790 and x1 > 780
+    exp = _sig(x0 - x1) * V[0, 0, 0] + _sig(x1 - x0) * V[0, 1, 0]
+    assert np.isfinite(out).all() and np.abs(out - exp).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------------
+
+def pin_placement_invariance():
+    """Any physical arrangement of the blocks gives exactly the same output."""
+    args = (11, "bf16", 8, 2, 64, [1, 17, 40, 64, 100])
+    outs, tables = [], []
+    for pl in (None, "identity", 123, 456):
+        w = custom(*args, placement=pl)
+        tables.append(w.block_tables)
+        outs.append(oracle.decode(w, oracle.filled_pool(w)))
+    assert not np.array_equal(tables[0], tables[1]) and not np.array_equal(tables[2], tables[3])
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def pin_negative_slot_skipped():
+    """A negative slot has no destination: the pool is left byte-identical, and the
+    filled pool holds exactly the valid tokens (the padding row landed nowhere)."""
+    w = _cfg(0)
+    pool = oracle.filled_pool(w, step_write=False)
+    before = [a.copy() for a in pool.arrays()]
+    oracle.write(w, pool, w.key, w.value, np.full(len(w.slot_mapping), -1, np.int64))
+    assert all(np.array_equal(b, a) for b, a in zip(before, pool.arrays()))
+    pool = oracle.filled_pool(w)
+    written = sum(int((a != nan_bits(w.dtype)).sum()) for a in pool.arrays())
+    assert written == 2 * int(w.seq_lens.sum()) * w.num_kv_heads * w.head_size
+
+
+def pin_unread_memory():
+    """Memory outside the visible tokens (block tails, unused blocks) is never read:
+    overwriting it with other values leaves the output bit-identical and finite."""
+    for w in (_cfg(0), custom(18, "bf16", 8, 2, 64, [1, 17, 31]), custom(21, "f16", 4, 4, 64, [2, 47], layout="nhd")):
+        pool = oracle.filled_pool(w)
+        out = oracle.decode(w, pool)
+        assert np.isfinite(out).all()
+        garbage = f64_to_bits(np.array([1.0e4]), w.dtype)[0]
+        for a in pool.arrays():
+            a[a == nan_bits(w.dtype)] = garbage
+        assert np.array_equal(oracle.decode(w, pool), out)
+
+
+def pin_table_padding():
+    """Entries past ceil(L/B) are padding (-1) and never dereferenced; a length that
+    would need them is refused."""
+    w = custom(19, "f32", 4, 4, 64, [3, 40], table_width=8)
+    assert (w.block_tables == -1).sum() >= 8
+    pool = oracle.filled_pool(w)
+    oracle.decode(w, pool)
+    for bad in (17, 8 * B + 1):
+        sl = w.seq_lens.copy()
+        sl[0] = bad
+        try:
+            oracle.decode(w, pool, seq_lens=sl)
+        except oracle.OracleError:
+            continue
+        raise AssertionError(f"seq_len {bad} over a padded row was accepted")
+
+
+def pin_write_out_of_range():
+    """A slot past the pool is refused rather than written."""
+    w = _cfg(0)
+    pool = oracle.empty_pool(w)
+    try:
+        oracle.write(w, pool, w.key[:1], w.value[:1], np.array([w.num_blocks * B], np.int64))
+    except oracle.OracleError:
+        return
+    raise AssertionError("out-of-range slot accepted")
+
+
+# ---------------------------------------------------------------------------------
+# independent references
+# ---------------------------------------------------------------------------------
+
+def _ref_cases():
+    return [
+        _cfg(0),
+        custom(7, "bf16", 32, 8, 128, [1, 15, 16, 17, 100, 511, 513]),
+        custom(8, "f16", 8, 8, 128, [3, 200]),
+        custom(9, "bf16", 32, 8, 64, [1, 2, 1000], layout="combined"),
+        custom(10, "f32", 8, 2, 64, [5, 64], layout="nhd"),
+        custom(22, "f16", 16, 4, 128, [40, 70], prefix_blocks=2, pad_count=1),
+    ]
+
+
+def pin_numpy_dense():
+    """numpy softmax(scale q K^T) V on the contiguous history agrees to 1e-12."""
+    for w in _ref_cases():
+        out = oracle.decode(w, oracle.filled_pool(w))
+        assert np.abs(out - dense_numpy(w)).max() < 1e-12, w.name
+
+
+def pin_torch_sdpa():
+    """torch scaled_dot_product_attention in float64 on the CPU agrees to 1e-12."""
+    import torch
+    w = custom(12, "bf16", 16, 4, 64, [1, 9, 130])
+    out = oracle.decode(w, oracle.filled_pool(w))
+    G = w.num_q_heads // w.num_kv_heads
+    q = torch.from_numpy(bits_to_f64(w.q, w.dtype))
+    for s in range(w.num_seqs):
+        K = torch.from_numpy(bits_to_f64(w.logical_k(s), w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        V = torch.from_numpy(bits_to_f64(w.logical_v(s), w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[s].unsqueeze(1).unsqueeze(0), K.unsqueeze(0),
+                                                               V.unsqueeze(0), scale=float(w.scale))
+        assert (ref[0, :, 0, :].numpy() - out[s]).__abs__().max() < 1e-12
+
+
+def pin_online_tiles():
+    """A tile-wise online softmax (running max/sum/accumulator) agrees to 1e-12."""
+    w = custom(16, "bf16", 32, 8, 128, [1, 16, 17, 300])
+    out = oracle.decode(w, oracle.filled_pool(w))
+    assert np.abs(out - online_tiles_numpy(w)).max() < 1e-12
+
+
+def pin_brute_force():
+    """A pure-Python per-token walk of the block table agrees to 1e-12."""
+    cases = [_cfg(0), custom(13, "bf16", 4, 2, 64, [1, 16, 17, 33]), custom(14, "f16", 2, 1, 64, [20]),
+             custom(15, "bf16", 4, 2, 64, [5, 30], layout="combined")]
+    for w in cases:
+        pool = oracle.filled_pool(w)
+        out = oracle.decode(w, pool)
+        ref = np.array(brute.paged_decode(w, pool.k, pool.v, pool.v_offset))
+        assert np.abs(out - ref).max() < 1e-12, w.name
+
+
+# ---------------------------------------------------------------------------------
+# the split identity
+# ---------------------------------------------------------------------------------
+
+def pin_split_identity():
+    """Partials of P-token partitions, merged by log-sum-exp, equal the whole-sequence
+    result; partitions past seq_len are left untouched; each partial is dense
+    attention over its own token range."""
+    w = custom(17, "f32", 4, 2, 64, [1, 15, 16, 17, 511, 512, 513, 1100])
+    pool = oracle.filled_pool(w)
+    dense = oracle.decode(w, pool)
+    q = bits_to_f64(w.q, w.dtype)
+    sc = float(w.scale)
+    for P in (16, 32, 48, 512):
+        tmp, ml, es = oracle.partials(w, pool, P)
+        for s in range(w.num_seqs):
+            L = int(w.seq_lens[s])
+            n = -(-L // P)
+            assert np.isnan(ml[s, :, n:]).all() and np.isnan(tmp[s, :, n:]).all()
+            assert np.isfinite(ml[s, :, :n]).all() and np.isfinite(tmp[s, :, :n]).all()
+            if s == w.num_seqs - 1:  # spot-check each partial of the longest sequence
+                K = bits_to_f64(w.logical_k(s), w.dtype)
+                V = bits_to_f64(w.logical_v(s), w.dtype)
+                for p in range(n):
+                    for h in (0, 3):
+                        x = sc * (K[p * P:(p + 1) * P, h // 2] @ q[s, h])
+                        e = np.exp(x - x.max())
+                        assert abs(ml[s, h, p] - x.max()) < 1e-13
+                        assert abs(es[s, h, p] - e.sum()) < 1e-12 * e.sum()
+                        assert np.abs(tmp[s, h, p] - e @ V[p * P:(p + 1) * P, h // 2] / e.sum()).max() < 1e-13
+        merged = oracle.merge(tmp, ml, es, w.seq_lens, P)
+        assert np.abs(merged - dense).max() < 1e-13, P
+
+
+PINS = [
+    pin_slot_write, pin_slot_read, pin_invariant_line, pin_gqa_mapping, pin_worked_decode,
+    pin_combined_block_layout, pin_one_token_exact, pin_special_values_exact, pin_zero_query_mean,
+    pin_equal_keys_mean, pin_two_tokens_sigmoid, pin_huge_logits, pin_placement_invariance,
+    pin_negative_slot_skipped, pin_unread_memory, pin_table_padding, pin_write_out_of_range,
+    pin_numpy_dense, pin_torch_sdpa, pin_online_tiles, pin_brute_force, pin_split_identity,
+]

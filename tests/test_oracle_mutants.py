@@ -1,0 +1,78 @@
+"""Planted mistakes in the oracle must be caught by the pins (CPU only).
+
+Each mutant is a copy of ``oracle/pc_oracle.c`` with one plausible mistake (a
+wrong index, a dropped term, a swapped stride, an off-by-one), compiled to a
+temporary library.  The pins run against it; at least one must fail.  Mistakes are
+only ever planted in the oracle, on the CPU.
+"""
+
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "pc_oracle.c")
+
+MUTANTS = {
+    "gqa_modulo": ("int kv = h / G;", "int kv = h % j->num_kv_heads;"),
+    "slot_offset_shift": ("int64_t off = slot % block_size;", "int64_t off = (slot + 1) % block_size;"),
+    "slot_block_divisor": ("int64_t blk = slot / block_size;", "int64_t blk = slot / (block_size + 1);"),
+    "write_strides_swapped": ("int64_t dst = blk * block_stride + off * token_stride + (int64_t)h * head_stride + d;",
+                              "int64_t dst = blk * block_stride + off * head_stride + (int64_t)h * token_stride + d;"),
+    "negative_slot_written": ("if (slot < 0)\n            continue;", "if (slot < -1)\n            continue;"),
+    "read_logical_block": ("int lb = t / j->block_size;", "int lb = t / (2 * j->block_size);"),
+    "read_offset_shift": ("int off = t % j->block_size;", "int off = (t + 1) % j->block_size;"),
+    "value_from_key_pool": ("V[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->v_pool, base + d, j->fmt);",
+                            "V[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->k_pool, base + d, j->fmt);"),
+    "query_head_swapped": ("qv[d] = load_elem(j->q, ((int64_t)s * j->num_q_heads + h) * D + d, j->fmt);",
+                           "qv[d] = load_elem(j->q, ((int64_t)s * j->num_q_heads + (h ^ 1)) * D + d, j->fmt);"),
+    "scale_dropped": ("x[t] = scale * dot;", "x[t] = dot;"),
+    "max_not_subtracted": ("x[t] = exp(x[t] - m);", "x[t] = exp(x[t]);"),
+    "epsilon_denominator": ("o[d] = acc / l;", "o[d] = acc / (l + 1e-6);"),
+    "last_token_dropped": ("dense_attention(qv, K, V, L, D, j->scale, x, o, &m, &l);",
+                           "dense_attention(qv, K, V, L > 1 ? L - 1 : L, D, j->scale, x, o, &m, &l);"),
+    "partition_not_clipped": ("int t1 = t0 + j->partition_size < L ? t0 + j->partition_size : L;",
+                              "int t1 = t0 + j->partition_size;"),
+    "merge_without_rescale": (
+        "double w = exp_sums[sh * max_partitions + p] * exp(max_logits[sh * max_partitions + p] - M);",
+        "double w = exp_sums[sh * max_partitions + p];"),
+    "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "f16_exponent_bias": ("v = ldexp((double)(m + 1024), e - 25);", "v = ldexp((double)(m + 1024), e - 24);"),
+    "f16_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+}
+
+
+def _build_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation site for {name} is not unique/present"
+    src = tmp_path / f"{name}.c"
+    src.write_text(text.replace(old, new))
+    out = tmp_path / f"{name}.so"
+    oracle.build(force=True, src=str(src), out=str(out))
+    return str(out)
+
+
+def _failures():
+    failed = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, oracle.OracleError, FloatingPointError):
+            failed.append(pin.__name__)
+    return failed
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _failures() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    path = _build_mutant(name, tmp_path)
+    with oracle.using(path):
+        failed = _failures()
+    assert failed, f"planted mistake '{name}' passed every pin"
