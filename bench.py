@@ -1,0 +1,228 @@
+"""Benchmark: one decode step of the paged KV-cache hot path on one MI355X.
+
+A step is the whole path over one batch: the write of each sequence's new token
+into the paged pool (pc_reshape_and_cache), the planner, and the decode (one pass,
+or the 512-token split plus its log-sum-exp reduce).  The default workload is
+64 sequences of 512..2048 tokens, 32 query / 8 KV heads, head size 128, bf16, one
+pass (the GQA decode the throughput target is quoted on).
+
+Inputs are resident in HBM before timing starts.  To keep the K/V stream honest
+with respect to the 256 MB last-level cache, the step rotates over ``--copies``
+independent copies of the pool (default: enough that more than 1 GiB of other K/V
+is read between two visits of one copy); ``warm_cache`` reports the same step on
+one copy back to back.
+
+Prints ONE JSON line.  ``value`` is effective GB/s over the whole step: K/V bytes
+of exactly seq_len tokens per sequence plus q and out, divided by the step time.
+``roofline`` is the decode kernel alone: the same algorithmic bytes per launch over
+its average launch time, measured with HIP events on the launch stream around every
+launch in the timed region.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+for p in (REPO, os.path.join(REPO, "tests")):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+METRIC = "paged decode attention effective GB/s and % of MI355X HBM peak; tokens/s"
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(REPO, "profiles", "decode_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (1 = the headline workload)")
+    ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate over (0 = auto, >1 GiB apart)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--path", choices=["plan", "single", "split"], default="plan")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(REPO, "paged_kv_cache_reshape_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds: float):
+    """The fp64 oracle on the host: the step's write plus the decode of the whole batch,
+    repeated until about ``seconds`` of wall time have passed."""
+    import oracle
+    threads = min(os.cpu_count() or 1, 16)
+    pool = oracle.filled_pool(wl, step_write=False)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.write(wl, pool, wl.key, wl.value, wl.slot_mapping)
+        oracle.decode(wl, pool, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": round(wl.effective_bytes() * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} full steps (write + fp64 decode of all {wl.num_seqs} sequences) of the same workload "
+                      f"in {el:.1f} s on {threads} host threads",
+            "tokens_per_s": round(wl.num_seqs * reps / el, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path runs per GPU with no "
+              "exchange between GPUs, so run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gpu_harness as gh
+    import paged_kv_cache_reshape_amd as pc
+    from workloads import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
+    wl = make_config(args.config)
+    S, Hq, D = wl.q.shape
+    per_copy = 2 * wl.pool_elems * wl.esize if wl.layout != "combined" else wl.pool_elems * wl.esize
+    copies = args.copies or max(1, min(8, -(-(1 << 30) // max(1, wl.kv_bytes())) + 1))
+    copies = max(1, min(copies, int(64e9 // per_copy)))
+    print(f"[bench] {wl.name}: {wl.kv_bytes() / 1e6:.1f} MB K/V per step, {copies} pool copies", file=sys.stderr,
+          flush=True)
+    pools = []
+    for _ in range(copies):
+        pools.append(gh.filled_pool(wl, step_write=False))
+    inp = gh.DecodeInputs(wl)
+    key = gh.to_dev(wl.key, wl.dtype)
+    value = gh.to_dev(wl.value, wl.dtype)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    out = torch.empty_like(inp.q)
+    msl = inp.max_seq_len
+    if args.path == "plan":
+        ps, P, _ = pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, gh.TORCH_DT[wl.dtype])
+    elif args.path == "split":
+        ps, P = pc.PARTITION_SIZE, -(-msl // pc.PARTITION_SIZE)
+    else:
+        ps, P = 0, 1
+    path = "split" if ps else "single"
+    if ps:
+        es = torch.empty((S, Hq, P), device=dev)
+        ml = torch.empty((S, Hq, P), device=dev)
+        tmp = torch.empty((S, Hq, P, D), device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        pool = pools[i % copies]
+        kw = pool.layout_kwargs()
+        pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **kw)
+        pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, gh.TORCH_DT[wl.dtype])
+        if ev is not None:
+            ev[0].record(stream)
+        if ps:
+            pc.paged_attention_decode(None, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), partition_size=ps,
+                                      exp_sums=es, max_logits=ml, tmp_out=tmp, **kw)
+            if ev is not None:
+                ev[1].record(stream)
+            pc.paged_attention_reduce(out, es, ml, tmp, inp.seq_lens)
+            if ev is not None:
+                ev[2].record(stream)
+        else:
+            pc.paged_attention_decode(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **kw)
+            if ev is not None:
+                ev[1].record(stream)
+
+    def timed(n, rotate=True):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            step(i if rotate else 0, evs[i])
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        dec = [e[0].elapsed_time(e[1]) for e in evs]
+        red = [e[1].elapsed_time(e[2]) for e in evs] if ps else [0.0] * n
+        return el, dec, red
+
+    for i in range(args.warmup):
+        step(i)
+    print(f"[bench] warmup done, timing {args.steps} steps ({path} path)", file=sys.stderr, flush=True)
+    el, dec, red = timed(args.steps)
+    for i in range(3):
+        step(0)
+    wel, wdec, _ = timed(args.steps, rotate=False)
+
+    eff = wl.effective_bytes()
+    ms = el / args.steps * 1e3
+    dec_ms = sum(dec) / len(dec)
+    red_ms = sum(red) / len(red)
+    achieved = eff / (dec_ms * 1e-3) / 1e9
+    traffic = stored_traffic(wl.name)
+    res = {
+        "metric": METRIC,
+        "value": round(eff / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads,
+                   "head_size": D, "block_size": wl.block_size, "layout": wl.layout, "path": path,
+                   "max_seq_len": msl, "kv_bytes_per_step": wl.kv_bytes(), "effective_bytes_per_step": eff,
+                   "pool_copies": copies},
+        "tokens_per_s": round(S / (ms * 1e-3), 1),
+        "us_per_call": round(ms * 1e3, 2),
+        "hbm_frac_step": round(eff / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_kernel_us": round(dec_ms * 1e3, 2),
+        "reduce_kernel_us": round(red_ms * 1e3, 2) if ps else None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel (one pass)" if not ps else "decode_kernel (split)",
+                     "bytes_per_launch": eff},
+        "warm_cache": {"ms_per_step": round(wel / args.steps * 1e3, 5),
+                       "decode_kernel_us": round(sum(wdec) / len(wdec) * 1e3, 2),
+                       "value": round(eff / (wel / args.steps) / 1e9, 2)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

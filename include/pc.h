@@ -1,0 +1,200 @@
+/*
+ * pc.h -- C ABI of the paged KV-cache library for AMD Instinct MI355X (gfx950).
+ *
+ * Three operations form the data-parallel hot path of a paged KV cache at decode
+ * time, plus a host-only planner:
+ *
+ *   pc_reshape_and_cache       scatter each new token's K/V rows into a pool of
+ *                              fixed-size physical blocks through slot_mapping;
+ *   pc_paged_attention_decode  for every (sequence, query head): walk the block
+ *                              table, gather K/V, scaled q.k scores, online softmax,
+ *                              softmax . V -- either in one pass, or per 512-token
+ *                              partition writing partial results;
+ *   pc_paged_attention_reduce  merge the partitions' partial results (log-sum-exp);
+ *   pc_paged_attention_plan    choose between the one-pass and the split path.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every data pointer is a DEVICE pointer (hipMalloc'd or equivalent),
+ *   except the out-parameters of pc_paged_attention_plan, which are host pointers.
+ *   The caller owns every buffer, allocates the split workspace (sizes from
+ *   pc_paged_attention_plan) and keeps it alive until the stream has executed the
+ *   call.  The library allocates no memory and keeps no state beyond a cached
+ *   device-property query.
+ * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).  All
+ *   device work is enqueued on it and nothing waits for it; a write followed by a
+ *   decode on the same stream sees the written tokens.
+ * Storage types.  q, out, key/value rows and the pool share one storage type
+ *   (pc_dtype); arithmetic is fp32 throughout (scores, softmax statistics and the
+ *   value accumulator); out is rounded to nearest-even from fp32.
+ * Pool layout.  A pool is described by ELEMENT strides (block_stride,
+ *   token_stride, head_stride); the head_size dimension is contiguous.  Examples:
+ *     HND  [num_blocks, num_kv_heads, block_size, head_size]:
+ *          {Hkv*B*D, D, B*D}   (the layout this library is tuned for)
+ *     NHD  [num_blocks, block_size, num_kv_heads, head_size]:
+ *          {B*Hkv*D, Hkv*D, D}
+ *     one buffer per block holding K for B tokens then V for B tokens
+ *     ("Splitting the KV cache into 16-token blocks", section "What one block
+ *     holds"): v_pool = k_pool + B*Hkv*D elements, strides {2*B*Hkv*D, Hkv*D, D}.
+ *   K and V use the same strides.  Element addresses are formed in 64 bits.
+ * Alignment.  The kernels move 16-byte vectors: pool bases, q, key/value rows,
+ *   and every stride times the element size must be multiples of 16 bytes, and
+ *   head_size * element size a multiple of 16 (else PC_ERR_UNSUPPORTED).
+ * Errors.  Arguments are validated on the host before anything is enqueued; a
+ *   failing check returns a negative status and launches nothing.  Data values
+ *   (slots, block ids, lengths) live in device memory and are checked by the
+ *   kernels: an out-of-range slot is skipped like a negative one; a sequence
+ *   whose length exceeds its table row (or max_seq_len on the split path) or
+ *   whose table names a block outside [0, num_blocks) gets NaN in every output
+ *   element of its heads instead of an out-of-bounds read.
+ * Concurrency.  Calls on different streams that write the same pool slots or
+ *   outputs race; slot_mapping must not name one slot twice in a call.
+ */
+#ifndef PC_H
+#define PC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type shared by q, out, key/value and the pool. */
+typedef enum { PC_F32 = 0, PC_F16 = 1, PC_BF16 = 2 } pc_dtype;
+
+/* Status codes. */
+#define PC_OK 0
+#define PC_ERR_INVALID_ARG (-1) /* a null pointer, negative size, or inconsistent sizes */
+#define PC_ERR_UNSUPPORTED (-2) /* a valid request this build has no kernel for */
+#define PC_ERR_LAUNCH (-3)      /* the HIP runtime refused the launch */
+
+/* Tokens per partition on the split path. */
+#define PC_PARTITION_SIZE 512
+
+/* Version of this ABI (bumped on any signature change). */
+int pc_abi_version(void);
+
+/* Short static description of a status code. */
+const char *pc_status_string(int status);
+
+/*
+ * pc_reshape_and_cache -- write new K/V rows into the paged pool.
+ *
+ * Defined by "Inside vLLM CUDA Kernels: KV-Cache Writes and Paged Attention",
+ * Part 2, sections "Decomposing a Slot into Block and Offset" and "Why Layout and
+ * Quantization Scale Produce Two Copy Paths", and "How vLLM CUDA Kernels Write
+ * and Read the Paged KV Cache", section "Writing K and V into the cache": token t
+ * goes to slot = slot_mapping[t]; a negative slot means the token has no
+ * destination (padding) and nothing is written; otherwise block = slot /
+ * block_size, offset = slot % block_size, and for every kv head h and dimension d
+ *     k_pool[block*block_stride + offset*token_stride + h*head_stride + d]
+ *         = key[t*key_row_stride + h*head_size + d]
+ * and the same for value into v_pool.  Bits are copied unchanged (no rounding,
+ * NaN payloads survive).
+ *
+ *   key, value        device, rows of num_kv_heads*head_size elements, row t at
+ *                     t*key_row_stride / t*value_row_stride elements
+ *   k_pool, v_pool    device pool bases (may lie in one buffer, see Pool layout)
+ *   num_blocks        physical blocks in the pool; slots >= num_blocks*block_size
+ *                     are skipped
+ *   slot_mapping      device int64 [num_tokens]
+ *   block_size        tokens per physical block (any positive value)
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ * num_tokens == 0 is a valid no-op.
+ */
+int pc_reshape_and_cache(const void *key, const void *value, int64_t key_row_stride, int64_t value_row_stride,
+                         void *k_pool, void *v_pool, int64_t num_blocks, int64_t block_stride,
+                         int64_t token_stride, int64_t head_stride, const int64_t *slot_mapping,
+                         int64_t num_tokens, int num_kv_heads, int head_size, int block_size, int dtype,
+                         void *stream);
+
+/*
+ * pc_paged_attention_decode -- one query token per sequence against its paged
+ * history.
+ *
+ * Defined by "vLLM 源码完全拆解（七）: PagedAttention Kernel", sections
+ * 先明确问题 (decode attention of query head h of sequence s over its L_s visible
+ * tokens), 线程组织 (query head h reads kv head h / (num_q_heads/num_kv_heads)),
+ * 第一步 (positions >= seq_len take no part), V1与V2 (512-token partitions, a
+ * partition past seq_len does nothing), and "Inside vLLM CUDA Kernels", Part 3,
+ * section "How Each K/V Tile Contributes to the Output" (scores = q.k * scale,
+ * online softmax with running max, sum and accumulator, output acc / l).  Logical
+ * token t of sequence s lives in physical block block_tables[s*max_blocks_per_seq
+ * + t/16] at offset t%16 ("How vLLM CUDA Kernels Write and Read the Paged KV
+ * Cache", section "Reading logical blocks during attention").
+ *
+ *   out               device [num_seqs, num_q_heads, head_size] (one-pass path only)
+ *   q                 device [num_seqs, num_q_heads, head_size], contiguous
+ *   k_pool, v_pool    device pool bases; num_blocks and strides as for the write
+ *   block_tables      device int32 [num_seqs, max_blocks_per_seq]; entries past
+ *                     ceil(seq_len/16) are never read (padding, e.g. -1)
+ *   seq_lens          device int32 [num_seqs]; must include this step's token
+ *   max_seq_len       host-known upper bound of seq_lens (sizes the split grid)
+ *   num_q_heads       multiple of num_kv_heads; num_q_heads/num_kv_heads in {1,2,4,8}
+ *   head_size         64 or 128
+ *   block_size        16
+ *   scale             multiplies q.k (typically 1/sqrt(head_size))
+ *   partition_size    0: one pass, writes out.  PC_PARTITION_SIZE: split path,
+ *                     writes only exp_sums, max_logits and tmp_out; follow with
+ *                     pc_paged_attention_reduce on the same stream.
+ *   exp_sums          device fp32 [num_seqs, num_q_heads, P] with
+ *   max_logits        P = ceil(max_seq_len / partition_size): per partition, the
+ *   tmp_out           sum of exp(score - max), the max score (natural-log domain)
+ *                     and the normalised partial output [.., P, head_size].
+ *                     Partitions past a sequence's length are not written.
+ *                     All three must be NULL when partition_size == 0.
+ * A sequence with seq_len 0 gets zeros (one pass) or no partials (split).
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ */
+int pc_paged_attention_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+                              int64_t num_blocks, int64_t block_stride, int64_t token_stride,
+                              int64_t head_stride, const int32_t *block_tables, int max_blocks_per_seq,
+                              const int32_t *seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
+                              int num_kv_heads, int head_size, int block_size, float scale, int partition_size,
+                              float *exp_sums, float *max_logits, float *tmp_out, int dtype, void *stream);
+
+/*
+ * pc_paged_attention_reduce -- merge the split path's partials.
+ *
+ * Defined by "Inside vLLM CUDA Kernels", Part 3, section "How Each K/V Tile
+ * Contributes to the Output" (partial states rescaled to a common maximum before
+ * merging) and "vLLM 源码完全拆解（七）", section V1与V2 (a second kernel merges
+ * the partitions).  For each (s, h), over the n = ceil(seq_len/partition_size)
+ * partitions that hold tokens: M = max max_logits, w_p = exp_sums_p *
+ * exp(max_logits_p - M), out = sum_p w_p tmp_out_p / sum_p w_p.  Only those n
+ * partitions are read.  seq_len 0 gives zeros; n > max_num_partitions gives NaN.
+ *
+ *   out                device [num_seqs, num_q_heads, head_size], storage dtype
+ *   exp_sums ...       device fp32, as written by pc_paged_attention_decode
+ *   max_num_partitions P of the decode call; partition_size PC_PARTITION_SIZE
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ */
+int pc_paged_attention_reduce(void *out, const float *exp_sums, const float *max_logits, const float *tmp_out,
+                              const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_size,
+                              int max_num_partitions, int partition_size, int dtype, void *stream);
+
+/*
+ * pc_paged_attention_plan -- pick the decode path for a batch (host only, no
+ * device work).
+ *
+ * The pages' rule of thumb trades the one-pass path's idle compute units when
+ * sequences are few and long against the split path's extra launch and partial
+ * traffic ("vLLM 源码完全拆解（七）", section V1与V2).  This planner counts work
+ * units of one (sequence, kv head) -- every query head of a group is computed
+ * from one read of its K/V -- against the GPU's compute units.
+ *
+ *   partition_size      out: 0 (one pass) or PC_PARTITION_SIZE (split)
+ *   max_num_partitions  out: P for the split path (1 for one pass)
+ *   workspace_bytes     out: bytes of exp_sums + max_logits + tmp_out the split
+ *                       path needs (0 for one pass)
+ * Any out-pointer may be NULL.  Returns PC_OK or PC_ERR_INVALID_ARG.
+ */
+int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_size, int max_seq_len,
+                            int dtype, int *partition_size, int *max_num_partitions, size_t *workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PC_H */

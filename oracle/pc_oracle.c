@@ -116,15 +116,14 @@ int oracle_write(void *k_pool, void *v_pool, int64_t pool_elems, int64_t num_blo
         if (blk >= num_blocks)
             return OR_ERANGE;
         for (int h = 0; h < num_kv_heads; ++h) {
-            for (int d = 0; d < head_size; ++d) {
-                int64_t dst = blk * block_stride + off * token_stride + (int64_t)h * head_stride + d;
-                if (dst < 0 || dst >= pool_elems)
-                    return OR_ERANGE;
-                int64_t ks = t * key_row_stride + (int64_t)h * head_size + d;
-                int64_t vs = t * value_row_stride + (int64_t)h * head_size + d;
-                memcpy((char *)k_pool + dst * es, (const char *)key + ks * es, (size_t)es);
-                memcpy((char *)v_pool + dst * es, (const char *)value + vs * es, (size_t)es);
-            }
+            /* the head_size elements of one head are contiguous on both sides */
+            int64_t dst = blk * block_stride + off * token_stride + (int64_t)h * head_stride;
+            if (dst < 0 || dst + head_size > pool_elems)
+                return OR_ERANGE;
+            int64_t ks = t * key_row_stride + (int64_t)h * head_size;
+            int64_t vs = t * value_row_stride + (int64_t)h * head_size;
+            memcpy((char *)k_pool + dst * es, (const char *)key + ks * es, (size_t)head_size * es);
+            memcpy((char *)v_pool + dst * es, (const char *)value + vs * es, (size_t)head_size * es);
         }
     }
     return OR_OK;

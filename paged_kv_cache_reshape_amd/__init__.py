@@ -1,0 +1,23 @@
+"""MI355X-native paged KV-cache write and paged decode attention.
+
+The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
+``include/pc.h``); this package only binds it.  Entry points mirror the C names:
+
+* ``reshape_and_cache``        -- scatter new K/V rows through ``slot_mapping``;
+* ``paged_attention_decode``   -- one-pass decode, or the 512-token split partials;
+* ``paged_attention_reduce``   -- log-sum-exp merge of the partials;
+* ``paged_attention_plan``     -- the planner's choice between the two paths.
+"""
+
+from ._native import (  # noqa: F401
+    LIB_PATH,
+    PARTITION_SIZE,
+    PagedCacheError,
+    abi_version,
+    library,
+    paged_attention_decode,
+    paged_attention_plan,
+    paged_attention_reduce,
+    reshape_and_cache,
+    status_string,
+)

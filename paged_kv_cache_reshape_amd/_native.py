@@ -1,0 +1,181 @@
+"""ctypes binding of ``libpcache.so`` (the C ABI in ``include/pc.h``).
+
+Argument marshalling only: torch tensors are reduced to device pointers, sizes and
+the current HIP stream, and every step runs in the library's kernels.  There is
+no CPU fallback -- a missing library raises at import of this module's functions.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpcache.so")
+
+PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED, PC_ERR_LAUNCH = 0, -1, -2, -3
+PARTITION_SIZE = 512
+_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_lib = None
+
+
+class PagedCacheError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({status_string(status)})")
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build() or "
+                               "python -m paged_kv_cache_reshape_amd.build)")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, i32, f32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        lib.pc_abi_version.restype = i32
+        lib.pc_abi_version.argtypes = []
+        lib.pc_status_string.restype = ctypes.c_char_p
+        lib.pc_status_string.argtypes = [i32]
+        lib.pc_reshape_and_cache.restype = i32
+        lib.pc_reshape_and_cache.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, i64, i64, vp, i64, i32, i32, i32,
+                                             i32, vp]
+        lib.pc_paged_attention_decode.restype = i32
+        lib.pc_paged_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32,
+                                                  i32, i32, i32, f32, i32, vp, vp, vp, i32, vp]
+        lib.pc_paged_attention_reduce.restype = i32
+        lib.pc_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.pc_paged_attention_plan.restype = i32
+        lib.pc_paged_attention_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
+                                                ctypes.POINTER(i32), ctypes.POINTER(sz)]
+        _lib = lib
+    return _lib
+
+
+def library():
+    """The loaded ``ctypes.CDLL`` (raises if the library has not been built)."""
+    return _load()
+
+
+def abi_version() -> int:
+    return _load().pc_abi_version()
+
+
+def status_string(status: int) -> str:
+    return _load().pc_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != PC_OK:
+        raise PagedCacheError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported storage dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _ptr(t, elem_offset: int = 0):
+    if t is None:
+        return None
+    return t.data_ptr() + elem_offset * t.element_size()
+
+
+def _stream(t: torch.Tensor, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _same_device(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must live on the GPU")
+        dev = dev or t.device
+        if t.device != dev:
+            raise ValueError("tensors on different devices")
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                      slot_mapping: torch.Tensor, *, num_blocks: int, block_stride: int, token_stride: int,
+                      head_stride: int, block_size: int = 16, v_offset: int = 0, stream=None) -> None:
+    """Scatter ``key``/``value`` [T, Hkv, D] into the pool through ``slot_mapping`` (int64 [T]).
+    ``v_offset`` places V that many elements past ``v_pool``'s start (one-buffer layouts)."""
+    _same_device(key, value, k_pool, v_pool, slot_mapping)
+    if key.dim() != 3 or value.shape != key.shape or key.stride(2) != 1 or value.stride(2) != 1 or \
+            key.stride(1) != key.shape[2] or value.stride(1) != value.shape[2]:
+        raise ValueError("key/value must be [T, Hkv, D] with contiguous rows")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous() or slot_mapping.numel() != key.shape[0]:
+        raise ValueError("slot_mapping must be a contiguous int64 [T]")
+    dt = _dtype_code(key)
+    for t in (value, k_pool, v_pool):
+        if _DTYPES.get(t.dtype) != dt:
+            raise TypeError("key, value and the pool must share one storage dtype")
+    T, Hkv, D = key.shape
+    st = _load().pc_reshape_and_cache(_ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(k_pool),
+                                      _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride, head_stride,
+                                      _ptr(slot_mapping), T, Hkv, D, block_size, dt, _stream(key, stream))
+    _check("pc_reshape_and_cache", st)
+
+
+def paged_attention_decode(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, *,
+                           num_kv_heads: int, scale: float, num_blocks: int, block_stride: int, token_stride: int,
+                           head_stride: int, block_size: int = 16, v_offset: int = 0, partition_size: int = 0,
+                           exp_sums=None, max_logits=None, tmp_out=None, stream=None) -> None:
+    """Decode attention of ``q`` [S, Hq, D] over the paged pool.  ``partition_size`` 0 writes
+    ``out``; 512 writes only the partials (``exp_sums``, ``max_logits`` [S, Hq, P], ``tmp_out``
+    [S, Hq, P, D], fp32)."""
+    _same_device(out, q, k_pool, v_pool, block_tables, seq_lens, exp_sums, max_logits, tmp_out)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [S, Hq, D]")
+    if out is not None and (out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype):
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous int32 [S, W]")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [S]")
+    for t in (exp_sums, max_logits, tmp_out):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("partials must be contiguous float32")
+    dt = _dtype_code(q)
+    if _DTYPES.get(k_pool.dtype) != dt or _DTYPES.get(v_pool.dtype) != dt:
+        raise TypeError("q and the pool must share one storage dtype")
+    S, Hq, D = q.shape
+    st = _load().pc_paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
+        head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads,
+        D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), dt,
+        _stream(q, stream))
+    _check("pc_paged_attention_decode", st)
+
+
+def paged_attention_reduce(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,
+                           tmp_out: torch.Tensor, seq_lens: torch.Tensor, *, partition_size: int = PARTITION_SIZE,
+                           stream=None) -> None:
+    """Merge partials [S, Hq, P(, D)] into ``out`` [S, Hq, D]."""
+    _same_device(out, exp_sums, max_logits, tmp_out, seq_lens)
+    if tmp_out.dim() != 4 or not (out.is_contiguous() and tmp_out.is_contiguous() and exp_sums.is_contiguous()
+                                  and max_logits.is_contiguous()):
+        raise ValueError("contiguous out [S,Hq,D] and partials [S,Hq,P(,D)] expected")
+    S, Hq, P, D = tmp_out.shape
+    st = _load().pc_paged_attention_reduce(_ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out),
+                                           _ptr(seq_lens), S, Hq, D, P, partition_size, _dtype_code(out),
+                                           _stream(out, stream))
+    _check("pc_paged_attention_reduce", st)
+
+
+def paged_attention_plan(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_size: int, max_seq_len: int,
+                         dtype: torch.dtype):
+    """(partition_size, max_num_partitions, workspace_bytes) chosen by the library's planner."""
+    ps, mp, ws = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_size_t(0)
+    st = _load().pc_paged_attention_plan(num_seqs, num_q_heads, num_kv_heads, head_size, max_seq_len,
+                                         _DTYPES[dtype], ctypes.byref(ps), ctypes.byref(mp), ctypes.byref(ws))
+    _check("pc_paged_attention_plan", st)
+    return ps.value, mp.value, ws.value

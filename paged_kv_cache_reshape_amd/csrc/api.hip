@@ -1,0 +1,179 @@
+// api.hip -- the C entry points declared in include/pc.h: argument validation on
+// the host (nothing is enqueued when a check fails), then one or two launches on
+// the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <mutex>
+
+#include "launch.h"
+#include "pc.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kBlockTokens = 16;
+
+int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool strides16(int es, std::initializer_list<int64_t> strides) {
+  for (int64_t s : strides)
+    if ((s * es) % 16 != 0) return false;
+  return true;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? PC_OK : PC_ERR_LAUNCH; }
+
+// Compute units of the current device, cached per device; MI355X's 256 when no
+// device can be queried (the planner is usable without a GPU).
+int compute_units() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pc_abi_version(void) { return kAbiVersion; }
+
+const char* pc_status_string(int status) {
+  switch (status) {
+    case PC_OK: return "ok";
+    case PC_ERR_INVALID_ARG: return "invalid argument";
+    case PC_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PC_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pc_reshape_and_cache(const void* key, const void* value, int64_t key_row_stride, int64_t value_row_stride,
+                         void* k_pool, void* v_pool, int64_t num_blocks, int64_t block_stride, int64_t token_stride,
+                         int64_t head_stride, const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                         int head_size, int block_size, int dtype, void* stream) {
+  const int es = esize(dtype);
+  if (!es || num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      block_stride <= 0 || token_stride <= 0 || head_stride <= 0 || key_row_stride < 0 || value_row_stride < 0)
+    return PC_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PC_OK;
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PC_ERR_INVALID_ARG;
+  if ((int64_t)num_kv_heads * head_size > key_row_stride && num_tokens > 1) return PC_ERR_INVALID_ARG;
+  if ((int64_t)num_kv_heads * head_size > value_row_stride && num_tokens > 1) return PC_ERR_INVALID_ARG;
+  if (num_tokens > INT_MAX || num_blocks > INT64_MAX / block_size) return PC_ERR_UNSUPPORTED;
+  const bool vec16 = aligned16(key) && aligned16(value) && aligned16(k_pool) && aligned16(v_pool) &&
+                     strides16(es, {key_row_stride, value_row_stride, block_stride, token_stride, head_stride,
+                                    (int64_t)head_size});
+  pcache::WriteArgs a{key,        value,        key_row_stride, value_row_stride, k_pool,     v_pool,
+                      num_blocks, block_stride, token_stride,   head_stride,      slot_mapping, num_tokens,
+                      num_kv_heads, head_size,  block_size};
+  return status_of(pcache::launch_write(a, dtype, vec16, static_cast<hipStream_t>(stream)));
+}
+
+int pc_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool, int64_t num_blocks,
+                              int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+                              int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
+                              int block_size, float scale, int partition_size, float* exp_sums, float* max_logits,
+                              float* tmp_out, int dtype, void* stream) {
+  const int es = esize(dtype);
+  if (!es || num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_size <= 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0)
+    return PC_ERR_INVALID_ARG;
+  const bool split = partition_size != 0;
+  if (split && partition_size != PC_PARTITION_SIZE) return partition_size < 0 ? PC_ERR_INVALID_ARG : PC_ERR_UNSUPPORTED;
+  if (split) {
+    if (!exp_sums || !max_logits || !tmp_out) return PC_ERR_INVALID_ARG;
+  } else if (exp_sums || max_logits || tmp_out) {
+    return PC_ERR_INVALID_ARG;
+  }
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return PC_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PC_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || (!split && !out)) return PC_ERR_INVALID_ARG;
+  if (num_blocks <= 0 || block_stride <= 0 || token_stride <= 0 || head_stride <= 0) return PC_ERR_INVALID_ARG;
+  if (block_size != kBlockTokens) return PC_ERR_UNSUPPORTED;
+  if (!pcache::decode_supported(dtype, head_size, num_q_heads / num_kv_heads)) return PC_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !strides16(es, {block_stride, token_stride, head_stride, (int64_t)head_size}))
+    return PC_ERR_UNSUPPORTED;
+  const int parts = split ? (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE : 1;
+  if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX) return PC_ERR_UNSUPPORTED;
+  if (split && parts == 0) return PC_OK;  // every sequence is empty: no partials exist
+  pcache::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_blocks = num_blocks;
+  a.block_stride = block_stride;
+  a.token_stride = token_stride;
+  a.head_stride = head_stride;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.max_partitions = parts;
+  a.exp_sums = exp_sums;
+  a.max_logits = max_logits;
+  a.tmp_out = tmp_out;
+  return status_of(pcache::launch_decode(a, dtype, head_size, split, static_cast<hipStream_t>(stream)));
+}
+
+int pc_paged_attention_reduce(void* out, const float* exp_sums, const float* max_logits, const float* tmp_out,
+                              const int32_t* seq_lens, int num_seqs, int num_q_heads, int head_size,
+                              int max_num_partitions, int partition_size, int dtype, void* stream) {
+  if (!esize(dtype) || num_seqs < 0 || num_q_heads <= 0 || head_size <= 0 || max_num_partitions < 0 ||
+      partition_size <= 0)
+    return PC_ERR_INVALID_ARG;
+  if (partition_size != PC_PARTITION_SIZE) return PC_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PC_OK;
+  if (!out || !seq_lens || (max_num_partitions > 0 && (!exp_sums || !max_logits || !tmp_out)))
+    return PC_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * num_q_heads > INT_MAX) return PC_ERR_UNSUPPORTED;
+  pcache::ReduceArgs a{out, exp_sums, max_logits, tmp_out, seq_lens, num_seqs, num_q_heads, head_size,
+                       max_num_partitions, partition_size};
+  return status_of(pcache::launch_reduce(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_size, int max_seq_len,
+                            int dtype, int* partition_size, int* max_num_partitions, size_t* workspace_bytes) {
+  if (!esize(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || max_seq_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return PC_ERR_INVALID_ARG;
+  const int parts = (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE;
+  // One (sequence, kv head) unit per workgroup on the one-pass path.  With fewer
+  // units than compute units the one-pass path leaves CUs idle while the long
+  // units stream their history; the split path multiplies the units by the
+  // partition count at the cost of a second launch and the partials' traffic.
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const bool split = parts > 1 && units < compute_units();
+  const int ps = split ? PC_PARTITION_SIZE : 0;
+  const int mp = split ? parts : 1;
+  if (partition_size) *partition_size = ps;
+  if (max_num_partitions) *max_num_partitions = mp;
+  if (workspace_bytes)
+    *workspace_bytes = split ? (size_t)num_seqs * num_q_heads * mp * ((size_t)head_size + 2) * sizeof(float) : 0;
+  return PC_OK;
+}
+
+}  // extern "C"

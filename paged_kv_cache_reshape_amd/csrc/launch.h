@@ -1,0 +1,54 @@
+// launch.h -- host-side launchers shared by the C entry points (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pcache {
+
+struct WriteArgs {
+  const void* key;
+  const void* value;
+  int64_t key_row_stride, value_row_stride;  // elements
+  void* k_pool;
+  void* v_pool;
+  int64_t num_blocks, block_stride, token_stride, head_stride;  // elements
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int num_kv_heads, head_size, block_size;
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  int64_t num_blocks, block_stride, token_stride, head_stride;  // elements
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* seq_lens;
+  int num_seqs, num_q_heads, num_kv_heads;
+  float scale_log2;    // scale * log2(e): scores are kept in the base-2 domain
+  int max_partitions;  // split path only
+  float* exp_sums;
+  float* max_logits;
+  float* tmp_out;
+};
+
+struct ReduceArgs {
+  void* out;
+  const float* exp_sums;
+  const float* max_logits;
+  const float* tmp_out;
+  const int32_t* seq_lens;
+  int num_seqs, num_q_heads, head_size, max_partitions, partition_size;
+};
+
+// Each returns hipSuccess or the launch error; `vec16` selects the 16-byte copy path.
+hipError_t launch_write(const WriteArgs& a, int dtype, bool vec16, hipStream_t stream);
+// Returns hipErrorInvalidValue for a (dtype, head_size, group) this build has no kernel for.
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, int dtype, hipStream_t stream);
+bool decode_supported(int dtype, int head_size, int group);
+
+}  // namespace pcache

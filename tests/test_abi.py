@@ -1,0 +1,138 @@
+"""The C ABI on the host: every declared symbol is exported, invalid arguments are
+refused before anything is enqueued, and the planner's choices (CPU only).
+
+Every call here either fails validation or is a documented no-op, so no kernel is
+ever launched (the pointers passed are never dereferenced).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_reshape_amd as pc
+from paged_kv_cache_reshape_amd import _native
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pc.LIB_PATH):
+        from paged_kv_cache_reshape_amd import build
+        build.build()
+    return pc.library()
+
+
+def declared_symbols():
+    text = open(os.path.join(REPO, "include", "pc.h")).read()
+    return sorted(set(re.findall(r"\b(pc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_symbols()
+    assert {"pc_reshape_and_cache", "pc_paged_attention_decode", "pc_paged_attention_reduce",
+            "pc_paged_attention_plan"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert pc.abi_version() == 1
+    assert pc.status_string(0) == "ok"
+    assert "invalid" in pc.status_string(-1)
+    assert "unsupported" in pc.status_string(-2)
+    assert "launch" in pc.status_string(-3)
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=100, bs=8 * 16 * 128, ts=128, hs=16 * 128, bt=FAKE, W=128,
+             sl=FAKE, S=4, msl=2048, Hq=32, Hkv=8, D=128, B=16, scale=0.088, ps=0, es=None, ml=None, tmp=None,
+             dt=2, stream=None)
+    a.update(kw)
+    return lib.pc_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"],
+                                         a["bt"], a["W"], a["sl"], a["S"], a["msl"], a["Hq"], a["Hkv"], a["D"],
+                                         a["B"], a["scale"], a["ps"], a["es"], a["ml"], a["tmp"], a["dt"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), -1),                      # unknown dtype
+    (dict(Hq=30), -1),                     # Hq not a multiple of Hkv
+    (dict(S=-1), -1),
+    (dict(msl=2049), -1),                  # longer than a table row can hold
+    (dict(out=None), -1),                  # one-pass path without out
+    (dict(q=None), -1),
+    (dict(nb=0), -1),
+    (dict(ps=512), -1),                    # split path without partials
+    (dict(es=FAKE), -1),                   # partials on the one-pass path
+    (dict(ps=256), -2),                    # partition size not offered
+    (dict(D=96, bs=8 * 16 * 96, hs=16 * 96, ts=96), -2),
+    (dict(B=8, W=256), -2),
+    (dict(Hq=64), -2),                     # group of 8 not built
+    (dict(q=ctypes.c_void_p(0x10008)), -2),  # not 16-byte aligned
+    (dict(ts=100), -2),                    # stride not a multiple of 16 bytes
+])
+def test_decode_validation(lib, kw, status):
+    assert _decode(lib, **kw) == status
+
+
+def test_decode_empty_batch_is_a_noop(lib):
+    assert _decode(lib, S=0) == 0
+    assert _decode(lib, S=0, q=None, k=None, v=None, bt=None, sl=None, out=None) == 0
+
+
+def test_write_validation(lib):
+    f = lib.pc_reshape_and_cache
+    ok = dict(key=FAKE, value=FAKE, krs=1024, vrs=1024, k=FAKE, v=FAKE, nb=10, bs=16384, ts=128, hs=2048,
+              sm=FAKE, T=3, Hkv=8, D=128, B=16, dt=2)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["key"], a["value"], a["krs"], a["vrs"], a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"],
+                 a["sm"], a["T"], a["Hkv"], a["D"], a["B"], a["dt"], None)
+
+    assert call(T=0) == 0  # no tokens: nothing to do
+    for bad in (dict(dt=3), dict(T=-1), dict(Hkv=0), dict(D=0), dict(B=0), dict(nb=0), dict(key=None),
+                dict(sm=None), dict(krs=100), dict(ts=0)):
+        assert call(**bad) == -1, bad
+
+
+def test_reduce_validation(lib):
+    f = lib.pc_paged_attention_reduce
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 128, 4, 512, 2, None) == 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 4, 256, 2, None) == -2
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 4, 512, 2, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 4, 512, 9, None) == -1
+
+
+def test_plan_choices():
+    bf16 = torch.bfloat16
+    # 64 sequences x 8 kv heads = 512 units: enough work units for a single pass
+    assert pc.paged_attention_plan(64, 32, 8, 128, 2048, bf16) == (0, 1, 0)
+    # 4 sequences x 8 kv heads = 32 units over 32768 tokens: split into 64 partitions
+    ps, P, ws = pc.paged_attention_plan(4, 32, 8, 128, 32768, bf16)
+    assert (ps, P) == (512, 64) and ws == 4 * 32 * 64 * (128 + 2) * 4
+    # a single partition never splits
+    assert pc.paged_attention_plan(1, 32, 8, 128, 512, bf16)[0] == 0
+    # many MHA units
+    assert pc.paged_attention_plan(256, 32, 32, 128, 8192, torch.float16)[0] == 0
+    with pytest.raises(pc.PagedCacheError):
+        pc.paged_attention_plan(4, 30, 8, 128, 100, bf16)
+
+
+def test_binding_refuses_host_tensors():
+    x = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pc.reshape_and_cache(x, x, x, x, torch.zeros(2, dtype=torch.int64), num_blocks=1, block_stride=1,
+                             token_stride=1, head_stride=1)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_native, "_lib", None)
+    monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _native.abi_version()

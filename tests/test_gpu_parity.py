@@ -1,0 +1,250 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded inputs.
+
+Bars: the cache write is bit-exact over the whole pool; attention is within
+max-abs 1e-5 (fp32 storage) or 1e-2 (bf16/fp16 storage) of the oracle.  The five
+named workloads run at full size in the path the benchmark times; smaller cases
+cover ragged tails, every (dtype, head size, group, layout) kernel, both paths,
+empty sequences and partitions, and invalid data.
+"""
+
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as gh
+import oracle
+import paged_kv_cache_reshape_amd as pc
+from helpers import bits_to_f64
+from workloads import custom, make_config, nan_bits
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}
+CONFIG_PATH = {0: "single", 1: "single", 2: "plan", 3: "split", 4: "plan"}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check_attention(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    i = np.unravel_index(int(err.argmax()), err.shape)
+    say(f"{what}: max|err| {err.max():.3e} at {tuple(int(x) for x in i)} (ref {ref[i]:.5f} got {got[i]:.5f}), "
+        f"max|o| {np.abs(ref).max():.3f}, tol {TOL[dtype]}")
+    assert err.max() <= TOL[dtype], what
+
+
+def pools_equal(dev: gh.DevicePool, host: oracle.Pool) -> bool:
+    torch.cuda.synchronize()
+    for d, h in zip(dev.arrays(), host.arrays()):
+        if not np.array_equal(gh.to_bits(d, dev.wl.dtype), h):
+            return False
+    return True
+
+
+# ---------------------------------------------------------------------------------
+# the five named workloads, full size
+# ---------------------------------------------------------------------------------
+
+@functools.lru_cache(maxsize=1)
+def _config_state(idx):
+    say(f"[config {idx}] generating")
+    wl = make_config(idx)
+    say(f"[config {idx}] oracle write + decode")
+    hpool = oracle.filled_pool(wl)
+    ref = oracle.decode(wl, hpool)
+    say(f"[config {idx}] GPU write")
+    dpool = gh.filled_pool(wl)
+    return wl, hpool, ref, dpool
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_config_write_bit_exact(idx):
+    wl, hpool, _, dpool = _config_state(idx)
+    say(f"[config {idx}] comparing {sum(a.nbytes for a in hpool.arrays()) / 1e9:.2f} GB of pool")
+    assert pools_equal(dpool, hpool)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_config_decode(idx):
+    wl, _, ref, dpool = _config_state(idx)
+    inp = gh.DecodeInputs(wl)
+    out, used = gh.decode(dpool, inp, CONFIG_PATH[idx])
+    torch.cuda.synchronize()
+    check_attention(gh.out_f64(out), ref, wl.dtype, f"[config {idx}] {used} path")
+    if idx == 1:
+        assert used == "single"
+    if idx == 3:
+        assert used == "split"
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_config_other_path(idx):
+    """The path the planner did not pick must agree too."""
+    wl, _, ref, dpool = _config_state(idx)
+    inp = gh.DecodeInputs(wl)
+    _, used = gh.decode(dpool, inp, "plan")
+    other = "split" if used == "single" else "single"
+    out, _ = gh.decode(dpool, inp, other)
+    torch.cuda.synchronize()
+    check_attention(gh.out_f64(out), ref, wl.dtype, f"[config {idx}] {other} path")
+
+
+# ---------------------------------------------------------------------------------
+# every kernel variant on ragged lengths
+# ---------------------------------------------------------------------------------
+
+LENGTHS = [1, 15, 16, 17, 100, 511, 512, 513, 1100]
+VARIANTS = [(dt, D, G, layout) for dt in ("f32", "f16", "bf16") for D in (64, 128) for G in (1, 2, 4)
+            for layout in ("hnd",)] + [("bf16", 64, 4, "combined"), ("f16", 128, 4, "nhd"), ("f32", 64, 2, "nhd"),
+                                        ("bf16", 128, 1, "combined")]
+
+
+@pytest.mark.parametrize("dt,D,G,layout", VARIANTS, ids=[f"{a}-d{b}-g{c}-{d}" for a, b, c, d in VARIANTS])
+@pytest.mark.parametrize("path", ["single", "split"])
+def test_variant_parity(dt, D, G, layout, path):
+    Hkv = 2
+    wl = custom(100 + D + G, dt, Hkv * G, Hkv, D, LENGTHS, layout=layout, extra_pad_rows=1)
+    hpool = oracle.filled_pool(wl)
+    dpool = gh.filled_pool(wl)
+    assert pools_equal(dpool, hpool)
+    out, _ = gh.decode(dpool, gh.DecodeInputs(wl), path)
+    torch.cuda.synchronize()
+    check_attention(gh.out_f64(out), oracle.decode(wl, hpool), dt, f"{dt} D{D} G{G} {layout} {path}")
+
+
+@pytest.mark.parametrize("path", ["single", "split"])
+def test_zero_length_sequences(path):
+    wl = custom(7, "bf16", 8, 2, 128, [0, 37, 0, 600])
+    dpool = gh.filled_pool(wl)
+    out, _ = gh.decode(dpool, gh.DecodeInputs(wl), path)
+    got = gh.out_f64(out)
+    assert (got[0] == 0).all() and (got[2] == 0).all()
+    check_attention(got, oracle.decode(wl, oracle.filled_pool(wl)), "bf16", f"zero-length {path}")
+
+
+def test_shared_prefix_and_padding_rows():
+    wl = custom(8, "f16", 16, 16, 128, [20, 64, 65, 300, 1030], prefix_blocks=4, pad_count=2, table_width=80)
+    hpool = oracle.filled_pool(wl)
+    dpool = gh.filled_pool(wl)
+    assert pools_equal(dpool, hpool)
+    for path in ("single", "split"):
+        out, _ = gh.decode(dpool, gh.DecodeInputs(wl), path)
+        check_attention(gh.out_f64(out), oracle.decode(wl, hpool), "f16", f"prefix+padding {path}")
+
+
+def test_split_partials_against_oracle():
+    wl = custom(9, "bf16", 8, 2, 128, [1, 511, 512, 513, 1500])
+    hpool = oracle.filled_pool(wl)
+    dpool = gh.filled_pool(wl)
+    inp = gh.DecodeInputs(wl)
+    S, Hq, D = wl.q.shape
+    P = -(-inp.max_seq_len // 512)
+    es = torch.full((S, Hq, P), float("nan"), device="cuda")
+    ml = torch.full((S, Hq, P), float("nan"), device="cuda")
+    tmp = torch.full((S, Hq, P, D), float("nan"), device="cuda")
+    pc.paged_attention_decode(None, inp.q, dpool.k, dpool.v, inp.block_tables, inp.seq_lens, inp.max_seq_len,
+                              num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), partition_size=512,
+                              exp_sums=es, max_logits=ml, tmp_out=tmp, **dpool.layout_kwargs())
+    torch.cuda.synchronize()
+    rt, rm, re = oracle.partials(wl, hpool, 512, P)
+    gt, gm, ge = tmp.double().cpu().numpy(), ml.double().cpu().numpy(), es.double().cpu().numpy()
+    written = ~np.isnan(rm)
+    assert np.array_equal(written, ~np.isnan(gm)), "partitions written differ"
+    assert np.abs(gm[written] - rm[written]).max() < 1e-5
+    assert (np.abs(ge[written] - re[written]) / re[written]).max() < 1e-5
+    assert np.abs(gt[written] - rt[written]).max() < 1e-4
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_reduce_alone(dt):
+    """Oracle partials rounded to fp32 in, GPU merge out, against the oracle merge."""
+    wl = custom(10, dt, 8, 4, 64, [3, 512, 513, 2000])
+    hpool = oracle.filled_pool(wl)
+    P = 4
+    rt, rm, re = oracle.partials(wl, hpool, 512, P, fill=0.0)
+    rt32, rm32, re32 = (np.asarray(x, np.float32) for x in (rt, rm, re))
+    ref = oracle.merge(rt32.astype(np.float64), rm32.astype(np.float64), re32.astype(np.float64), wl.seq_lens, 512)
+    out = torch.empty(wl.q.shape, dtype=gh.TORCH_DT[dt], device="cuda")
+    pc.paged_attention_reduce(out, torch.from_numpy(re32).cuda(), torch.from_numpy(rm32).cuda(),
+                              torch.from_numpy(rt32).cuda(), torch.from_numpy(wl.seq_lens).cuda())
+    check_attention(gh.out_f64(out), ref, dt, f"reduce alone {dt}")
+
+
+# ---------------------------------------------------------------------------------
+# invalid data: kernels turn it into NaN or a skipped write, never an out-of-range access
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["single", "split"])
+def test_invalid_block_id_poisons_only_its_sequence(path):
+    wl = custom(11, "bf16", 8, 2, 128, [40, 700, 33])
+    hpool = oracle.filled_pool(wl)
+    dpool = gh.filled_pool(wl)
+    bt = wl.block_tables.copy()
+    bt[1, 1] = wl.num_blocks + 3
+    out, _ = gh.decode(dpool, gh.DecodeInputs(wl, block_tables=bt), path)
+    got = gh.out_f64(out)
+    assert np.isnan(got[1]).all()
+    ref = oracle.decode(wl, hpool)
+    check_attention(got[[0, 2]], ref[[0, 2]], "bf16", f"neighbours of a bad table row ({path})")
+
+
+def test_length_past_table_row_is_flagged():
+    wl = custom(12, "f16", 4, 4, 64, [40, 20], table_width=3)
+    dpool = gh.filled_pool(wl)
+    sl = wl.seq_lens.copy()
+    sl[1] = 3 * 16 + 5  # needs a 4th block the row does not have
+    inp = gh.DecodeInputs(wl, seq_lens=sl)
+    with pytest.raises(pc.PagedCacheError):  # the host knows max_seq_len exceeds the row: refused
+        gh.decode(dpool, inp, "single")
+    out, _ = gh.decode(dpool, inp, "single", max_seq_len=48)  # a caller that understates it: kernel flags NaN
+    got = gh.out_f64(out)
+    assert np.isnan(got[1]).all() and np.isfinite(got[0]).all()
+
+
+def test_write_skips_negative_and_out_of_range_slots():
+    wl = custom(13, "bf16", 8, 2, 128, [5, 9])
+    dpool = gh.filled_pool(wl)
+    before = [gh.to_bits(a, wl.dtype).copy() for a in dpool.arrays()]
+    slots = np.array([-1, -7, wl.num_blocks * 16, wl.num_blocks * 16 + 99], np.int64)
+    rows = np.repeat(wl.key[:1], 4, axis=0)
+    gh.write(dpool, rows, rows, slots)
+    torch.cuda.synchronize()
+    for b, a in zip(before, dpool.arrays()):
+        assert np.array_equal(b, gh.to_bits(a, wl.dtype))
+
+
+def test_write_unaligned_rows_fall_back_to_element_copies():
+    wl = custom(14, "bf16", 8, 2, 128, [3, 30])
+    hpool = oracle.filled_pool(wl)
+    dpool = gh.DevicePool(wl)
+    for key, value, slots in ((wl.pre_key, wl.pre_value, wl.pre_slots), (wl.key, wl.value, wl.slot_mapping)):
+        T = len(slots)
+        big_k = torch.zeros(T * 257 + 1, dtype=torch.bfloat16, device="cuda")
+        big_v = torch.zeros(T * 257 + 1, dtype=torch.bfloat16, device="cuda")
+        kk = big_k[1:].as_strided((T, 2, 128), (257, 128, 1))  # odd element offset and row stride
+        vv = big_v[1:].as_strided((T, 2, 128), (257, 128, 1))
+        kk.copy_(gh.to_dev(key, "bf16"))
+        vv.copy_(gh.to_dev(value, "bf16"))
+        pc.reshape_and_cache(kk, vv, dpool.k, dpool.v, torch.from_numpy(slots).cuda(), **dpool.layout_kwargs())
+    assert pools_equal(dpool, hpool)
+
+
+def test_side_stream_ordering():
+    """Write then decode on a non-default stream: the decode sees the written tokens."""
+    wl = custom(15, "bf16", 8, 2, 128, [77, 300])
+    hpool = oracle.filled_pool(wl)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dpool = gh.DevicePool(wl)
+        gh.write(dpool, wl.pre_key, wl.pre_value, wl.pre_slots)
+        gh.write(dpool, wl.key, wl.value, wl.slot_mapping)
+        out, _ = gh.decode(dpool, gh.DecodeInputs(wl), "single")
+    s.synchronize()
+    check_attention(gh.out_f64(out), oracle.decode(wl, hpool), "bf16", "side stream")

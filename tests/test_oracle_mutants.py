@@ -19,8 +19,8 @@ MUTANTS = {
     "gqa_modulo": ("int kv = h / G;", "int kv = h % j->num_kv_heads;"),
     "slot_offset_shift": ("int64_t off = slot % block_size;", "int64_t off = (slot + 1) % block_size;"),
     "slot_block_divisor": ("int64_t blk = slot / block_size;", "int64_t blk = slot / (block_size + 1);"),
-    "write_strides_swapped": ("int64_t dst = blk * block_stride + off * token_stride + (int64_t)h * head_stride + d;",
-                              "int64_t dst = blk * block_stride + off * head_stride + (int64_t)h * token_stride + d;"),
+    "write_strides_swapped": ("int64_t dst = blk * block_stride + off * token_stride + (int64_t)h * head_stride;",
+                              "int64_t dst = blk * block_stride + off * head_stride + (int64_t)h * token_stride;"),
     "negative_slot_written": ("if (slot < 0)\n            continue;", "if (slot < -1)\n            continue;"),
     "read_logical_block": ("int lb = t / j->block_size;", "int lb = t / (2 * j->block_size);"),
     "read_offset_shift": ("int off = t % j->block_size;", "int off = (t + 1) % j->block_size;"),
