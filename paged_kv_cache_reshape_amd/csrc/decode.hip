@@ -100,29 +100,50 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_kernel(DecodeArgs a) {
   const int64_t load_step = (int64_t)TPI * a.token_stride * EB;
   const int64_t block_bytes = a.block_stride * EB;
 
-  uint4 kc[NI], vc[NI];
-  auto load_block = [&](int b, uint4 (&kd)[NI], uint4 (&vd)[NI]) {
-    const int phys = table[b];
-    if (phys < 0 || phys >= a.num_blocks) {
-      bad = true;
-#pragma unroll
-      for (int j = 0; j < NI; ++j) kd[j] = vd[j] = make_uint4(0, 0, 0, 0);
-      return;
-    }
-    const char* kp = kbase + (int64_t)phys * block_bytes + lane_off;
-    const char* vp = vbase + (int64_t)phys * block_bytes + lane_off;
-#pragma unroll
-    for (int j = 0; j < NI; ++j) kd[j] = *reinterpret_cast<const uint4*>(kp + j * load_step);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) vd[j] = *reinterpret_cast<const uint4*>(vp + j * load_step);
+  // This wave takes blocks b_begin + w, b_begin + w + kWaves, ...: nw of them.  Their
+  // physical ids are fetched 64 at a time into one VGPR (lane k holds the k-th) and
+  // read back with readlane, so no table load sits on the per-block path.
+  const int first = b_begin + w;
+  const int nw = first < b_end ? (b_end - first + kWaves - 1) / kWaves : 0;
+  int tv = 0;
+  auto fetch_table = [&](int chunk) {
+    const int idx = chunk * kWave + lane;
+    int v = 0;
+    if (idx < nw) v = table[first + idx * kWaves];
+    const bool out_of_pool = idx < nw && (v < 0 || (int64_t)v >= a.num_blocks);
+    if (__builtin_amdgcn_ballot_w64(out_of_pool) != 0) bad = true;
+    tv = v;
   };
+  int n_iter = nw;
+  if (n_iter > 0) {
+    fetch_table(0);
+    if (bad) n_iter = 0;  // a block id outside the pool: nothing is read, the outputs become NaN
+  }
 
-  int b = b_begin + w;
-  if (b < b_end) load_block(b, kc, vc);
-  for (; b < b_end; b += kWaves) {
-    uint4 kn[NI], vn[NI];
-    const int bn = b + kWaves;
-    if (bn < b_end) load_block(bn, kn, vn);
+  uint4 kc[NI], vc[NI], kn[NI], vn[NI];
+  if (n_iter > 0) {
+    const int64_t boff = (int64_t)__builtin_amdgcn_readlane(tv, 0) * block_bytes + lane_off;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) kc[j] = *reinterpret_cast<const uint4*>(kbase + boff + j * load_step);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) vc[j] = *reinterpret_cast<const uint4*>(vbase + boff + j * load_step);
+  }
+  for (int it = 0; it < n_iter; ++it) {
+    const int b = first + it * kWaves;
+    const int nx = it + 1;
+    if (nx < n_iter) {
+      if ((nx & (kWave - 1)) == 0) {
+        fetch_table(nx / kWave);
+        if (bad) n_iter = nx;  // stop before the first chunk holding a bad id
+      }
+      if (nx < n_iter) {
+        const int64_t boff = (int64_t)__builtin_amdgcn_readlane(tv, nx & (kWave - 1)) * block_bytes + lane_off;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) kn[j] = *reinterpret_cast<const uint4*>(kbase + boff + j * load_step);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) vn[j] = *reinterpret_cast<const uint4*>(vbase + boff + j * load_step);
+      }
+    }
 
     // scores of this block: sc[j][g] for token row j*TPI + lr, query head h0 + g
     float sc[NI][G];
@@ -135,11 +156,14 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_kernel(DecodeArgs a) {
     if (visible < kBlockTokens) {  // last block: positions >= seq_len take no part
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        if (j * TPI + lr >= visible) {
+        const bool masked = j * TPI + lr >= visible;
 #pragma unroll
-          for (int g = 0; g < G; ++g) sc[j][g] = -INFINITY;
-          vc[j] = make_uint4(0, 0, 0, 0);  // stale V may be NaN, and 0 * NaN = NaN
-        }
+        for (int g = 0; g < G; ++g) sc[j][g] = masked ? -INFINITY : sc[j][g];
+        // stale V may be NaN, and 0 * NaN = NaN
+        vc[j].x = masked ? 0u : vc[j].x;
+        vc[j].y = masked ? 0u : vc[j].y;
+        vc[j].z = masked ? 0u : vc[j].z;
+        vc[j].w = masked ? 0u : vc[j].w;
       }
     }
 
@@ -149,14 +173,17 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 1; j < NI; ++j) bm = fmaxf(bm, sc[j][g]);
       const float mn = fmaxf(m[g], bm);
-      const float alpha = fast_exp2(m[g] - mn);
+      // a lane row may not have seen a visible token yet (mn = -inf): use 0 as the
+      // exponent reference so exp2(-inf - ref) gives 0 instead of NaN
+      const float ref = mn == -INFINITY ? 0.f : mn;
+      const float alpha = fast_exp2(m[g] - ref);
       m[g] = mn;
       l[g] *= alpha;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const float p = fast_exp2(sc[j][g] - mn);
+        const float p = fast_exp2(sc[j][g] - ref);
         l[g] += p;
         sc[j][g] = p;
       }

@@ -111,7 +111,10 @@ __device__ __forceinline__ uint32_t to_storage<BF16>(float x) {
 // lanes.  A 32-lane group first folds lane i with i^16 through ds_swizzle.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  // every control used here reads a lane of the same row, so bound_ctrl never matters;
+  // setting it lets the compiler fold the move into the consuming v_add/v_max
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 constexpr int kDppRowMirror = 0x140;
