@@ -132,9 +132,10 @@ int pc_reshape_and_cache(const void *key, const void *value, int64_t key_row_str
  *   seq_lens          device int32 [num_seqs]; must include this step's token
  *   max_seq_len       host-known upper bound of seq_lens (sizes the split grid)
  *   num_q_heads       multiple of num_kv_heads; num_q_heads/num_kv_heads in {1,2,4,8}
+ *                     for fp16/bf16, {1,2,4} for fp32
  *   head_size         64 or 128
  *   block_size        16
- *   scale             multiplies q.k (typically 1/sqrt(head_size))
+ *   scale             multiplies q.k (typically 1/sqrt(head_size)); positive, finite
  *   partition_size    0: one pass, writes out.  PC_PARTITION_SIZE: split path,
  *                     writes only exp_sums, max_logits and tmp_out; follow with
  *                     pc_paged_attention_reduce on the same stream.

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 #include <cstdint>
 #include <mutex>
 
@@ -108,6 +109,7 @@ int pc_paged_attention_decode(void* out, const void* q, const void* k_pool, cons
   if (num_seqs == 0) return PC_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || (!split && !out)) return PC_ERR_INVALID_ARG;
   if (num_blocks <= 0 || block_stride <= 0 || token_stride <= 0 || head_stride <= 0) return PC_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PC_ERR_INVALID_ARG;
   if (block_size != kBlockTokens) return PC_ERR_UNSUPPORTED;
   if (!pcache::decode_supported(dtype, head_size, num_q_heads / num_kv_heads)) return PC_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
@@ -145,7 +147,7 @@ int pc_paged_attention_reduce(void* out, const float* exp_sums, const float* max
   if (!esize(dtype) || num_seqs < 0 || num_q_heads <= 0 || head_size <= 0 || max_num_partitions < 0 ||
       partition_size <= 0)
     return PC_ERR_INVALID_ARG;
-  if (partition_size != PC_PARTITION_SIZE) return PC_ERR_UNSUPPORTED;
+  if (partition_size != PC_PARTITION_SIZE || !pcache::reduce_supported(head_size)) return PC_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PC_OK;
   if (!out || !seq_lens || (max_num_partitions > 0 && (!exp_sums || !max_logits || !tmp_out)))
     return PC_ERR_INVALID_ARG;

@@ -1,5 +1,6 @@
 // decode.hip -- paged decode attention: one query token per (sequence, head)
-// against the sequence's paged K/V, in one pass or per 512-token partition.
+// against the sequence's paged K/V, in one pass or per 512-token partition.  This
+// VALU kernel serves fp32 storage; fp16 / bf16 storage runs decode_mfma.hip.
 //
 // What is computed ("vLLM 源码完全拆解（七）: PagedAttention Kernel", sections
 // 先明确问题, 线程组织, 第一步 and V1与V2; "Inside vLLM CUDA Kernels", Part 3,
@@ -296,15 +297,18 @@ hipError_t launch_dim(const DecodeArgs& a, int head_size, bool split, hipStream_
 }  // namespace
 
 bool decode_supported(int dtype, int head_size, int group) {
-  return (dtype == 0 || dtype == 1 || dtype == 2) && (head_size == 64 || head_size == 128) &&
-         (group == 1 || group == 2 || group == 4);
+  if (head_size != 64 && head_size != 128) return false;
+  if (dtype == 0) return group == 1 || group == 2 || group == 4;
+  if (dtype == 1 || dtype == 2) return group == 1 || group == 2 || group == 4 || group == 8;
+  return false;
 }
 
+// fp32 storage runs the VALU kernel above; fp16 / bf16 take the matrix-core kernel.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream) {
   switch (dtype) {
     case 0: return launch_dim<F32>(a, head_size, split, stream);
-    case 1: return launch_dim<F16>(a, head_size, split, stream);
-    case 2: return launch_dim<BF16>(a, head_size, split, stream);
+    case 1:
+    case 2: return launch_decode_mfma(a, dtype, head_size, split, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -134,4 +134,16 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// ---- lanes of one wave exchanging values through LDS -----------------------------
+// A store by one lane and a load of the same LDS word by another lane of the same
+// wave are unsynchronised in the language's memory model, so the compiler may move
+// the load above the store (or forward a lane's own store).  This wavefront-scope
+// release/acquire pair pins the order: everything stored before it is visible to
+// every lane's loads after it.  No s_barrier is involved.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace pcache

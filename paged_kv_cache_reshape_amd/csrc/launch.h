@@ -48,7 +48,10 @@ struct ReduceArgs {
 hipError_t launch_write(const WriteArgs& a, int dtype, bool vec16, hipStream_t stream);
 // Returns hipErrorInvalidValue for a (dtype, head_size, group) this build has no kernel for.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
+// 16-bit storage: q.k on the matrix cores (decode_mfma.hip).
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, hipStream_t stream);
 bool decode_supported(int dtype, int head_size, int group);
+bool reduce_supported(int head_size);
 
 }  // namespace pcache

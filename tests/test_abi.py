@@ -72,7 +72,7 @@ def _decode(lib, **kw):
     (dict(ps=256), -2),                    # partition size not offered
     (dict(D=96, bs=8 * 16 * 96, hs=16 * 96, ts=96), -2),
     (dict(B=8, W=256), -2),
-    (dict(Hq=64), -2),                     # group of 8 not built
+    (dict(Hq=128), -2),                    # group of 16 not built
     (dict(q=ctypes.c_void_p(0x10008)), -2),  # not 16-byte aligned
     (dict(ts=100), -2),                    # stride not a multiple of 16 bytes
 ])
