@@ -168,7 +168,8 @@ int pc_paged_attention_decode(void *out, const void *q, const void *k_pool, cons
  *
  *   out                device [num_seqs, num_q_heads, head_size], storage dtype
  *   exp_sums ...       device fp32, as written by pc_paged_attention_decode
- *   max_num_partitions P of the decode call; partition_size PC_PARTITION_SIZE
+ *   max_num_partitions P of the decode call; partition_size PC_PARTITION_SIZE;
+ *                      tmp_out 16-byte aligned (as for the decode)
  * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
  */
 int pc_paged_attention_reduce(void *out, const float *exp_sums, const float *max_logits, const float *tmp_out,

@@ -28,9 +28,13 @@ bool strides16(int es, std::initializer_list<int64_t> strides) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? PC_OK : PC_ERR_LAUNCH; }
 
+}  // namespace
+
+namespace pcache {
+
 // Compute units of the current device, cached per device; MI355X's 256 when no
 // device can be queried (the planner is usable without a GPU).
-int compute_units() {
+int device_compute_units() {
   static std::mutex mu;
   static int cached[64] = {0};
   int dev = 0;
@@ -50,7 +54,7 @@ int compute_units() {
   return cached[dev];
 }
 
-}  // namespace
+}  // namespace pcache
 
 extern "C" {
 
@@ -151,6 +155,7 @@ int pc_paged_attention_reduce(void* out, const float* exp_sums, const float* max
   if (num_seqs == 0) return PC_OK;
   if (!out || !seq_lens || (max_num_partitions > 0 && (!exp_sums || !max_logits || !tmp_out)))
     return PC_ERR_INVALID_ARG;
+  if (!aligned16(tmp_out)) return PC_ERR_UNSUPPORTED;
   if ((int64_t)num_seqs * num_q_heads > INT_MAX) return PC_ERR_UNSUPPORTED;
   pcache::ReduceArgs a{out, exp_sums, max_logits, tmp_out, seq_lens, num_seqs, num_q_heads, head_size,
                        max_num_partitions, partition_size};
@@ -168,7 +173,7 @@ int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int
   // units stream their history; the split path multiplies the units by the
   // partition count at the cost of a second launch and the partials' traffic.
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  const bool split = parts > 1 && units < compute_units();
+  const bool split = parts > 1 && units < pcache::device_compute_units();
   const int ps = split ? PC_PARTITION_SIZE : 0;
   const int mp = split ? parts : 1;
   if (partition_size) *partition_size = ps;

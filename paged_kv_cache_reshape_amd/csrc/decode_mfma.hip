@@ -23,9 +23,19 @@
 //   LDS words to the lanes that hold the row group's V slices; P.V then runs on
 //   the VALU in fp32: lane (r, i) holds 16 bytes of each of its tokens' V rows and
 //   all G heads' accumulators for those 8 (or, for head_size 64, 8 of 64) dims.
-// * Two register sets alternate, so block n+1's K/V loads are in flight while
-//   block n is consumed, and each wave reads its block ids 64 at a time into one
-//   VGPR.  The unit's waves merge their states once, at the end.
+// * A ring of STAGES register sets keeps the next STAGES-1 blocks' K/V loads in
+//   flight while one block is consumed; each wave reads its block ids 64 at a time
+//   into one VGPR.  A unit's waves merge their states once, at the end.
+//
+// Work distribution:
+// * Split path: one workgroup per (sequence, kv head, 512-token partition); the
+//   partitions are equal-sized, so the grid balances itself.
+// * One-pass path: a unit is a whole (sequence, kv head) and unit lengths can differ
+//   several-fold, so a grid of one unit per workgroup ends with a few long units
+//   running alone.  Instead the kernel is persistent: one workgroup per resident
+//   slot; units are ordered longest first and dealt in snake order (workgroup k of
+//   W takes positions k, 2W-1-k, 2W+k, ...), so every workgroup receives about the
+//   same number of blocks.  Each unit is still computed by exactly one workgroup.
 #include <cmath>
 
 #include "device_common.h"
@@ -36,8 +46,21 @@ namespace {
 
 constexpr int kBlockTokens = 16;
 constexpr int kPartition = 512;
-constexpr int kWaves = 4;
-constexpr float kLazy = 8.f;  // log2-domain slack before the exponent reference moves
+constexpr float kLazy = 8.f;         // log2-domain slack before the exponent reference moves
+constexpr int kMaxRankedSeqs = 512;  // sequences ranked by length in-kernel (beyond: index order)
+
+#ifndef PCACHE_ONEPASS_WAVES
+#define PCACHE_ONEPASS_WAVES 8
+#endif
+#ifndef PCACHE_ONEPASS_STAGES
+#define PCACHE_ONEPASS_STAGES 2
+#endif
+#ifndef PCACHE_SPLIT_WAVES
+#define PCACHE_SPLIT_WAVES 4
+#endif
+#ifndef PCACHE_SPLIT_STAGES
+#define PCACHE_SPLIT_STAGES 2
+#endif
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -58,24 +81,29 @@ __device__ __forceinline__ f32x4_t mfma16<F16>(const uint4& a, const uint4& b, f
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <class ST, int D, int G, bool SPLIT>
-__global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a) {
+template <int NW, int D, int G>
+struct UnitLds {
+  __align__(16) float p[NW][4][4 * G];  // probabilities of a row group (read as float4)
+  __align__(16) float a[NW][4][G];      // rescale / fold factors of a row group
+  __align__(16) float acc[NW][G][D];    // each wave's folded accumulator
+  float mw[NW][G];
+  float lw[NW][G];
+  int bad[NW];
+};
+
+// One unit: kv head `kvh` of sequence `s`, tokens [t_begin, t_end).  All waves of
+// the workgroup call it together (it ends with a barrier-separated merge).  Writes
+// out (one pass) or the partition's partials (split).
+template <class ST, int D, int G, int NW, int STAGES, bool SPLIT>
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, G>& sm, int s, int kvh, int part) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
   static_assert(D == 64 || D == 128, "head size 64 or 128");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group of 1, 2, 4 or 8 query heads");
-  constexpr int KS = D / 32;         // MFMA k-steps per block
-  constexpr int RL = D / 8;          // lanes per V token row (16-byte slices)
-  constexpr int RPG = 16 / RL;       // V rows per row group per load
-  constexpr int NJ = 4 / RPG;        // V loads per block
-  constexpr int kSlots = 4 * G;      // floats of probabilities per row group
-
-  // p_lds is read and written as float4: it needs 16-byte alignment explicitly
-  __shared__ __align__(16) float p_lds[kWaves][4][kSlots];
-  __shared__ __align__(16) float a_lds[kWaves][4][G];
-  __shared__ __align__(16) float acc_lds[kWaves][G][D];
-  __shared__ float mw_lds[kWaves][G];
-  __shared__ float lw_lds[kWaves][G];
-  __shared__ int bad_lds[kWaves];
+  static_assert(STAGES >= 2 && STAGES <= 4, "prefetch ring of 2..4 register sets");
+  constexpr int KS = D / 32;    // MFMA k-steps per block
+  constexpr int RL = D / 8;     // lanes per V token row (16-byte slices)
+  constexpr int RPG = 16 / RL;  // V rows per row group per load
+  constexpr int NJ = 4 / RPG;   // V loads per block
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -84,17 +112,10 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
   const int vsub = col / RL;    // which of the row group's rows this lane loads per V load
   const int vchunk = col % RL;  // 16-byte slice of a V row
 
-  int64_t id = blockIdx.x;
-  const int kvh = (int)(id % a.num_kv_heads);
-  id /= a.num_kv_heads;
-  const int s = (int)(id % a.num_seqs);
-  const int part = SPLIT ? (int)(id / a.num_seqs) : 0;
-
   const int L = a.seq_lens[s];
   bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
              (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition);
   const int t_begin = SPLIT ? part * kPartition : 0;
-  if (SPLIT && !bad && t_begin >= L) return;  // a partition past the sequence writes nothing
   const int t_end = bad ? t_begin : (SPLIT ? min(L, t_begin + kPartition) : L);
   const int b_begin = t_begin / kBlockTokens;
   const int b_end = (t_end + kBlockTokens - 1) / kBlockTokens;
@@ -129,13 +150,14 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
   const int64_t v_step = (int64_t)RPG * tok_bytes;
   const int64_t block_bytes = a.block_stride * 2;
 
+  // This wave takes blocks first, first + NW, ...: nw of them.
   const int first = b_begin + w;
-  const int nw = first < b_end ? (b_end - first + kWaves - 1) / kWaves : 0;
+  const int nw = first < b_end ? (b_end - first + NW - 1) / NW : 0;
   int tv = 0;
   auto fetch_table = [&](int chunk) {
     const int idx = chunk * kWave + lane;
     int v = 0;
-    if (idx < nw) v = table[first + idx * kWaves];
+    if (idx < nw) v = table[first + idx * NW];
     if (__builtin_amdgcn_ballot_w64(idx < nw && (v < 0 || (int64_t)v >= a.num_blocks)) != 0) bad = true;
     tv = v;
   };
@@ -145,7 +167,7 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
     if (bad) n_iter = 0;  // a block id outside the pool: nothing is read, the outputs become NaN
   }
 
-  uint4 kx[KS], vx[NJ], ky[KS], vy[NJ];
+  uint4 kb[STAGES][KS], vb[STAGES][NJ];
 
 #define PC_LOAD(KD, VD, IT)                                                                          \
   do {                                                                                               \
@@ -161,7 +183,7 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
   do {                                                                                               \
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};                                                                \
     _Pragma("unroll") for (int k = 0; k < KS; ++k) c = mfma16<ST>(KC[k], qb[k], c);                 \
-    const int visible = t_end - (first + (IT) * kWaves) * kBlockTokens;                             \
+    const int visible = t_end - (first + (IT) * NW) * kBlockTokens;                                  \
     if (visible < kBlockTokens) {                                                                    \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) c[i] = 4 * rg + i < visible ? c[i] : -INFINITY; \
       _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                              \
@@ -176,29 +198,29 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
     m_true = fmaxf(m_true, bm);                                                                      \
     const bool need = col < G && bm > m_ref + lazy_raw;                                              \
     const bool rescale = __builtin_amdgcn_ballot_w64(need) != 0;                                     \
-    wave_lds_sync(); /* the previous block's loads of p_lds / a_lds come before these stores */      \
+    wave_lds_sync(); /* the previous block's loads of sm.p / sm.a come before these stores */        \
     if (rescale) {                                                                                   \
       const float alpha = need ? exp2_fast((m_ref - bm) * cs) : 1.f;                                 \
       m_ref = need ? bm : m_ref;                                                                     \
       lsum *= alpha;                                                                                 \
-      if (col < G) a_lds[w][rg][col] = alpha;                                                        \
+      if (col < G) sm.a[w][rg][col] = alpha;                                                         \
     }                                                                                                \
     const float ref = m_ref == -INFINITY ? 0.f : m_ref * cs;                                         \
     float pr[4];                                                                                     \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(fmaf(c[i], cs, -ref));          \
     lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);                                                       \
     if (col < G)                                                                                     \
-      *reinterpret_cast<float4*>(&p_lds[w][rg][4 * col]) = make_float4(pr[0], pr[1], pr[2], pr[3]); \
+      *reinterpret_cast<float4*>(&sm.p[w][rg][4 * col]) = make_float4(pr[0], pr[1], pr[2], pr[3]);  \
     wave_lds_sync(); /* other lanes' stores above are visible to the loads below */                 \
     if (rescale) {                                                                                   \
       _Pragma("unroll") for (int g = 0; g < G; ++g) {                                               \
-        const float al = a_lds[w][rg][g];                                                            \
+        const float al = sm.a[w][rg][g];                                                             \
         _Pragma("unroll") for (int e = 0; e < 8; ++e) acc[g][e] *= al;                              \
       }                                                                                              \
     }                                                                                                \
     float pv[G][4];                                                                                  \
     _Pragma("unroll") for (int g = 0; g < G; ++g) {                                                 \
-      const float4 t4 = *reinterpret_cast<const float4*>(&p_lds[w][rg][4 * g]);                    \
+      const float4 t4 = *reinterpret_cast<const float4*>(&sm.p[w][rg][4 * g]);                      \
       pv[g][0] = t4.x;                                                                               \
       pv[g][1] = t4.y;                                                                               \
       pv[g][2] = t4.z;                                                                               \
@@ -214,25 +236,26 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
   } while (0)
 
   const float lazy_raw = kLazy / cs;
-  if (n_iter > 0) PC_LOAD(kx, vx, 0);
-  for (int it = 0; it < n_iter; it += 2) {
-    if (it + 1 < n_iter) {
-      if (((it + 1) & (kWave - 1)) == 0) {
-        fetch_table((it + 1) / kWave);
-        if (bad) n_iter = it + 1;
+  if (n_iter > 0) {
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < n_iter) PC_LOAD(kb[st], vb[st], st);
+  }
+  for (int it0 = 0; it0 < n_iter; it0 += STAGES) {
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st) {
+      const int it = it0 + st;
+      if (it >= n_iter) break;
+      const int nx = it + STAGES - 1;  // the block this step starts fetching
+      if (nx < n_iter) {
+        if ((nx & (kWave - 1)) == 0) {
+          fetch_table(nx / kWave);
+          if (bad) n_iter = nx;  // stop before the first chunk holding a bad id
+        }
+        if (nx < n_iter) PC_LOAD(kb[(st + STAGES - 1) % STAGES], vb[(st + STAGES - 1) % STAGES], nx);
       }
-      if (it + 1 < n_iter) PC_LOAD(ky, vy, it + 1);
+      PC_BLOCK(kb[st], vb[st], it);
     }
-    PC_BLOCK(kx, vx, it);
-    if (it + 1 >= n_iter) break;
-    if (it + 2 < n_iter) {
-      if (((it + 2) & (kWave - 1)) == 0) {
-        fetch_table((it + 2) / kWave);
-        if (bad) n_iter = it + 2;
-      }
-      if (it + 2 < n_iter) PC_LOAD(kx, vx, it + 2);
-    }
-    PC_BLOCK(ky, vy, it + 1);
   }
 #undef PC_LOAD
 #undef PC_BLOCK
@@ -248,11 +271,11 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
   lw += __shfl_xor(lw, 16);
   lw += __shfl_xor(lw, 32);
   wave_lds_sync();
-  if (col < G) a_lds[w][rg][col] = f;
+  if (col < G) sm.a[w][rg][col] = f;
   wave_lds_sync();
   float fr[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) fr[g] = a_lds[w][rg][g];
+  for (int g = 0; g < G; ++g) fr[g] = sm.a[w][rg][g];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -267,32 +290,32 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc_lds[w][g][8 * vchunk + e] = acc[g][e];
+      for (int e = 0; e < 8; ++e) sm.acc[w][g][8 * vchunk + e] = acc[g][e];
   }
   if (rg == 0 && col < G) {
-    mw_lds[w][col] = mw;
-    lw_lds[w][col] = lw;
+    sm.mw[w][col] = mw;
+    sm.lw[w][col] = lw;
   }
-  if (lane == 0) bad_lds[w] = bad ? 1 : 0;
+  if (lane == 0) sm.bad[w] = bad ? 1 : 0;
   __syncthreads();
 
   // ---- merge the waves and write ------------------------------------------------------
   bool any_bad = false;
 #pragma unroll
-  for (int ww = 0; ww < kWaves; ++ww) any_bad |= bad_lds[ww] != 0;
-  for (int o = threadIdx.x; o < G * D; o += kWaves * kWave) {
+  for (int ww = 0; ww < NW; ++ww) any_bad |= sm.bad[ww] != 0;
+  for (int o = threadIdx.x; o < G * D; o += NW * kWave) {
     const int g = o / D;
     const int d = o - g * D;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, mw_lds[ww][g]);
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm.mw[ww][g]);
     float ls = 0.f, os = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float fw = mw_lds[ww][g] == -INFINITY ? 0.f : exp2_fast((mw_lds[ww][g] - M) * cs);
-        ls = fmaf(lw_lds[ww][g], fw, ls);
-        os = fmaf(acc_lds[ww][g][d], fw, os);
+      for (int ww = 0; ww < NW; ++ww) {
+        const float fw = sm.mw[ww][g] == -INFINITY ? 0.f : exp2_fast((sm.mw[ww][g] - M) * cs);
+        ls = fmaf(sm.lw[ww][g], fw, ls);
+        os = fmaf(sm.acc[ww][g][d], fw, os);
       }
     }
     float res = M == -INFINITY ? 0.f : os / ls;
@@ -311,15 +334,94 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_mfma_kernel(DecodeArgs a
   }
 }
 
+// Split path: workgroup = (kv head, sequence, partition), fastest-varying first.
+template <class ST, int D, int G>
+__global__ __launch_bounds__(PCACHE_SPLIT_WAVES* kWave) void decode_split_kernel(DecodeArgs a) {
+  constexpr int NW = PCACHE_SPLIT_WAVES;
+  __shared__ UnitLds<NW, D, G> sm;
+  int64_t id = blockIdx.x;
+  const int kvh = (int)(id % a.num_kv_heads);
+  id /= a.num_kv_heads;
+  const int s = (int)(id % a.num_seqs);
+  const int part = (int)(id / a.num_seqs);
+  const int L = a.seq_lens[s];
+  const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
+                   (int64_t)L > (int64_t)a.max_partitions * kPartition;
+  if (!bad && part * kPartition >= L) return;  // a partition past the sequence writes nothing
+  decode_unit<ST, D, G, NW, PCACHE_SPLIT_STAGES, true>(a, sm, s, kvh, part);
+}
+
+// One-pass path: persistent workgroups, units longest first, dealt in snake order.
+template <class ST, int D, int G>
+__global__ __launch_bounds__(PCACHE_ONEPASS_WAVES* kWave) void decode_onepass_kernel(DecodeArgs a) {
+  constexpr int NW = PCACHE_ONEPASS_WAVES;
+  constexpr int kThreads = NW * kWave;
+  __shared__ UnitLds<NW, D, G> sm;
+  __shared__ int order_lds[kMaxRankedSeqs];  // order_lds[rank] = sequence of that length rank
+  __shared__ int len_lds[kMaxRankedSeqs];
+
+  const int S = a.num_seqs;
+  const bool ranked = a.longest_first && S <= kMaxRankedSeqs;
+  if (ranked) {
+    for (int t = threadIdx.x; t < S; t += kThreads) len_lds[t] = a.seq_lens[t];
+    __syncthreads();
+    for (int t = threadIdx.x; t < S; t += kThreads) {
+      const int lt = len_lds[t];
+      int rank = 0;
+      for (int u = 0; u < S; ++u) {
+        const int lu = len_lds[u];
+        rank += (lu > lt) || (lu == lt && u < t);
+      }
+      order_lds[rank] = t;
+    }
+    __syncthreads();
+  }
+  const int64_t units = (int64_t)S * a.num_kv_heads;
+  const int64_t W = gridDim.x;
+  const int64_t k = blockIdx.x;
+  for (int64_t round = 0; round * W < units; ++round) {
+    const int64_t pos = round * W + ((round & 1) ? W - 1 - k : k);
+    if (pos >= units) continue;  // the last round is partial
+    const int rank = (int)(pos / a.num_kv_heads);
+    const int kvh = (int)(pos % a.num_kv_heads);
+    const int s = ranked ? order_lds[rank] : rank;
+    decode_unit<ST, D, G, NW, PCACHE_ONEPASS_STAGES, false>(a, sm, s, kvh, 0);
+    __syncthreads();  // the next unit reuses the LDS merge buffers
+  }
+}
+
+// Resident workgroups per CU for the one-pass kernel, queried once per instance.
+template <class ST, int D, int G>
+int onepass_blocks_per_cu() {
+  static int cached = 0;
+  if (!cached) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G>,
+                                                     PCACHE_ONEPASS_WAVES * kWave, 0) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      n = 1;
+    }
+    cached = n;
+  }
+  return cached;
+}
+
 template <class ST, int D, int G>
 hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
-  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * (split ? a.max_partitions : 1);
+  if (split) {
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_split_kernel<ST, D, G>), dim3((unsigned)units), dim3(PCACHE_SPLIT_WAVES * kWave), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
   if (units == 0) return hipSuccess;
-  const dim3 grid((unsigned)units), block(kWaves * kWave);
-  if (split)
-    hipLaunchKernelGGL((decode_mfma_kernel<ST, D, G, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<ST, D, G, false>), grid, block, 0, stream, a);
+  const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G>();
+  const int64_t grid = units < slots ? units : slots;
+  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G>), dim3((unsigned)grid), dim3(PCACHE_ONEPASS_WAVES * kWave), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -345,7 +447,12 @@ hipError_t launch_dim(const DecodeArgs& a, int head_size, bool split, hipStream_
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream) {
+hipError_t launch_decode_mfma(const DecodeArgs& a_in, int dtype, int head_size, bool split, hipStream_t stream) {
+  DecodeArgs a = a_in;
+#ifndef PCACHE_LONGEST_FIRST
+#define PCACHE_LONGEST_FIRST 1
+#endif
+  a.longest_first = PCACHE_LONGEST_FIRST && !split && a.num_seqs > 1;
   switch (dtype) {
     case 1: return launch_dim<F16>(a, head_size, split, stream);
     case 2: return launch_dim<BF16>(a, head_size, split, stream);

@@ -30,6 +30,7 @@ struct DecodeArgs {
   int num_seqs, num_q_heads, num_kv_heads;
   float scale_log2;    // scale * log2(e): scores are kept in the base-2 domain
   int max_partitions;  // split path only
+  int longest_first;   // one-pass path: workgroup i takes the i-th longest sequence's units
   float* exp_sums;
   float* max_logits;
   float* tmp_out;
@@ -53,5 +54,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, boo
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, hipStream_t stream);
 bool decode_supported(int dtype, int head_size, int group);
 bool reduce_supported(int head_size);
+// Compute units of the current device (cached per device; 256, MI355X's count, when
+// no device can be queried).
+int device_compute_units();
 
 }  // namespace pcache

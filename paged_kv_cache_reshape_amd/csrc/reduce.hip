@@ -8,9 +8,9 @@
 // One 256-thread workgroup per (sequence, query head).  The n (m_p, l_p) pairs are
 // read once, cooperatively: a block-wide max gives M, and each weight w_p is formed
 // once and kept in LDS (in chunks of kChunk partitions).  The lanes then split into
-// 256 / head_size partition groups; each lane accumulates one output dimension over
-// its group's partitions with independent, coalesced loads of the partial rows, and
-// the groups' sums meet in LDS.
+// 256 / (head_size/4) partition groups; each lane accumulates four output dimensions
+// (one 16-byte load per partition) over its group's partitions, with up to eight
+// loads in flight, and the groups' sums meet in LDS.
 #include <cmath>
 
 #include "device_common.h"
@@ -38,12 +38,16 @@ template <class ST>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
   __shared__ float w_lds[kChunk];
   __shared__ float red[kReduceThreads / kWave];
-  __shared__ float part_o[kReduceThreads];
+  __shared__ __align__(16) float4 part_o[kReduceThreads];
   __shared__ float part_w[kReduceThreads];
 
   const int h = blockIdx.x % a.num_q_heads;
   const int s = blockIdx.x / a.num_q_heads;
   const int D = a.head_size;
+  const int D4 = D / 4;                      // float4 columns of a partial row
+  const int groups = kReduceThreads / D4;    // partitions summed side by side
+  const int d4 = threadIdx.x % D4;
+  const int grp = threadIdx.x / D4;
   const int L = a.seq_lens[s];
   const int64_t n64 = L <= 0 ? 0 : ((int64_t)L + a.partition_size - 1) / a.partition_size;
   const bool bad = L < 0 || n64 > a.max_partitions;
@@ -57,43 +61,51 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
   for (int p = threadIdx.x; p < n; p += kReduceThreads) M = fmaxf(M, ml[p]);
   M = block_max(M, red);
 
-  // lanes t: dimension d = t % D of partition group t / D (D divides 256 for 64/128)
-  const int groups = kReduceThreads / D;
-  const int d = threadIdx.x % D;
-  const int grp = threadIdx.x / D;
-  float o = 0.f, ws = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ws = 0.f;
   for (int c0 = 0; c0 < n; c0 += kChunk) {
     const int cn = min(kChunk, n - c0);
     for (int p = threadIdx.x; p < cn; p += kReduceThreads)
       w_lds[p] = es[c0 + p] * __builtin_amdgcn_exp2f((ml[c0 + p] - M) * kLog2e);
     __syncthreads();
-    if (grp < groups) {
-      const float* row = tmp + (int64_t)c0 * D + d;
-      int p = grp;
-#pragma unroll 4
-      for (; p < cn; p += groups) {
-        const float wp = w_lds[p];
-        ws += wp;
-        o = fmaf(wp, row[(int64_t)p * D], o);
-      }
+    const float4* rows = reinterpret_cast<const float4*>(tmp + (int64_t)c0 * D) + d4;
+#pragma unroll 8
+    for (int p = grp; p < cn; p += groups) {
+      const float wp = w_lds[p];
+      const float4 t = rows[(int64_t)p * D4];
+      ws += wp;
+      o.x = fmaf(wp, t.x, o.x);
+      o.y = fmaf(wp, t.y, o.y);
+      o.z = fmaf(wp, t.z, o.z);
+      o.w = fmaf(wp, t.w, o.w);
     }
     __syncthreads();
   }
   part_o[threadIdx.x] = o;
   part_w[threadIdx.x] = ws;
   __syncthreads();
-  if (threadIdx.x < D) {
-    float to = 0.f, tw = 0.f;
+  if (threadIdx.x < D4) {
+    float4 to = make_float4(0.f, 0.f, 0.f, 0.f);
+    float tw = 0.f;
     for (int g = 0; g < groups; ++g) {
-      to += part_o[g * D + threadIdx.x];
-      tw += part_w[g * D + threadIdx.x];
+      const float4 v = part_o[g * D4 + threadIdx.x];
+      to.x += v.x;
+      to.y += v.y;
+      to.z += v.z;
+      to.w += v.w;
+      tw += part_w[g * D4 + threadIdx.x];
     }
-    const float r = bad ? NAN : (n == 0 ? 0.f : to / tw);
-    const uint32_t bits = to_storage<ST>(r);
-    if constexpr (ST::kBytes == 4)
-      static_cast<uint32_t*>(a.out)[sh * D + threadIdx.x] = bits;
-    else
-      static_cast<uint16_t*>(a.out)[sh * D + threadIdx.x] = (uint16_t)bits;
+    const float inv = 1.f / tw;
+    float r[4] = {to.x * inv, to.y * inv, to.z * inv, to.w * inv};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = bad ? NAN : (n == 0 ? 0.f : r[e]);
+      const uint32_t bits = to_storage<ST>(r[e]);
+      if constexpr (ST::kBytes == 4)
+        static_cast<uint32_t*>(a.out)[sh * D + 4 * threadIdx.x + e] = bits;
+      else
+        static_cast<uint16_t*>(a.out)[sh * D + 4 * threadIdx.x + e] = (uint16_t)bits;
+    }
   }
 }
 
@@ -102,8 +114,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, hipStream_t stream) {
   const int64_t n = (int64_t)a.num_seqs * a.num_q_heads;
   if (n == 0) return hipSuccess;
-  if (a.head_size <= 0 || a.head_size > kReduceThreads || kReduceThreads % a.head_size != 0)
-    return hipErrorInvalidValue;
+  if (!reduce_supported(a.head_size)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n), block(kReduceThreads);
   switch (dtype) {
     case 0: hipLaunchKernelGGL((reduce_kernel<F32>), grid, block, 0, stream, a); break;
@@ -115,7 +126,8 @@ hipError_t launch_reduce(const ReduceArgs& a, int dtype, hipStream_t stream) {
 }
 
 bool reduce_supported(int head_size) {
-  return head_size > 0 && head_size <= kReduceThreads && kReduceThreads % head_size == 0;
+  return head_size >= 4 && head_size % 4 == 0 && head_size / 4 <= kReduceThreads &&
+         kReduceThreads % (head_size / 4) == 0;
 }
 
 }  // namespace pcache
