@@ -36,7 +36,9 @@
  *     one buffer per block holding K for B tokens then V for B tokens
  *     ("Splitting the KV cache into 16-token blocks", section "What one block
  *     holds"): v_pool = k_pool + B*Hkv*D elements, strides {2*B*Hkv*D, Hkv*D, D}.
- *   K and V use the same strides.  Element addresses are formed in 64 bits.
+ *   K and V use the same strides.  Element addresses are formed in 64 bits; the
+ *   decode additionally needs 16 * token_stride * element size < 2^31 (else
+ *   PC_ERR_UNSUPPORTED).
  * Alignment.  The kernels move 16-byte vectors: pool bases, q, key/value rows,
  *   and every stride times the element size must be multiples of 16 bytes, and
  *   head_size * element size a multiple of 16 (else PC_ERR_UNSUPPORTED).

@@ -119,6 +119,8 @@ int pc_paged_attention_decode(void* out, const void* q, const void* k_pool, cons
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !strides16(es, {block_stride, token_stride, head_stride, (int64_t)head_size}))
     return PC_ERR_UNSUPPORTED;
+  // a block's 16 token rows of one head are addressed with 32-bit byte offsets
+  if (token_stride > INT_MAX / (kBlockTokens * es)) return PC_ERR_UNSUPPORTED;
   const int parts = split ? (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE : 1;
   if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX) return PC_ERR_UNSUPPORTED;
   if (split && parts == 0) return PC_OK;  // every sequence is empty: no partials exist

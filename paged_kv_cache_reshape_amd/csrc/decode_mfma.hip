@@ -11,21 +11,30 @@
 // * q.k as one 16x16 tile: v_mfma_f32_16x16x32_{bf16,f16} with A = the block's K
 //   (16 token rows x 32 dims per instruction) and B = the group's query heads
 //   (G <= 8 of the 16 columns, the rest zero), head_size/32 instructions per block.
-//   Lane l receives the scores of tokens 4*(l/16) + i (i < 4) for head l % 16, so a
-//   lane (row group r = l/16, head g = l%16 < G) owns the softmax of its 4 tokens
-//   and computes each probability exactly once.
-// * Online softmax with a lazy reference: the exponent reference m_ref of a (row
-//   group, head) stream moves only when a block's max exceeds it by more than
-//   2^8 (log2 domain), so most blocks skip the accumulator rescale entirely (a
+//   Lane l receives the scores of tokens 4*(l/16) + i (i < 4) for head l % 16.
+// * Online softmax per query head with a lazy reference: the exponent reference
+//   m_ref of a head moves only when a block's max exceeds it by more than 2^8
+//   (log2 domain), so most blocks skip the accumulator rescale entirely (a
 //   wave-uniform branch); the true running max is tracked alongside and the final
 //   state is expressed relative to it.
-// * The 16 probabilities of a row group and the rescale factors go through a few
-//   LDS words to the lanes that hold the row group's V slices; P.V then runs on
-//   the VALU in fp32: lane (r, i) holds 16 bytes of each of its tokens' V rows and
-//   all G heads' accumulators for those 8 (or, for head_size 64, 8 of 64) dims.
-// * A ring of STAGES register sets keeps the next STAGES-1 blocks' K/V loads in
-//   flight while one block is consumed; each wave reads its block ids 64 at a time
-//   into one VGPR.  A unit's waves merge their states once, at the end.
+// * P.V on the matrix cores too, as out^T = V^T . P^T in 16x16 tiles with
+//   v_mfma_f32_16x16x16_{bf16,f16}: the B operand P^T (16 tokens x 16 heads) is the
+//   score tile's own register layout after the exponential (lane l holds tokens
+//   4*(l/16) .. +3 of head l % 16), rounded to the storage type, so probabilities
+//   never move between lanes.  The A operand of tile j holds dims
+//   (D/16)*m + j (m < 16) of the same four tokens: lane (r, c) loads 16 (head_size
+//   128) or 8 (64) contiguous bytes of each of its four V rows (dims (D/16)*c ..)
+//   and picks element j of each with v_perm_b32.  Lane (r, c) accumulates, for
+//   head c, dims (D/16)*(4r + i) + j (i < 4, j < D/16): D/4 fp32 registers, no
+//   cross-lane reduction.
+// * Loads are buffer loads whose base is the block's tile, formed in scalar
+//   registers from the block id; the per-lane offsets are loop constants.  A ring
+//   of STAGES register sets keeps the next STAGES-1 blocks in flight while one is
+//   consumed.  The ring loop has wave-uniform control flow, issues every load
+//   unconditionally (clamped to the wave's last block) and exits only at its
+//   bottom, so the compiler waits for exactly the ring stage being consumed.
+// * A unit's block ids are staged in LDS by the whole workgroup, which checks them
+//   against the pool once; each wave reads its ids from there one block ahead.
 //
 // Work distribution:
 // * Split path: one workgroup per (sequence, kv head, 512-token partition); the
@@ -46,17 +55,38 @@ namespace {
 
 constexpr int kBlockTokens = 16;
 constexpr int kPartition = 512;
-constexpr float kLazy = 8.f;         // log2-domain slack before the exponent reference moves
-constexpr int kMaxRankedSeqs = 512;  // sequences ranked by length in-kernel (beyond: index order)
+constexpr float kLazy = 8.f;            // log2-domain slack before the exponent reference moves
+constexpr int kMaxRankedSeqs = 512;     // sequences ranked by length in-kernel (beyond: index order)
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, dword 3 for gfx9-family parts
 
-#ifndef PCACHE_ONEPASS_WAVES
-#define PCACHE_ONEPASS_WAVES 8
+// One-pass workgroup: one per CU, as many waves as the register allocation lets a
+// CU hold (3 per SIMD at head_size 128, 4 at 64), so the persistent grid fills the
+// chip with one workgroup per CU and the units dealt to it share its waves.
+#ifndef PCACHE_ONEPASS_WAVES_D128
+#define PCACHE_ONEPASS_WAVES_D128 12
 #endif
+#ifndef PCACHE_ONEPASS_WAVES_D64
+#define PCACHE_ONEPASS_WAVES_D64 16
+#endif
+template <int D>
+constexpr int onepass_waves() {
+  return D == 64 ? PCACHE_ONEPASS_WAVES_D64 : PCACHE_ONEPASS_WAVES_D128;
+}
 #ifndef PCACHE_ONEPASS_STAGES
 #define PCACHE_ONEPASS_STAGES 2
 #endif
+#ifndef PCACHE_ONEPASS_TABLE
+#define PCACHE_ONEPASS_TABLE 1024  // block ids staged in LDS at once (16384 tokens)
+#endif
 #ifndef PCACHE_SPLIT_WAVES
 #define PCACHE_SPLIT_WAVES 4
+#endif
+// waves per SIMD the register allocation must allow (the kernels fit 3 without spills)
+#ifndef PCACHE_SPLIT_OCC
+#define PCACHE_SPLIT_OCC 3
+#endif
+#ifndef PCACHE_ONEPASS_OCC
+#define PCACHE_ONEPASS_OCC 3
 #endif
 #ifndef PCACHE_SPLIT_STAGES
 #define PCACHE_SPLIT_STAGES 2
@@ -79,38 +109,89 @@ __device__ __forceinline__ f32x4_t mfma16<F16>(const uint4& a, const uint4& b, f
                                                 0, 0);
 }
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+// out^T tile += V^T tile . P^T tile (K = 16 tokens)
+template <class ST>
+__device__ __forceinline__ f32x4_t mfma_pv(const uint2& v, const uint2& p, f32x4_t c);
+template <>
+__device__ __forceinline__ f32x4_t mfma_pv<BF16>(const uint2& v, const uint2& p, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v), __builtin_bit_cast(bf16x4_t, p),
+                                                   c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4_t mfma_pv<F16>(const uint2& v, const uint2& p, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, v), __builtin_bit_cast(f16x4_t, p), c, 0, 0,
+                                               0);
+}
+
+// two floats rounded to nearest-even into one dword of the storage type
+template <class ST>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <>
+__device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  const bf16x2_v v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
+  typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+  const f16x2_v v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// a lane's slice of one V row: 8 (head_size 128) or 4 (64) 16-bit values
+template <int N>
+struct VRowOf;
+template <>
+struct VRowOf<8> {
+  using type = uint4;
+};
+template <>
+struct VRowOf<4> {
+  using type = uint2;
+};
+__device__ __forceinline__ uint32_t vword(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+__device__ __forceinline__ uint32_t vword(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int NW, int D, int G>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+template <int NW, int D, int G, int TABLE>
 struct UnitLds {
-  __align__(16) float p[NW][4][4 * G];  // probabilities of a row group (read as float4)
-  __align__(16) float a[NW][4][G];      // rescale / fold factors of a row group
-  __align__(16) float acc[NW][G][D];    // each wave's folded accumulator
+  __align__(16) float acc[NW][G][D];  // each wave's scaled accumulator
   float mw[NW][G];
   float lw[NW][G];
-  int bad[NW];
+  int ids[TABLE];  // block ids of the unit's current chunk
 };
 
 // One unit: kv head `kvh` of sequence `s`, tokens [t_begin, t_end).  All waves of
-// the workgroup call it together (it ends with a barrier-separated merge).  Writes
-// out (one pass) or the partition's partials (split).
-template <class ST, int D, int G, int NW, int STAGES, bool SPLIT>
-__device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, G>& sm, int s, int kvh, int part) {
+// the workgroup call it together (it uses block-wide barriers).  Writes out (one
+// pass) or the partition's partials (split).
+template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT>
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, G, TABLE>& sm, int s, int kvh,
+                                            int part) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
   static_assert(D == 64 || D == 128, "head size 64 or 128");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group of 1, 2, 4 or 8 query heads");
   static_assert(STAGES >= 2 && STAGES <= 4, "prefetch ring of 2..4 register sets");
-  constexpr int KS = D / 32;    // MFMA k-steps per block
-  constexpr int RL = D / 8;     // lanes per V token row (16-byte slices)
-  constexpr int RPG = 16 / RL;  // V rows per row group per load
-  constexpr int NJ = 4 / RPG;   // V loads per block
+  static_assert(!SPLIT || TABLE >= kPartition / kBlockTokens, "a partition's ids fit the table");
+  constexpr int KS = D / 32;   // q.k MFMA k-steps per block
+  constexpr int DPL = D / 16;  // V dims a lane loads per row = out^T tiles per block
+  constexpr int NT = DPL;
+  constexpr int kThreads = NW * kWave;
+  using VRow = typename VRowOf<DPL>::type;
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  const int rg = lane >> 4;     // row group: tokens 4*rg .. 4*rg+3 of a block
-  const int col = lane & 15;    // MFMA column (query head of the group) / V slice index
-  const int vsub = col / RL;    // which of the row group's rows this lane loads per V load
-  const int vchunk = col % RL;  // 16-byte slice of a V row
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int rg = lane >> 4;   // row group of the score tile: tokens 4*rg .. 4*rg+3
+  const int col = lane & 15;  // score column: query head of the group
 
   const int L = a.seq_lens[s];
   bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
@@ -121,6 +202,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const int b_end = (t_end + kBlockTokens - 1) / kBlockTokens;
   const int h0 = kvh * G;
   const float cs = a.scale_log2;  // > 0 (validated on the host)
+  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
   // B operand: query head `col` (zero for col >= G), dims 32*k + 8*rg .. +8
   uint4 qb[KS];
@@ -132,178 +214,148 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       qb[k] = col < G ? *reinterpret_cast<const uint4*>(qrow + 32 * k) : make_uint4(0, 0, 0, 0);
   }
 
-  // softmax state of stream (row group rg, head col) -- meaningful for col < G
+  // softmax state of head `col` (meaningful for col < G): the four row-group lanes
+  // of a head share m_ref; m_true and the sum cover the lane's own tokens
   float m_ref = -INFINITY, m_true = -INFINITY, lsum = 0.f;
-  float acc[G][8];
+  f32x4_t acc[NT];  // out^T tiles: acc[j][i] = head col, dim DPL*(4*rg + i) + j
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int64_t head_off = (int64_t)kvh * a.head_stride * 2;
-  const char* kbase = static_cast<const char*>(a.k_pool) + head_off;
-  const char* vbase = static_cast<const char*>(a.v_pool) + head_off;
-  const int64_t tok_bytes = a.token_stride * 2;
-  const int64_t k_lane = (int64_t)col * tok_bytes + 16 * rg;  // + 64*k per MFMA step
-  const int64_t v_lane = (int64_t)(4 * rg + vsub) * tok_bytes + 16 * vchunk;
-  const int64_t v_step = (int64_t)RPG * tok_bytes;
+  const int64_t head_bytes = (int64_t)kvh * a.head_stride * 2;
+  const char* kpool = static_cast<const char*>(a.k_pool) + head_bytes;
+  const char* vpool = static_cast<const char*>(a.v_pool) + head_bytes;
   const int64_t block_bytes = a.block_stride * 2;
+  const int tok_bytes = (int)(a.token_stride * 2);                   // < 2^27 (validated on the host)
+  const uint32_t tile_bytes = (uint32_t)(kBlockTokens * tok_bytes);  // extent of one tile's rows
+  const int k_off = col * tok_bytes + 16 * rg;                       // + 64*k per MFMA step
+  const int v_off = 4 * rg * tok_bytes + col * (2 * DPL);            // + e*tok_bytes for row 4*rg + e
+  const float lazy_raw = kLazy / cs;
 
-  // This wave takes blocks first, first + NW, ...: nw of them.
-  const int first = b_begin + w;
-  const int nw = first < b_end ? (b_end - first + NW - 1) / NW : 0;
-  int tv = 0;
-  auto fetch_table = [&](int chunk) {
-    const int idx = chunk * kWave + lane;
-    int v = 0;
-    if (idx < nw) v = table[first + idx * NW];
-    if (__builtin_amdgcn_ballot_w64(idx < nw && (v < 0 || (int64_t)v >= a.num_blocks)) != 0) bad = true;
-    tv = v;
-  };
-  int n_iter = nw;
-  if (n_iter > 0) {
-    fetch_table(0);
-    if (bad) n_iter = 0;  // a block id outside the pool: nothing is read, the outputs become NaN
-  }
+  uint4 kb[STAGES][KS];
+  VRow vb[STAGES][4];
 
-  uint4 kb[STAGES][KS], vb[STAGES][NJ];
-
-#define PC_LOAD(KD, VD, IT)                                                                          \
+  // K/V of the block with id BID into ring slot KD / VD
+#define PC_LOAD(KD, VD, BID)                                                                         \
   do {                                                                                               \
-    const int64_t boff = (int64_t)__builtin_amdgcn_readlane(tv, (IT) & (kWave - 1)) * block_bytes; \
+    const int64_t boff_ = (int64_t)(BID) * block_bytes;                                              \
+    const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, tile_bytes);                         \
+    const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                         \
     _Pragma("unroll") for (int k = 0; k < KS; ++k) KD[k] =                                          \
-        *reinterpret_cast<const uint4*>(kbase + boff + k_lane + 64 * k);                             \
-    _Pragma("unroll") for (int j = 0; j < NJ; ++j) VD[j] =                                          \
-        *reinterpret_cast<const uint4*>(vbase + boff + v_lane + j * v_step);                         \
+        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 64 * k, 0, 0)); \
+    _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                 \
+      if constexpr (DPL == 8)                                                                        \
+        VD[e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b128(vr_, v_off, e * tok_bytes, 0)); \
+      else                                                                                           \
+        VD[e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+    }                                                                                                \
   } while (0)
 
-  // consume block IT whose K/V sit in KC/VC
-#define PC_BLOCK(KC, VC, IT)                                                                         \
+  // consume the block in KC/VC whose first token is TOK0
+#define PC_BLOCK(KC, VC, TOK0)                                                                       \
   do {                                                                                               \
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};                                                                \
     _Pragma("unroll") for (int k = 0; k < KS; ++k) c = mfma16<ST>(KC[k], qb[k], c);                 \
-    const int visible = t_end - (first + (IT) * NW) * kBlockTokens;                                  \
+    const int visible = t_end - (TOK0);                                                              \
     if (visible < kBlockTokens) {                                                                    \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) c[i] = 4 * rg + i < visible ? c[i] : -INFINITY; \
-      _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                              \
-        const bool mk = 4 * rg + j * RPG + vsub >= visible;                                          \
-        VC[j].x = mk ? 0u : VC[j].x;                                                                 \
-        VC[j].y = mk ? 0u : VC[j].y;                                                                 \
-        VC[j].z = mk ? 0u : VC[j].z;                                                                 \
-        VC[j].w = mk ? 0u : VC[j].w;                                                                 \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                               \
+        const bool keep = 4 * rg + e < visible;                                                      \
+        c[e] = keep ? c[e] : -INFINITY;                                                              \
+        VC[e] = keep ? VC[e] : VRow{};                                                               \
       }                                                                                              \
     }                                                                                                \
-    const float bm = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));                                    \
-    m_true = fmaxf(m_true, bm);                                                                      \
-    const bool need = col < G && bm > m_ref + lazy_raw;                                              \
-    const bool rescale = __builtin_amdgcn_ballot_w64(need) != 0;                                     \
-    wave_lds_sync(); /* the previous block's loads of sm.p / sm.a come before these stores */        \
-    if (rescale) {                                                                                   \
-      const float alpha = need ? exp2_fast((m_ref - bm) * cs) : 1.f;                                 \
-      m_ref = need ? bm : m_ref;                                                                     \
+    const float lm = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));                                    \
+    m_true = fmaxf(m_true, lm);                                                                      \
+    if (__builtin_amdgcn_ballot_w64(col < G && lm > m_ref + lazy_raw) != 0) {                        \
+      float hm = fmaxf(lm, __shfl_xor(lm, 16));                                                      \
+      hm = fmaxf(hm, __shfl_xor(hm, 32));                                                            \
+      const bool mv = hm > m_ref + lazy_raw;                                                         \
+      const float alpha = mv ? exp2_fast((m_ref - hm) * cs) : 1.f;                                   \
+      m_ref = mv ? hm : m_ref;                                                                       \
       lsum *= alpha;                                                                                 \
-      if (col < G) sm.a[w][rg][col] = alpha;                                                         \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j) acc[j] *= alpha;                               \
     }                                                                                                \
     const float ref = m_ref == -INFINITY ? 0.f : m_ref * cs;                                         \
     float pr[4];                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(fmaf(c[i], cs, -ref));          \
+    _Pragma("unroll") for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(fmaf(c[e], cs, -ref));          \
     lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);                                                       \
-    if (col < G)                                                                                     \
-      *reinterpret_cast<float4*>(&sm.p[w][rg][4 * col]) = make_float4(pr[0], pr[1], pr[2], pr[3]);  \
-    wave_lds_sync(); /* other lanes' stores above are visible to the loads below */                 \
-    if (rescale) {                                                                                   \
-      _Pragma("unroll") for (int g = 0; g < G; ++g) {                                               \
-        const float al = sm.a[w][rg][g];                                                             \
-        _Pragma("unroll") for (int e = 0; e < 8; ++e) acc[g][e] *= al;                              \
-      }                                                                                              \
-    }                                                                                                \
-    float pv[G][4];                                                                                  \
-    _Pragma("unroll") for (int g = 0; g < G; ++g) {                                                 \
-      const float4 t4 = *reinterpret_cast<const float4*>(&sm.p[w][rg][4 * g]);                      \
-      pv[g][0] = t4.x;                                                                               \
-      pv[g][1] = t4.y;                                                                               \
-      pv[g][2] = t4.z;                                                                               \
-      pv[g][3] = t4.w;                                                                               \
-    }                                                                                                \
-    _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                                \
-      const int tj = j * RPG + vsub;                                                                 \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                               \
-        const float v = elem<ST>(VC[j], e);                                                          \
-        _Pragma("unroll") for (int g = 0; g < G; ++g) acc[g][e] = fmaf(pv[g][tj], v, acc[g][e]);    \
-      }                                                                                              \
+    const uint2 pb = make_uint2(pack2<ST>(pr[0], pr[1]), pack2<ST>(pr[2], pr[3]));                   \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                \
+      /* element j of each of the four rows: tokens 4*rg .. 4*rg+3 at dim DPL*col + j */             \
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;                                      \
+      const uint2 va = make_uint2(__builtin_amdgcn_perm(vword(VC[1], j >> 1), vword(VC[0], j >> 1), sel), \
+                                  __builtin_amdgcn_perm(vword(VC[3], j >> 1), vword(VC[2], j >> 1), sel)); \
+      acc[j] = mfma_pv<ST>(va, pb, acc[j]);                                                          \
     }                                                                                                \
   } while (0)
 
-  const float lazy_raw = kLazy / cs;
-  if (n_iter > 0) {
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-      if (st < n_iter) PC_LOAD(kb[st], vb[st], st);
-  }
-  for (int it0 = 0; it0 < n_iter; it0 += STAGES) {
-#pragma unroll
-    for (int st = 0; st < STAGES; ++st) {
-      const int it = it0 + st;
-      if (it >= n_iter) break;
-      const int nx = it + STAGES - 1;  // the block this step starts fetching
-      if (nx < n_iter) {
-        if ((nx & (kWave - 1)) == 0) {
-          fetch_table(nx / kWave);
-          if (bad) n_iter = nx;  // stop before the first chunk holding a bad id
-        }
-        if (nx < n_iter) PC_LOAD(kb[(st + STAGES - 1) % STAGES], vb[(st + STAGES - 1) % STAGES], nx);
-      }
-      PC_BLOCK(kb[st], vb[st], it);
+  // ---- the unit's blocks, TABLE ids at a time -----------------------------------------
+  __syncthreads();  // the previous unit's readers of sm are done
+  for (int cb = b_begin; cb < b_end; cb += TABLE) {
+    const int cn = min(TABLE, b_end - cb);  // blocks in this chunk
+    if (cb != b_begin) __syncthreads();     // every wave has read the previous chunk's ids
+    int anybad = 0;
+    for (int i = tid; i < cn; i += kThreads) {
+      const int v = table[cb + i];
+      sm.ids[i] = v;
+      anybad |= v < 0 || (int64_t)v >= a.num_blocks;
     }
+    if (__syncthreads_or(anybad)) {
+      bad = true;  // a block id outside the pool: nothing more is read, the outputs become NaN
+      break;
+    }
+    // this wave: chunk blocks w, w + NW, ...
+    const int nwc = __builtin_amdgcn_readfirstlane(w < cn ? (cn - w + NW - 1) / NW : 0);
+    if (nwc == 0) continue;
+    auto id_of = [&](int j) -> int { return sm.ids[w + min(j, nwc - 1) * NW]; };
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) PC_LOAD(kb[st], vb[st], __builtin_amdgcn_readfirstlane(id_of(st)));
+    int id_next = id_of(STAGES - 1);
+    // The ring turns a whole number of times: a step past the wave's last block in
+    // the chunk consumes a repeat of that block (fetched again from cache) with
+    // every token masked, which changes no state.
+    int it0 = 0;
+    do {
+#pragma unroll
+      for (int st = 0; st < STAGES; ++st) {
+        const int it = it0 + st;
+        PC_LOAD(kb[(st + STAGES - 1) % STAGES], vb[(st + STAGES - 1) % STAGES],
+                __builtin_amdgcn_readfirstlane(id_next));
+        id_next = id_of(it + STAGES);
+        // keep the scheduler from sinking the prefetch below the wait for this block
+        __builtin_amdgcn_sched_barrier(0);
+        // a step past the wave's last block of this chunk sees no token
+        PC_BLOCK(kb[st], vb[st], it < nwc ? (cb + w + it * NW) * kBlockTokens : t_end);
+      }
+      it0 += STAGES;
+    } while (it0 < nwc);
+    // retire the unconsumed tail loads (s_waitcnt vmcnt(0)) before the ring is reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 #undef PC_LOAD
 #undef PC_BLOCK
 
-  // ---- this wave: fold its 4 row groups into one state per head ---------------------
-  // reference for head g: the wave's true max M_w[g]; stream (rg, g) carries
-  // f = 2^((m_ref - M_w) * cs) <= 1
-  float mw = m_true;
-  mw = fmaxf(mw, __shfl_xor(mw, 16));
-  mw = fmaxf(mw, __shfl_xor(mw, 32));
-  const float f = m_ref == -INFINITY ? 0.f : exp2_fast((m_ref - mw) * cs);
-  float lw = lsum * f;
+  // ---- this wave: one state per head, relative to the head's true max ----------------
+  float mt = fmaxf(m_true, __shfl_xor(m_true, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const float f = m_ref == -INFINITY ? 0.f : exp2_fast((m_ref - mt) * cs);
+  float lw = lsum;
   lw += __shfl_xor(lw, 16);
   lw += __shfl_xor(lw, 32);
-  wave_lds_sync();
-  if (col < G) sm.a[w][rg][col] = f;
-  wave_lds_sync();
-  float fr[G];
+  if (col < G) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) fr[g] = sm.a[w][rg][g];
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = acc[g][e] * fr[g];
-      if constexpr (RPG == 2) x += dpp<0x128>(x);  // row_ror:8 -- the row group's other V row
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[g][e] = x;
+      for (int i = 0; i < 4; ++i) sm.acc[w][col][DPL * (4 * rg + i) + j] = acc[j][i] * f;
+    if (rg == 0) {
+      sm.mw[w][col] = mt;
+      sm.lw[w][col] = lw * f;
     }
-  if (rg == 0 && vsub == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.acc[w][g][8 * vchunk + e] = acc[g][e];
   }
-  if (rg == 0 && col < G) {
-    sm.mw[w][col] = mw;
-    sm.lw[w][col] = lw;
-  }
-  if (lane == 0) sm.bad[w] = bad ? 1 : 0;
   __syncthreads();
 
   // ---- merge the waves and write ------------------------------------------------------
-  bool any_bad = false;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) any_bad |= sm.bad[ww] != 0;
-  for (int o = threadIdx.x; o < G * D; o += NW * kWave) {
+  const bool any_bad = bad;  // block-uniform (the table check is a block-wide vote)
+  for (int o = tid; o < G * D; o += kThreads) {
     const int g = o / D;
     const int d = o - g * D;
     float M = -INFINITY;
@@ -336,9 +388,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 
 // Split path: workgroup = (kv head, sequence, partition), fastest-varying first.
 template <class ST, int D, int G>
-__global__ __launch_bounds__(PCACHE_SPLIT_WAVES* kWave) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(PCACHE_SPLIT_WAVES* kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
+void decode_split_kernel(DecodeArgs a) {
   constexpr int NW = PCACHE_SPLIT_WAVES;
-  __shared__ UnitLds<NW, D, G> sm;
+  constexpr int TABLE = kPartition / kBlockTokens;
+  __shared__ UnitLds<NW, D, G, TABLE> sm;
   int64_t id = blockIdx.x;
   const int kvh = (int)(id % a.num_kv_heads);
   id /= a.num_kv_heads;
@@ -348,15 +402,16 @@ __global__ __launch_bounds__(PCACHE_SPLIT_WAVES* kWave) void decode_split_kernel
   const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
                    (int64_t)L > (int64_t)a.max_partitions * kPartition;
   if (!bad && part * kPartition >= L) return;  // a partition past the sequence writes nothing
-  decode_unit<ST, D, G, NW, PCACHE_SPLIT_STAGES, true>(a, sm, s, kvh, part);
+  decode_unit<ST, D, G, NW, PCACHE_SPLIT_STAGES, TABLE, true>(a, sm, s, kvh, part);
 }
 
 // One-pass path: persistent workgroups, units longest first, dealt in snake order.
 template <class ST, int D, int G>
-__global__ __launch_bounds__(PCACHE_ONEPASS_WAVES* kWave) void decode_onepass_kernel(DecodeArgs a) {
-  constexpr int NW = PCACHE_ONEPASS_WAVES;
+__global__ __launch_bounds__(onepass_waves<D>() * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_ONEPASS_OCC)))
+void decode_onepass_kernel(DecodeArgs a) {
+  constexpr int NW = onepass_waves<D>();
   constexpr int kThreads = NW * kWave;
-  __shared__ UnitLds<NW, D, G> sm;
+  __shared__ UnitLds<NW, D, G, PCACHE_ONEPASS_TABLE> sm;
   __shared__ int order_lds[kMaxRankedSeqs];  // order_lds[rank] = sequence of that length rank
   __shared__ int len_lds[kMaxRankedSeqs];
 
@@ -385,8 +440,7 @@ __global__ __launch_bounds__(PCACHE_ONEPASS_WAVES* kWave) void decode_onepass_ke
     const int rank = (int)(pos / a.num_kv_heads);
     const int kvh = (int)(pos % a.num_kv_heads);
     const int s = ranked ? order_lds[rank] : rank;
-    decode_unit<ST, D, G, NW, PCACHE_ONEPASS_STAGES, false>(a, sm, s, kvh, 0);
-    __syncthreads();  // the next unit reuses the LDS merge buffers
+    decode_unit<ST, D, G, NW, PCACHE_ONEPASS_STAGES, PCACHE_ONEPASS_TABLE, false>(a, sm, s, kvh, 0);
   }
 }
 
@@ -397,7 +451,7 @@ int onepass_blocks_per_cu() {
   if (!cached) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G>,
-                                                     PCACHE_ONEPASS_WAVES * kWave, 0) != hipSuccess ||
+                                                     onepass_waves<D>() * kWave, 0) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
       n = 1;
@@ -418,9 +472,13 @@ hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
   }
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
   if (units == 0) return hipSuccess;
+#ifdef PCACHE_ONEPASS_BLOCKS_PER_CU
+  const int64_t slots = (int64_t)device_compute_units() * PCACHE_ONEPASS_BLOCKS_PER_CU;
+#else
   const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G>();
+#endif
   const int64_t grid = units < slots ? units : slots;
-  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G>), dim3((unsigned)grid), dim3(PCACHE_ONEPASS_WAVES * kWave), 0,
+  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G>), dim3((unsigned)grid), dim3(onepass_waves<D>() * kWave), 0,
                      stream, a);
   return hipGetLastError();
 }

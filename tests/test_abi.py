@@ -75,6 +75,7 @@ def _decode(lib, **kw):
     (dict(Hq=128), -2),                    # group of 16 not built
     (dict(q=ctypes.c_void_p(0x10008)), -2),  # not 16-byte aligned
     (dict(ts=100), -2),                    # stride not a multiple of 16 bytes
+    (dict(ts=1 << 26), -2),                # 16 token rows span 2 GiB: past 32-bit offsets
 ])
 def test_decode_validation(lib, kw, status):
     assert _decode(lib, **kw) == status
