@@ -13,10 +13,15 @@ is read between two visits of one copy); ``warm_cache`` reports the same step on
 one copy back to back.
 
 Prints ONE JSON line.  ``value`` is effective GB/s over the whole step: K/V bytes
-of exactly seq_len tokens per sequence plus q and out, divided by the step time.
+of exactly seq_len tokens per sequence plus q and out, divided by the step time
+(wall clock over the timed steps, bracketed by device synchronisations, with
+nothing else enqueued).
 ``roofline`` is the decode kernel alone: the same algorithmic bytes per launch over
-its average launch time, measured with HIP events on the launch stream around every
-launch in the timed region.
+its average launch time.  That time is measured with HIP events on the launch
+stream over a run of back-to-back decode launches (rotating over the pool copies,
+one event pair around the run, so the events' own dispatch cost is spread over the
+run); the per-launch event pairs inside the timed steps are reported beside it
+(``decode_kernel_us``, with median and p10/p90), and include one dispatch each.
 """
 
 from __future__ import annotations
@@ -176,30 +181,64 @@ def main():
                 ev[1].record(stream)
 
     def timed(n, rotate=True):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        """Wall time of n whole steps (barrier-free: nothing but the steps is enqueued)."""
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(n):
-            step(i if rotate else 0, evs[i])
+            step(i if rotate else 0)
         torch.cuda.synchronize()
-        el = time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    def per_launch(n):
+        """The same steps with an event pair around each decode (and reduce) launch."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            step(i, evs[i])
+        torch.cuda.synchronize()
         dec = [e[0].elapsed_time(e[1]) for e in evs]
         red = [e[1].elapsed_time(e[2]) for e in evs] if ps else [0.0] * n
-        return el, dec, red
+        return dec, red
+
+    def decode_only(i):
+        pool = pools[i % copies]
+        kw = pool.layout_kwargs()
+        if ps:
+            pc.paged_attention_decode(None, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), partition_size=ps,
+                                      exp_sums=es, max_logits=ml, tmp_out=tmp, **kw)
+        else:
+            pc.paged_attention_decode(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **kw)
+
+    def batched(fn, n):
+        """Average launch time of n back-to-back launches, one event pair on the stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for i in range(args.warmup):
         step(i)
     print(f"[bench] warmup done, timing {args.steps} steps ({path} path)", file=sys.stderr, flush=True)
-    el, dec, red = timed(args.steps)
+    el = timed(args.steps)
+    dec_b = batched(decode_only, args.steps)
+    dec, red = per_launch(args.steps)
     for i in range(3):
         step(0)
-    wel, wdec, _ = timed(args.steps, rotate=False)
+    wel = timed(args.steps, rotate=False)
+    wdec_b = batched(lambda i: decode_only(0), args.steps)
 
     eff = wl.effective_bytes()
     ms = el / args.steps * 1e3
     dec_ms = sum(dec) / len(dec)
     red_ms = sum(red) / len(red)
-    achieved = eff / (dec_ms * 1e-3) / 1e9
+    achieved = eff / (dec_b * 1e-3) / 1e9
+    q = lambda xs, f: round(float(sorted(xs)[min(len(xs) - 1, int(f * len(xs)))]) * 1e3, 2)
     traffic = stored_traffic(wl.name)
     res = {
         "metric": METRIC,
@@ -222,13 +261,16 @@ def main():
         "us_per_call": round(ms * 1e3, 2),
         "hbm_frac_step": round(eff / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "decode_kernel_us": round(dec_ms * 1e3, 2),
+        "decode_kernel_us_p10_p50_p90": [q(dec, 0.1), q(dec, 0.5), q(dec, 0.9)],
+        "decode_kernel_us_batched": round(dec_b * 1e3, 2),
         "reduce_kernel_us": round(red_ms * 1e3, 2) if ps else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_kernel (one pass)" if not ps else "decode_kernel (split)",
-                     "bytes_per_launch": eff},
+                     "kernel": "decode_split_kernel" if ps else "decode_onepass_kernel",
+                     "bytes_per_launch": eff, "launch_us": round(dec_b * 1e3, 2),
+                     "timing": "HIP events around back-to-back launches on the launch stream"},
         "warm_cache": {"ms_per_step": round(wel / args.steps * 1e3, 5),
-                       "decode_kernel_us": round(sum(wdec) / len(wdec) * 1e3, 2),
+                       "decode_kernel_us_batched": round(wdec_b * 1e3, 2),
                        "value": round(eff / (wel / args.steps) / 1e9, 2)},
     }
     if not args.no_cpu_baseline:

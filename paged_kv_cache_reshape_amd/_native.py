@@ -84,9 +84,14 @@ def _ptr(t, elem_offset: int = 0):
     return t.data_ptr() + elem_offset * t.element_size()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor, stream):
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if _raw_stream is not None:  # the current stream's handle without building a Stream object
+        return _raw_stream(t.device.index)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
