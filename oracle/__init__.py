@@ -7,7 +7,7 @@ calls anything here, and nothing here touches the GPU library.
 The arithmetic lives in ``pc_oracle.c`` (plain C loops, double precision); this
 module compiles it with gcc when the shared object is missing or older than the
 source, and marshals numpy arrays into it.  Storage types are handled as raw bit
-patterns (uint32 for fp32, uint16 for fp16/bf16).
+patterns (uint32 for fp32, uint16 for fp16/bf16, uint8 for an OCP E4M3 cache).
 
 Parity pins: every function here is pinned by tests that do not reuse its code
 (worked examples printed on the pages, closed forms, invariants, numpy and torch
@@ -61,6 +61,19 @@ def _bind(lib):
                                     i32, i32, f32, i32, i32, i32, i32]
     lib.oracle_merge.restype = i32
     lib.oracle_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32]
+    lib.oracle_write_kv8.restype = i32
+    lib.oracle_write_kv8.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, i64, i64, vp, i64, i32, i32, i32, i32,
+                                     vp, vp, i64]
+    lib.oracle_decode_kv8.restype = i32
+    lib.oracle_decode_kv8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32, i32, i32,
+                                      f32, i32, vp, vp, i64, i32]
+    lib.oracle_partials_kv8.restype = i32
+    lib.oracle_partials_kv8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32,
+                                        i32, i32, f32, i32, i32, i32, vp, vp, i64, i32]
+    lib.oracle_e4m3_decode.restype = None
+    lib.oracle_e4m3_decode.argtypes = [vp, vp, i64]
+    lib.oracle_e4m3_encode.restype = None
+    lib.oracle_e4m3_encode.argtypes = [vp, vp, i64]
     return lib
 
 
@@ -142,14 +155,43 @@ def empty_pool(wl) -> Pool:
 # operations
 # ---------------------------------------------------------------------------------
 
+def _scales(wl):
+    return (np.ascontiguousarray(wl.k_scale, dtype=np.float32), np.ascontiguousarray(wl.v_scale, dtype=np.float32),
+            int(wl.scale_stride))
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values (float64) of OCP E4M3 codes."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    load().oracle_e4m3_decode(_ptr(out), _ptr(c), c.size)
+    return out
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest OCP E4M3 codes (ties to even, saturating at 448, NaN -> 0xFF) of float32 values."""
+    v = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    load().oracle_e4m3_encode(_ptr(out), _ptr(v), v.size)
+    return out
+
+
 def write(wl, pool: Pool, key: np.ndarray, value: np.ndarray, slot_mapping: np.ndarray):
-    """Scatter ``key``/``value`` rows [T, Hkv, D] into ``pool`` through ``slot_mapping``."""
+    """Scatter ``key``/``value`` rows [T, Hkv, D] into ``pool`` through ``slot_mapping``
+    (quantised with the workload's scales when its cache is 8-bit)."""
     lib = load()
     key = np.ascontiguousarray(key)
     value = np.ascontiguousarray(value)
     slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
     T = int(slots.shape[0])
     row = wl.num_kv_heads * wl.head_size
+    if getattr(wl, "fp8", False):
+        ks, vs, st = _scales(wl)
+        rc = lib.oracle_write_kv8(pool.k_ptr(), pool.v_ptr(), pool.bound, wl.num_blocks, wl.block_stride,
+                                  wl.token_stride, wl.head_stride, _ptr(key), _ptr(value), row, row, _ptr(slots), T,
+                                  wl.num_kv_heads, wl.head_size, wl.block_size, _FMT[wl.dtype], _ptr(ks), _ptr(vs), st)
+        _check(rc, "oracle_write_kv8")
+        return pool
     rc = lib.oracle_write(pool.k_ptr(), pool.v_ptr(), pool.bound, wl.num_blocks, wl.block_stride,
                           wl.token_stride, wl.head_stride, _ptr(key), _ptr(value), row, row, _ptr(slots), T,
                           wl.num_kv_heads, wl.head_size, wl.block_size, _FMT[wl.dtype])
@@ -175,6 +217,15 @@ def decode(wl, pool: Pool, q: np.ndarray | None = None, seq_lens=None, block_tab
     bt = np.ascontiguousarray(wl.block_tables if block_tables is None else block_tables, dtype=np.int32)
     S = int(sl.shape[0])
     out = np.zeros((S, wl.num_q_heads, wl.head_size), dtype=np.float64)
+    if getattr(wl, "fp8", False):
+        ks, vs, st = _scales(wl)
+        rc = lib.oracle_decode_kv8(_ptr(out), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound, wl.num_blocks,
+                                   wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt), int(bt.shape[1]),
+                                   _ptr(sl), S, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size,
+                                   float(wl.scale if scale is None else scale), _FMT[wl.dtype], _ptr(ks), _ptr(vs),
+                                   st, _nthreads(nthreads))
+        _check(rc, "oracle_decode_kv8")
+        return out
     rc = lib.oracle_decode(_ptr(out), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound, wl.num_blocks,
                            wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt), int(bt.shape[1]), _ptr(sl), S,
                            wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size,
@@ -198,6 +249,15 @@ def partials(wl, pool: Pool, partition_size: int, max_partitions: int | None = N
     tmp = np.full((S, H, max_partitions, D), fill, dtype=np.float64)
     ml = np.full((S, H, max_partitions), fill, dtype=np.float64)
     es = np.full((S, H, max_partitions), fill, dtype=np.float64)
+    if getattr(wl, "fp8", False):
+        ks, vs, st = _scales(wl)
+        rc = lib.oracle_partials_kv8(_ptr(tmp), _ptr(ml), _ptr(es), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound,
+                                     wl.num_blocks, wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt),
+                                     int(bt.shape[1]), _ptr(sl), S, H, wl.num_kv_heads, D, wl.block_size,
+                                     float(wl.scale), partition_size, max_partitions, _FMT[wl.dtype], _ptr(ks),
+                                     _ptr(vs), st, _nthreads(nthreads))
+        _check(rc, "oracle_partials_kv8")
+        return tmp, ml, es
     rc = lib.oracle_partials(_ptr(tmp), _ptr(ml), _ptr(es), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound,
                              wl.num_blocks, wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt),
                              int(bt.shape[1]), _ptr(sl), S, H, wl.num_kv_heads, D, wl.block_size, float(wl.scale),

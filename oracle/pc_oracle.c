@@ -40,7 +40,19 @@
  *                    output o_p; the merge forms M = max m_p, w_p = l_p e^(m_p - M),
  *                    out = sum w_p o_p / sum w_p.
  *
- * Storage formats: 0 = fp32, 1 = fp16, 2 = bf16 (raw bits in memory).
+ *  oracle_write_kv8, oracle_decode_kv8, oracle_partials_kv8 -- the same with an
+ *                    8-bit floating-point cache ("Inside vLLM CUDA Kernels", Part 2,
+ *                    "Why Layout and Quantization Scale Produce Two Copy Paths":
+ *                    k_scale / v_scale, one shared scale when kv_scale_stride is 0,
+ *                    else head h uses scale[h * kv_scale_stride]; "vLLM 源码完全拆解
+ *                    （七）", 参数与内存布局: the kernel converts the quantised cache
+ *                    with k_scale / v_scale when it loads it).  The pages name no
+ *                    format; this oracle takes OCP E4M3 (see e4m3_to_double).  The
+ *                    write stores code(x / scale), x / scale computed in binary32;
+ *                    the decode reads code value * scale, in double.
+ *
+ * Storage formats: 0 = fp32, 1 = fp16, 2 = bf16 (raw bits in memory); caches may
+ * also be 3 = OCP FP8 E4M3 (one byte per element).
  * Return codes: 0 ok, -1 invalid argument, -2 a data value points outside the
  * pool (slot, block id or sequence length) -- the oracle refuses to read or write
  * out of range, so a test that passes proves no such access was needed.
@@ -82,7 +94,44 @@ static double bf16_to_double(uint16_t b) {
     return (double)f;
 }
 
+/* OCP 8-bit floating point, E4M3 variant: sign bit, 4 exponent bits (bias 7), 3
+ * mantissa bits.  Exponent field 0 holds subnormals m/8 * 2^-6; there are no
+ * infinities; exponent 1111 with mantissa 111 is NaN, so the largest finite
+ * magnitude is 1.75 * 2^8 = 448. */
+static double e4m3_to_double(uint8_t c) {
+    int sign = c >> 7;
+    int e = (c >> 3) & 0xf;
+    int m = c & 7;
+    if (e == 0xf && m == 7)
+        return NAN;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return sign ? -v : v;
+}
+
+/* The E4M3 code nearest to y, found by comparing against every finite positive
+ * code (codes 0..0x7E increase with their value); a tie goes to the code with the
+ * even mantissa.  Magnitudes of 448 and above (infinities included) give +-448;
+ * NaN gives 0xFF. */
+static uint8_t e4m3_from_float(float y) {
+    if (isnan(y))
+        return 0xff;
+    uint8_t sign = signbit(y) ? 0x80 : 0;
+    double a = fabs((double)y);
+    if (a >= 448.0)
+        return sign | 0x7e;
+    int lo = 0; /* largest code whose value is <= a */
+    for (int c = 1; c <= 0x7e; ++c)
+        if (e4m3_to_double((uint8_t)c) <= a)
+            lo = c;
+    double below = a - e4m3_to_double((uint8_t)lo);
+    double above = e4m3_to_double((uint8_t)(lo + 1)) - a;
+    int c = below < above ? lo : above < below ? lo + 1 : ((lo & 1) ? lo + 1 : lo);
+    return sign | (uint8_t)c;
+}
+
 static double load_elem(const void *base, int64_t idx, int fmt) {
+    if (fmt == 3)
+        return e4m3_to_double(((const uint8_t *)base)[idx]);
     if (fmt == 0) {
         float f;
         memcpy(&f, (const char *)base + idx * 4, 4);
@@ -129,6 +178,44 @@ int oracle_write(void *k_pool, void *v_pool, int64_t pool_elems, int64_t num_blo
     return OR_OK;
 }
 
+/* The write into an E4M3 cache: element x of head h becomes the code of
+ * x / scale[h * scale_stride], the division done in binary32 (x is exact in it). */
+int oracle_write_kv8(uint8_t *k_pool, uint8_t *v_pool, int64_t pool_elems, int64_t num_blocks,
+                     int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                     const void *key, const void *value, int64_t key_row_stride, int64_t value_row_stride,
+                     const int64_t *slot_mapping, int64_t num_tokens, int num_kv_heads, int head_size,
+                     int block_size, int src_fmt, const float *k_scale, const float *v_scale,
+                     int64_t scale_stride) {
+    if (!esize_of(src_fmt) || !k_pool || !v_pool || num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 ||
+        block_size <= 0 || scale_stride < 0 || !k_scale || !v_scale)
+        return OR_EINVAL;
+    if (num_tokens > 0 && (!key || !value || !slot_mapping))
+        return OR_EINVAL;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0)
+            continue; /* padding: no destination */
+        int64_t blk = slot / block_size;
+        int64_t off = slot % block_size;
+        if (blk >= num_blocks)
+            return OR_ERANGE;
+        for (int h = 0; h < num_kv_heads; ++h) {
+            int64_t dst = blk * block_stride + off * token_stride + (int64_t)h * head_stride;
+            if (dst < 0 || dst + head_size > pool_elems)
+                return OR_ERANGE;
+            float ks = k_scale[(int64_t)h * scale_stride];
+            float vs = v_scale[(int64_t)h * scale_stride];
+            for (int d = 0; d < head_size; ++d) {
+                float kx = (float)load_elem(key, t * key_row_stride + (int64_t)h * head_size + d, src_fmt);
+                float vx = (float)load_elem(value, t * value_row_stride + (int64_t)h * head_size + d, src_fmt);
+                k_pool[dst + d] = e4m3_from_float(kx / ks);
+                v_pool[dst + d] = e4m3_from_float(vx / vs);
+            }
+        }
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* decode                                                                     */
 /* ------------------------------------------------------------------------- */
@@ -141,7 +228,10 @@ typedef struct {
     const int32_t *seq_lens;
     int num_seqs, num_q_heads, num_kv_heads, head_size, block_size;
     double scale;
-    int fmt;
+    int fmt;                         /* q (and out) */
+    int kv_fmt;                      /* the pool */
+    const float *k_scale, *v_scale;  /* E4M3 pool: head kv uses scale[kv * scale_stride] */
+    int64_t scale_stride;
     int partition_size; /* 0: whole sequence (decode); > 0: partials */
     int max_partitions;
     /* outputs */
@@ -174,9 +264,14 @@ static int gather_rows(const job_t *j, int s, int kv, int t0, int t1, double *K,
         int64_t base = phys * j->block_stride + (int64_t)off * j->token_stride + (int64_t)kv * j->head_stride;
         if (base < 0 || base + j->head_size > j->pool_elems)
             return OR_ERANGE;
+        double ks = 1.0, vs = 1.0;
+        if (j->kv_fmt == 3) {
+            ks = (double)j->k_scale[(int64_t)kv * j->scale_stride];
+            vs = (double)j->v_scale[(int64_t)kv * j->scale_stride];
+        }
         for (int d = 0; d < j->head_size; ++d) {
-            K[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->k_pool, base + d, j->fmt);
-            V[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->v_pool, base + d, j->fmt);
+            K[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->k_pool, base + d, j->kv_fmt) * ks;
+            V[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->v_pool, base + d, j->kv_fmt) * vs;
         }
     }
     return OR_OK;
@@ -372,6 +467,7 @@ int oracle_decode(double *out, const void *q, const void *k_pool, const void *v_
     j.block_size = block_size;
     j.scale = (double)scale;
     j.fmt = fmt;
+    j.kv_fmt = fmt;
     j.out = out;
     j.n_items = (int64_t)num_seqs * num_q_heads;
     return run_job(&j, nthreads);
@@ -408,6 +504,7 @@ int oracle_partials(double *tmp_out, double *max_logits, double *exp_sums, const
     j.block_size = block_size;
     j.scale = (double)scale;
     j.fmt = fmt;
+    j.kv_fmt = fmt;
     j.partition_size = partition_size;
     j.max_partitions = max_partitions;
     j.tmp_out = tmp_out;
@@ -456,4 +553,103 @@ int oracle_merge(double *out, const double *tmp_out, const double *max_logits, c
         }
     }
     return OR_OK;
+}
+
+/* The decode and the partials over an E4M3 pool (q, out in fmt). */
+int oracle_decode_kv8(double *out, const void *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t pool_elems,
+                      int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                      const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_size, int block_size, float scale, int fmt,
+                      const float *k_scale, const float *v_scale, int64_t scale_stride, int nthreads) {
+    int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                          head_size, block_size, max_blocks_per_seq, fmt);
+    if (rc)
+        return rc;
+    if ((num_seqs > 0 && !out) || !k_scale || !v_scale || scale_stride < 0)
+        return OR_EINVAL;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.q = q;
+    j.k_pool = k_pool;
+    j.v_pool = v_pool;
+    j.pool_elems = pool_elems;
+    j.num_blocks = num_blocks;
+    j.block_stride = block_stride;
+    j.token_stride = token_stride;
+    j.head_stride = head_stride;
+    j.block_tables = block_tables;
+    j.max_blocks_per_seq = max_blocks_per_seq;
+    j.seq_lens = seq_lens;
+    j.num_seqs = num_seqs;
+    j.num_q_heads = num_q_heads;
+    j.num_kv_heads = num_kv_heads;
+    j.head_size = head_size;
+    j.block_size = block_size;
+    j.scale = (double)scale;
+    j.fmt = fmt;
+    j.kv_fmt = 3;
+    j.k_scale = k_scale;
+    j.v_scale = v_scale;
+    j.scale_stride = scale_stride;
+    j.out = out;
+    j.n_items = (int64_t)num_seqs * num_q_heads;
+    return run_job(&j, nthreads);
+}
+
+int oracle_partials_kv8(double *tmp_out, double *max_logits, double *exp_sums, const void *q, const uint8_t *k_pool,
+                        const uint8_t *v_pool, int64_t pool_elems, int64_t num_blocks, int64_t block_stride,
+                        int64_t token_stride, int64_t head_stride, const int32_t *block_tables,
+                        int max_blocks_per_seq, const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_size, int block_size, float scale, int partition_size,
+                        int max_partitions, int fmt, const float *k_scale, const float *v_scale,
+                        int64_t scale_stride, int nthreads) {
+    int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                          head_size, block_size, max_blocks_per_seq, fmt);
+    if (rc)
+        return rc;
+    if (partition_size <= 0 || max_partitions < 0 || (num_seqs > 0 && (!tmp_out || !max_logits || !exp_sums)) ||
+        !k_scale || !v_scale || scale_stride < 0)
+        return OR_EINVAL;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.q = q;
+    j.k_pool = k_pool;
+    j.v_pool = v_pool;
+    j.pool_elems = pool_elems;
+    j.num_blocks = num_blocks;
+    j.block_stride = block_stride;
+    j.token_stride = token_stride;
+    j.head_stride = head_stride;
+    j.block_tables = block_tables;
+    j.max_blocks_per_seq = max_blocks_per_seq;
+    j.seq_lens = seq_lens;
+    j.num_seqs = num_seqs;
+    j.num_q_heads = num_q_heads;
+    j.num_kv_heads = num_kv_heads;
+    j.head_size = head_size;
+    j.block_size = block_size;
+    j.scale = (double)scale;
+    j.fmt = fmt;
+    j.kv_fmt = 3;
+    j.k_scale = k_scale;
+    j.v_scale = v_scale;
+    j.scale_stride = scale_stride;
+    j.partition_size = partition_size;
+    j.max_partitions = max_partitions;
+    j.tmp_out = tmp_out;
+    j.max_logits = max_logits;
+    j.exp_sums = exp_sums;
+    j.n_items = (int64_t)num_seqs * num_q_heads * max_partitions;
+    return run_job(&j, nthreads);
+}
+
+/* Element-wise access for tests: the value of E4M3 codes, and the codes of floats. */
+void oracle_e4m3_decode(double *out, const uint8_t *codes, int64_t n) {
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = e4m3_to_double(codes[i]);
+}
+
+void oracle_e4m3_encode(uint8_t *out, const float *x, int64_t n) {
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = e4m3_from_float(x[i]);
 }

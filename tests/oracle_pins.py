@@ -8,7 +8,9 @@ the oracle disagrees with something it does not compute itself:
 * invariants (any physical placement of the blocks, unread memory, padding rows);
 * independent references (numpy and torch float64 dense attention on the contiguous
   history, a tile-wise online softmax, a pure-Python per-token brute force);
-* the split identity (per-partition partials merged = the whole sequence).
+* the split identity (per-partition partials merged = the whole sequence);
+* for the 8-bit cache: the OCP E4M3 landmarks and torch's float8_e4m3fn converter,
+  and dense attention on dequantised rows.
 
 ``tests/test_oracle_pins.py`` runs them; ``tests/test_oracle_mutants.py`` plants
 mistakes in copies of the oracle and requires some pin to fail for each.
@@ -27,7 +29,7 @@ import numpy as np
 import brute
 import oracle
 from helpers import GOLDEN, bits_to_f64, dense_numpy, f64_to_bits, online_tiles_numpy
-from workloads import custom, make_config, nan_bits
+from workloads import custom, fp8_variant, make_config, nan_bits
 
 B = 16
 
@@ -447,10 +449,131 @@ def pin_split_identity():
         assert np.abs(merged - dense).max() < 1e-13, P
 
 
+# ---------------------------------------------------------------------------------
+# 8-bit (OCP E4M3) cache
+# ---------------------------------------------------------------------------------
+
+def _torch_e4m3_value(codes: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _torch_e4m3_code(x32: np.ndarray) -> np.ndarray:
+    """torch's nearest-even float8_e4m3fn conversion, after clamping to +-448 (torch
+    maps larger magnitudes to NaN)."""
+    import torch
+    y = np.where(np.isnan(x32), x32, np.clip(x32, -448.0, 448.0)).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    codes[np.isnan(x32)] = 0xFF
+    return codes
+
+
+def pin_e4m3_values():
+    """Every code's value: the OCP definition's landmarks and torch's float8_e4m3fn."""
+    codes = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3_decode(codes)
+    t = _torch_e4m3_value(codes)
+    assert np.array_equal(np.isnan(v), np.isnan(t)) and np.array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+    assert np.isnan(v[[0x7F, 0xFF]]).all() and np.isnan(v).sum() == 2  # no infinities, one NaN per sign
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0xFE] == -448.0  # 1.75 * 2^8 is the largest
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9 and v[0x08] == 2.0 ** -6  # subnormals, min normal
+    assert v[0x00] == 0.0 and np.signbit(v[0x80])
+    assert (np.diff(v[:0x7F]) > 0).all()  # codes 0..0x7E increase
+
+
+def pin_e4m3_rounding():
+    """Nearest code, ties to the even mantissa, saturation at 448, NaN -> 0xFF."""
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.e4m3_decode(finite).astype(np.float32)
+    back = oracle.e4m3_encode(vals)
+    assert np.array_equal(back[vals != 0], finite[vals != 0])  # every finite value maps to its own code
+    pos = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)  # exact in binary32
+    tie = oracle.e4m3_encode(mid)
+    lo = np.arange(0x7E)
+    assert np.array_equal(tie, np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8))
+    up = oracle.e4m3_encode(np.nextafter(mid, np.float32(1e9)))
+    down = oracle.e4m3_encode(np.nextafter(mid, np.float32(-1e9)))
+    assert np.array_equal(up, lo + 1) and np.array_equal(down, lo)
+    big = np.array([448, 449, 463.9, 464, 480, 1e4, 3e38, np.inf], dtype=np.float32)
+    assert (oracle.e4m3_encode(big) == 0x7E).all() and (oracle.e4m3_encode(-big) == 0xFE).all()
+    assert oracle.e4m3_encode(np.array([np.nan], dtype=np.float32))[0] == 0xFF
+    x = (np.random.default_rng(3).standard_normal(50000) * 60).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_encode(x), _torch_e4m3_code(x))
+
+
+@functools.lru_cache(maxsize=None)
+def _fp8_wl(per_head=True):
+    # small scales: values beyond ~2.2 sigma saturate, so that branch is exercised
+    return fp8_variant(custom(21, "bf16", 8, 2, 64, [1, 16, 17, 40, 530], extra_pad_rows=1), per_head=per_head,
+                       lo=0.005, hi=0.02)
+
+
+def _quantised_history(w):
+    """Per sequence [L, Hkv, D]: codes of the logical history, by torch's converter."""
+    ks, vs = w.k_scale.astype(np.float32), w.v_scale.astype(np.float32)
+    kh = np.repeat(ks, w.num_kv_heads) if w.scale_stride == 0 else ks
+    vh = np.repeat(vs, w.num_kv_heads) if w.scale_stride == 0 else vs
+    out = []
+    for s in range(w.num_seqs):
+        K = bits_to_f64(w.logical_k(s), w.dtype).astype(np.float32)
+        V = bits_to_f64(w.logical_v(s), w.dtype).astype(np.float32)
+        out.append((_torch_e4m3_code(K / kh[None, :, None]), _torch_e4m3_code(V / vh[None, :, None]), kh, vh))
+    return out
+
+
+def pin_kv8_write():
+    """The 8-bit write stores the code of x / scale of its head (torch's converter), in
+    the slot the flattening names; nothing else changes."""
+    sat = 0
+    for per_head in (True, False):
+        w = _fp8_wl(per_head)
+        pool = oracle.filled_pool(w)
+        hist = _quantised_history(w)
+        written = np.zeros(w.pool_elems, bool)
+        for s in range(w.num_seqs):
+            kc, vc, _, _ = hist[s]
+            for t in range(int(w.seq_lens[s])):
+                phys = int(w.block_tables[s, t // B])
+                for h in range(w.num_kv_heads):
+                    base = phys * w.block_stride + (t % B) * w.token_stride + h * w.head_stride
+                    assert np.array_equal(pool.k[base:base + w.head_size], kc[t, h]), (per_head, s, t, h)
+                    assert np.array_equal(pool.v[base:base + w.head_size], vc[t, h]), (per_head, s, t, h)
+                    written[base:base + w.head_size] = True
+        assert (pool.k[~written] == 0x7F).all() and (pool.v[~written] == 0x7F).all()
+        sat += sum(int((np.abs(oracle.e4m3_decode(c)) == 448).sum()) for kc, vc, _, _ in hist for c in (kc, vc))
+    assert sat > 0  # the scales make some values saturate: that branch is exercised
+
+
+def pin_kv8_decode():
+    """Decode over the 8-bit pool = dense attention on code value * scale (numpy),
+    q = 0 gives the mean of the dequantised V, and the partials merge to it."""
+    w = _fp8_wl(True)
+    pool = oracle.filled_pool(w)
+    out = oracle.decode(w, pool)
+    hist = _quantised_history(w)
+    q = bits_to_f64(w.q, w.dtype)
+    G = w.num_q_heads // w.num_kv_heads
+    zero = oracle.decode(w, pool, q=np.zeros_like(w.q))
+    for s in range(w.num_seqs):
+        kc, vc, kh, vh = hist[s]
+        K = _torch_e4m3_value(kc) * kh[None, :, None].astype(np.float64)
+        V = _torch_e4m3_value(vc) * vh[None, :, None].astype(np.float64)
+        for h in range(w.num_q_heads):
+            x = float(w.scale) * (K[:, h // G] @ q[s, h])
+            e = np.exp(x - x.max())
+            assert np.abs(out[s, h] - e @ V[:, h // G] / e.sum()).max() < 1e-12, (s, h)
+            assert np.abs(zero[s, h] - V[:, h // G].mean(axis=0)).max() < 1e-12, (s, h)
+    for P in (16, 512):
+        tmp, ml, es = oracle.partials(w, pool, P)
+        assert np.abs(oracle.merge(tmp, ml, es, w.seq_lens, P) - out).max() < 1e-13
+
+
 PINS = [
     pin_slot_write, pin_slot_read, pin_invariant_line, pin_gqa_mapping, pin_worked_decode,
     pin_combined_block_layout, pin_one_token_exact, pin_special_values_exact, pin_zero_query_mean,
     pin_equal_keys_mean, pin_two_tokens_sigmoid, pin_huge_logits, pin_placement_invariance,
     pin_negative_slot_skipped, pin_unread_memory, pin_table_padding, pin_write_out_of_range,
     pin_numpy_dense, pin_torch_sdpa, pin_online_tiles, pin_brute_force, pin_split_identity,
+    pin_e4m3_values, pin_e4m3_rounding, pin_kv8_write, pin_kv8_decode,
 ]

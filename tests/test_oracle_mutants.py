@@ -24,8 +24,8 @@ MUTANTS = {
     "negative_slot_written": ("if (slot < 0)\n            continue;", "if (slot < -1)\n            continue;"),
     "read_logical_block": ("int lb = t / j->block_size;", "int lb = t / (2 * j->block_size);"),
     "read_offset_shift": ("int off = t % j->block_size;", "int off = (t + 1) % j->block_size;"),
-    "value_from_key_pool": ("V[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->v_pool, base + d, j->fmt);",
-                            "V[(int64_t)(t - t0) * j->head_size + d] = load_elem(j->k_pool, base + d, j->fmt);"),
+    "value_from_key_pool": ("load_elem(j->v_pool, base + d, j->kv_fmt) * vs;",
+                            "load_elem(j->k_pool, base + d, j->kv_fmt) * vs;"),
     "query_head_swapped": ("qv[d] = load_elem(j->q, ((int64_t)s * j->num_q_heads + h) * D + d, j->fmt);",
                            "qv[d] = load_elem(j->q, ((int64_t)s * j->num_q_heads + (h ^ 1)) * D + d, j->fmt);"),
     "scale_dropped": ("x[t] = scale * dot;", "x[t] = dot;"),
@@ -41,6 +41,15 @@ MUTANTS = {
     "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
     "f16_exponent_bias": ("v = ldexp((double)(m + 1024), e - 25);", "v = ldexp((double)(m + 1024), e - 24);"),
     "f16_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "e4m3_exponent_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 9)"),
+    "e4m3_subnormal_scale": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "e4m3_ties_to_odd": ("((lo & 1) ? lo + 1 : lo)", "((lo & 1) ? lo : lo + 1)"),
+    "e4m3_overflow_to_nan": ("if (a >= 448.0)\n        return sign | 0x7e;", "if (a >= 464.0)\n        return sign | 0x7f;"),
+    "kv8_scale_multiplied": ("k_pool[dst + d] = e4m3_from_float(kx / ks);", "k_pool[dst + d] = e4m3_from_float(kx * ks);"),
+    "kv8_write_scale_head0": ("float vs = v_scale[(int64_t)h * scale_stride];", "float vs = v_scale[0];"),
+    "kv8_read_scale_dropped": ("ks = (double)j->k_scale[(int64_t)kv * j->scale_stride];", "ks = 1.0;"),
+    "kv8_read_v_scale_from_k": ("vs = (double)j->v_scale[(int64_t)kv * j->scale_stride];",
+                                "vs = (double)j->k_scale[(int64_t)kv * j->scale_stride];"),
 }
 
 
@@ -48,7 +57,8 @@ def _build_mutant(name, tmp_path):
     old, new = MUTANTS[name]
     with open(SRC) as f:
         text = f.read()
-    assert text.count(old) == 1, f"mutation site for {name} is not unique/present"
+    # a site shared by the plain and the 8-bit write is mutated in both
+    assert text.count(old) >= 1, f"mutation site for {name} is not present"
     src = tmp_path / f"{name}.c"
     src.write_text(text.replace(old, new))
     out = tmp_path / f"{name}.so"

@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     Workload,
     custom,
     dtype_nbytes,
+    fp8_variant,
     make_config,
     nan_bits,
 )

@@ -41,7 +41,7 @@ from __future__ import annotations
 import math
 import os
 from concurrent.futures import ThreadPoolExecutor
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -152,6 +152,12 @@ class Workload:
     bank_v: np.ndarray = field(repr=False, default=None)
     prefix_blocks: int = 0
     notes: str = ""
+    # 8-bit cache: kv_dtype 'fp8' stores OCP E4M3 codes; head h of K uses
+    # k_scale[h * scale_stride] (scale_stride 0: one shared scale), V likewise
+    kv_dtype: str = ""
+    k_scale: np.ndarray = field(repr=False, default=None)  # float32
+    v_scale: np.ndarray = field(repr=False, default=None)
+    scale_stride: int = 0
 
     # ----- sizes -------------------------------------------------------------------
     @property
@@ -170,9 +176,17 @@ class Workload:
     def bits_dtype(self):
         return _BITS_NP[self.dtype]
 
+    @property
+    def fp8(self) -> bool:
+        return self.kv_dtype == "fp8"
+
+    @property
+    def kv_esize(self) -> int:
+        return 1 if self.fp8 else self.esize
+
     def kv_bytes(self) -> int:
         """K and V bytes of exactly seq_len tokens per sequence (no block padding)."""
-        return int(self.seq_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_size * 2 * self.esize
+        return int(self.seq_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_size * 2 * self.kv_esize
 
     def qo_bytes(self) -> int:
         return self.num_seqs * self.num_q_heads * self.head_size * 2 * self.esize
@@ -190,11 +204,13 @@ class Workload:
                 b = int(self.block_tables[s, j])
                 tok = min(self.block_size, L - j * self.block_size)
                 used[b] = max(used.get(b, 0), tok)
-        return sum(used.values()) * self.num_kv_heads * self.head_size * 2 * self.esize
+        return sum(used.values()) * self.num_kv_heads * self.head_size * 2 * self.kv_esize
 
     # ----- memory images ---------------------------------------------------------
     def nan_pool(self) -> np.ndarray:
-        """One pool buffer (element bits) filled with the quiet-NaN pattern."""
+        """One pool buffer (element bits) filled with the quiet-NaN pattern (0x7F for E4M3)."""
+        if self.fp8:
+            return np.full(self.pool_elems, 0x7F, dtype=np.uint8)
         return np.full(self.pool_elems, nan_bits(self.dtype), dtype=self.bits_dtype)
 
     def logical_k(self, s: int) -> np.ndarray:
@@ -468,3 +484,16 @@ def custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head_size
     return _assemble(name=name, seed=seed, rng=rng, dtype=dtype, Hq=num_q_heads, Hkv=num_kv_heads, D=head_size,
                      layout=layout, num_blocks=num_blocks, seq_lens=seq_lens, block_tables=table,
                      prefix_blocks=prefix_blocks, pad_count=pad_count, extra_pad_rows=extra_pad_rows)
+
+
+def fp8_variant(wl: Workload, per_head: bool = True, lo: float = 0.008, hi: float = 0.03) -> Workload:
+    """The same workload over an 8-bit (OCP E4M3) cache: the history and the step's
+    rows (still in ``wl.dtype``) are quantised by the write.  Scales are float32 drawn
+    uniformly in [lo, hi) from stream 5 -- one per kv head (per_head) or one shared;
+    with standard-normal values a few |x| / scale exceed 448 and saturate."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 5])))
+    n = wl.num_kv_heads if per_head else 1
+    ks = rng.uniform(lo, hi, size=n).astype(np.float32)
+    vs = rng.uniform(lo, hi, size=n).astype(np.float32)
+    name = wl.name.replace(wl.dtype, f"{wl.dtype}q_fp8e4m3", 1) if wl.dtype in wl.name else wl.name + "_fp8e4m3"
+    return replace(wl, name=name, kv_dtype="fp8", k_scale=ks, v_scale=vs, scale_stride=1 if per_head else 0)
