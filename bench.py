@@ -4,7 +4,9 @@ A step is the whole path over one batch: the write of each sequence's new token
 into the paged pool (pc_reshape_and_cache), the planner, and the decode (one pass,
 or the 512-token split plus its log-sum-exp reduce).  The default workload is
 64 sequences of 512..2048 tokens, 32 query / 8 KV heads, head size 128, bf16, one
-pass (the GQA decode the throughput target is quoted on).
+pass (the GQA decode the throughput target is quoted on).  ``--kv fp8`` runs the
+same step over an 8-bit (OCP E4M3) cache with per-kv-head scales: the write
+quantises, the decode reads one byte per K/V element.
 
 Inputs are resident in HBM before timing starts.  To keep the K/V stream honest
 with respect to the 256 MB last-level cache, the step rotates over ``--copies``
@@ -52,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--path", choices=["plan", "single", "split"], default="plan")
+    ap.add_argument("--kv", choices=["native", "fp8"], default="native",
+                    help="cache element type: the query's type, or OCP E4M3 codes with per-kv-head scales")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -123,15 +127,17 @@ def main():
 
     import gpu_harness as gh
     import paged_kv_cache_reshape_amd as pc
-    from workloads import make_config
+    from workloads import fp8_variant, make_config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     wl = make_config(args.config)
+    if args.kv == "fp8":
+        wl = fp8_variant(wl)
     S, Hq, D = wl.q.shape
-    per_copy = 2 * wl.pool_elems * wl.esize if wl.layout != "combined" else wl.pool_elems * wl.esize
+    per_copy = (2 if wl.layout != "combined" else 1) * wl.pool_elems * wl.kv_esize
     copies = args.copies or max(1, min(8, -(-(1 << 30) // max(1, wl.kv_bytes())) + 1))
     copies = max(1, min(copies, int(64e9 // per_copy)))
     print(f"[bench] {wl.name}: {wl.kv_bytes() / 1e6:.1f} MB K/V per step, {copies} pool copies", file=sys.stderr,
@@ -152,33 +158,47 @@ def main():
     else:
         ps, P = 0, 1
     path = "split" if ps else "single"
+    es = ml = tmp = None
     if ps:
         es = torch.empty((S, Hq, P), device=dev)
         ml = torch.empty((S, Hq, P), device=dev)
         tmp = torch.empty((S, Hq, P, D), device=dev)
     stream = torch.cuda.current_stream(dev)
+    fp8 = wl.fp8
+    split_kw = dict(partition_size=ps, exp_sums=es, max_logits=ml, tmp_out=tmp) if ps else {}
+
+    def write(pool):
+        if fp8:
+            pc.reshape_and_cache_fp8(key, value, pool.k, pool.v, slots, pool.k_scale, pool.v_scale,
+                                     **pool.layout_kwargs(), **pool.scale_kwargs())
+        else:
+            pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **pool.layout_kwargs())
+
+    def decode(pool):
+        o = None if ps else out
+        if fp8:
+            pc.paged_attention_decode_fp8(o, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                          pool.k_scale, pool.v_scale, num_kv_heads=wl.num_kv_heads,
+                                          scale=float(wl.scale), **pool.layout_kwargs(), **pool.scale_kwargs(),
+                                          **split_kw)
+        else:
+            pc.paged_attention_decode(o, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pool.layout_kwargs(),
+                                      **split_kw)
 
     def step(i, ev=None):
         pool = pools[i % copies]
-        kw = pool.layout_kwargs()
-        pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **kw)
+        write(pool)
         pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, gh.TORCH_DT[wl.dtype])
         if ev is not None:
             ev[0].record(stream)
+        decode(pool)
+        if ev is not None:
+            ev[1].record(stream)
         if ps:
-            pc.paged_attention_decode(None, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
-                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), partition_size=ps,
-                                      exp_sums=es, max_logits=ml, tmp_out=tmp, **kw)
-            if ev is not None:
-                ev[1].record(stream)
             pc.paged_attention_reduce(out, es, ml, tmp, inp.seq_lens)
             if ev is not None:
                 ev[2].record(stream)
-        else:
-            pc.paged_attention_decode(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
-                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **kw)
-            if ev is not None:
-                ev[1].record(stream)
 
     def timed(n, rotate=True):
         """Wall time of n whole steps (barrier-free: nothing but the steps is enqueued)."""
@@ -201,15 +221,7 @@ def main():
         return dec, red
 
     def decode_only(i):
-        pool = pools[i % copies]
-        kw = pool.layout_kwargs()
-        if ps:
-            pc.paged_attention_decode(None, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
-                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), partition_size=ps,
-                                      exp_sums=es, max_logits=ml, tmp_out=tmp, **kw)
-        else:
-            pc.paged_attention_decode(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
-                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **kw)
+        decode(pools[i % copies])
 
     def batched(fn, n):
         """Average launch time of n back-to-back launches, one event pair on the stream."""
@@ -255,6 +267,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads,
                    "head_size": D, "block_size": wl.block_size, "layout": wl.layout, "path": path,
+                   "kv_cache": "fp8_e4m3 (per-kv-head scales)" if fp8 else wl.dtype,
                    "max_seq_len": msl, "kv_bytes_per_step": wl.kv_bytes(), "effective_bytes_per_step": eff,
                    "pool_copies": copies},
         "tokens_per_s": round(S / (ms * 1e-3), 1),

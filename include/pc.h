@@ -13,6 +13,10 @@
  *   pc_paged_attention_reduce  merge the partitions' partial results (log-sum-exp);
  *   pc_paged_attention_plan    choose between the one-pass and the split path.
  *
+ * The write and the decode also exist for an 8-bit cache (suffix _fp8): the pool
+ * holds OCP E4M3 codes with one dequantisation scale per kv head for K and one
+ * for V (see pc_reshape_and_cache_fp8).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers.  Every data pointer is a DEVICE pointer (hipMalloc'd or equivalent),
@@ -156,6 +160,61 @@ int pc_paged_attention_decode(void *out, const void *q, const void *k_pool, cons
                               const int32_t *seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
                               int num_kv_heads, int head_size, int block_size, float scale, int partition_size,
                               float *exp_sums, float *max_logits, float *tmp_out, int dtype, void *stream);
+
+/*
+ * pc_reshape_and_cache_fp8 -- write new K/V rows into an 8-bit (OCP E4M3) pool.
+ *
+ * Defined by "Inside vLLM CUDA Kernels", Part 2, "Why Layout and Quantization
+ * Scale Produce Two Copy Paths" (an 8-bit cache stores each element converted with
+ * a scale; the per-head form reads the scale of head h at h * kv_scale_stride, the
+ * shared form passes stride 0) and the slot rules of pc_reshape_and_cache.  For
+ * every written element x of kv head h the pool byte becomes the E4M3 code of
+ * y = x / k_scale[h * kv_scale_stride] (V: v_scale), where the division is fp32
+ * (correctly rounded), y is clamped to [-448, 448] (the largest finite E4M3
+ * magnitude; E4M3 has no infinity), and the code is y rounded to nearest-even.
+ * NaN becomes the NaN code 0xFF.  A code c stands for E4M3(c) * scale.
+ *
+ *   key, value          device, storage dtype (fp32, fp16 or bf16), rows as for
+ *                       pc_reshape_and_cache (element strides)
+ *   k_pool, v_pool      device uint8 pools; strides in bytes (= elements)
+ *   k_scale, v_scale    device fp32, read at h * kv_scale_stride for h < num_kv_heads
+ *   kv_scale_stride     >= 0 (0: one scale for every head)
+ * Pools, block_stride, token_stride and head_stride must be multiples of 4 bytes
+ * and head_size a multiple of 4 (four codes per store; else PC_ERR_UNSUPPORTED).
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ */
+int pc_reshape_and_cache_fp8(const void *key, const void *value, int64_t key_row_stride, int64_t value_row_stride,
+                             uint8_t *k_pool, uint8_t *v_pool, int64_t num_blocks, int64_t block_stride,
+                             int64_t token_stride, int64_t head_stride, const int64_t *slot_mapping,
+                             int64_t num_tokens, int num_kv_heads, int head_size, int block_size,
+                             const float *k_scale, const float *v_scale, int64_t kv_scale_stride, int dtype,
+                             void *stream);
+
+/*
+ * pc_paged_attention_decode_fp8 -- pc_paged_attention_decode over an 8-bit pool.
+ *
+ * Same operation and arguments as pc_paged_attention_decode, with K and V the
+ * dequantised pool values: token row element d of kv head h is E4M3(code) *
+ * k_scale[h * kv_scale_stride] for K and E4M3(code) * v_scale[...] for V (the
+ * scaled conversion of "Why Layout and Quantization Scale Produce Two Copy Paths"
+ * read back).  q and out are fp16 or bf16 (fp32 gives PC_ERR_UNSUPPORTED); the
+ * split path's partials and pc_paged_attention_reduce are unchanged.
+ *
+ *   k_pool, v_pool    device uint8 pools written by pc_reshape_and_cache_fp8;
+ *                     strides in bytes, multiples of 16; pool bases 16-byte aligned
+ *   k_scale, v_scale  device fp32 as for the write; each used scale must be
+ *                     positive and finite with scale * k_scale * log2(e) in
+ *                     [2^-120, 2^120], else that kv head's outputs are NaN
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ */
+int pc_paged_attention_decode_fp8(void *out, const void *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                                  int64_t num_blocks, int64_t block_stride, int64_t token_stride,
+                                  int64_t head_stride, const int32_t *block_tables, int max_blocks_per_seq,
+                                  const int32_t *seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
+                                  int num_kv_heads, int head_size, int block_size, float scale,
+                                  int partition_size, float *exp_sums, float *max_logits, float *tmp_out,
+                                  const float *k_scale, const float *v_scale, int64_t kv_scale_stride, int dtype,
+                                  void *stream);
 
 /*
  * pc_paged_attention_reduce -- merge the split path's partials.

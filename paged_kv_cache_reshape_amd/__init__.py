@@ -6,7 +6,9 @@ The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
 * ``reshape_and_cache``        -- scatter new K/V rows through ``slot_mapping``;
 * ``paged_attention_decode``   -- one-pass decode, or the 512-token split partials;
 * ``paged_attention_reduce``   -- log-sum-exp merge of the partials;
-* ``paged_attention_plan``     -- the planner's choice between the two paths.
+* ``paged_attention_plan``     -- the planner's choice between the two paths;
+* ``reshape_and_cache_fp8`` / ``paged_attention_decode_fp8`` -- the same over an
+  8-bit (OCP E4M3) pool with per-kv-head scales.
 """
 
 from ._native import (  # noqa: F401
@@ -16,8 +18,10 @@ from ._native import (  # noqa: F401
     abi_version,
     library,
     paged_attention_decode,
+    paged_attention_decode_fp8,
     paged_attention_plan,
     paged_attention_reduce,
     reshape_and_cache,
+    reshape_and_cache_fp8,
     status_string,
 )

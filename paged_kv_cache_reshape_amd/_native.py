@@ -45,6 +45,13 @@ def _load():
         lib.pc_paged_attention_decode.restype = i32
         lib.pc_paged_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32,
                                                   i32, i32, i32, f32, i32, vp, vp, vp, i32, vp]
+        lib.pc_reshape_and_cache_fp8.restype = i32
+        lib.pc_reshape_and_cache_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, i64, i64, vp, i64, i32, i32,
+                                                 i32, vp, vp, i64, i32, vp]
+        lib.pc_paged_attention_decode_fp8.restype = i32
+        lib.pc_paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32,
+                                                      i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, i64, i32,
+                                                      vp]
         lib.pc_paged_attention_reduce.restype = i32
         lib.pc_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.pc_paged_attention_plan.restype = i32
@@ -159,6 +166,74 @@ def paged_attention_decode(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
         D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), dt,
         _stream(q, stream))
     _check("pc_paged_attention_decode", st)
+
+
+def _check_kv_scales(k_scale, v_scale, num_kv_heads: int, kv_scale_stride: int):
+    for t in (k_scale, v_scale):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("k_scale / v_scale must be contiguous float32")
+        if kv_scale_stride < 0 or t.numel() <= (num_kv_heads - 1) * kv_scale_stride:
+            raise ValueError("k_scale / v_scale must hold an entry at h * kv_scale_stride for every kv head")
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                          slot_mapping: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor, *,
+                          num_blocks: int, block_stride: int, token_stride: int, head_stride: int,
+                          kv_scale_stride: int = 1, block_size: int = 16, v_offset: int = 0, stream=None) -> None:
+    """Quantise ``key``/``value`` [T, Hkv, D] (fp32/fp16/bf16) to OCP E4M3 codes in uint8 pools;
+    head h divides by ``k_scale[h * kv_scale_stride]`` / ``v_scale[...]``.  Pool strides are bytes."""
+    _same_device(key, value, k_pool, v_pool, slot_mapping, k_scale, v_scale)
+    if key.dim() != 3 or value.shape != key.shape or key.stride(2) != 1 or value.stride(2) != 1 or \
+            key.stride(1) != key.shape[2] or value.stride(1) != value.shape[2]:
+        raise ValueError("key/value must be [T, Hkv, D] with contiguous rows")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous() or slot_mapping.numel() != key.shape[0]:
+        raise ValueError("slot_mapping must be a contiguous int64 [T]")
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise TypeError("8-bit pools must be uint8")
+    dt = _dtype_code(key)
+    if _DTYPES.get(value.dtype) != dt:
+        raise TypeError("key and value must share one dtype")
+    T, Hkv, D = key.shape
+    _check_kv_scales(k_scale, v_scale, Hkv, kv_scale_stride)
+    st = _load().pc_reshape_and_cache_fp8(_ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(k_pool),
+                                          _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
+                                          head_stride, _ptr(slot_mapping), T, Hkv, D, block_size, _ptr(k_scale),
+                                          _ptr(v_scale), kv_scale_stride, dt, _stream(key, stream))
+    _check("pc_reshape_and_cache_fp8", st)
+
+
+def paged_attention_decode_fp8(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                               block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                               k_scale: torch.Tensor, v_scale: torch.Tensor, *, num_kv_heads: int, scale: float,
+                               num_blocks: int, block_stride: int, token_stride: int, head_stride: int,
+                               kv_scale_stride: int = 1, block_size: int = 16, v_offset: int = 0,
+                               partition_size: int = 0, exp_sums=None, max_logits=None, tmp_out=None,
+                               stream=None) -> None:
+    """``paged_attention_decode`` over uint8 pools of E4M3 codes (strides in bytes); K and V are
+    the codes times the kv head's ``k_scale`` / ``v_scale``.  ``q`` is fp16 or bf16."""
+    _same_device(out, q, k_pool, v_pool, block_tables, seq_lens, exp_sums, max_logits, tmp_out, k_scale, v_scale)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [S, Hq, D]")
+    if out is not None and (out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype):
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous int32 [S, W]")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [S]")
+    for t in (exp_sums, max_logits, tmp_out):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("partials must be contiguous float32")
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise TypeError("8-bit pools must be uint8")
+    _check_kv_scales(k_scale, v_scale, num_kv_heads, kv_scale_stride)
+    dt = _dtype_code(q)
+    S, Hq, D = q.shape
+    st = _load().pc_paged_attention_decode_fp8(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
+        head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads,
+        D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(k_scale),
+        _ptr(v_scale), kv_scale_stride, dt, _stream(q, stream))
+    _check("pc_paged_attention_decode_fp8", st)
 
 
 def paged_attention_reduce(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,

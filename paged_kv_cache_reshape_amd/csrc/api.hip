@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kBlockTokens = 16;
 
 int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
@@ -27,6 +27,86 @@ bool strides16(int es, std::initializer_list<int64_t> strides) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? PC_OK : PC_ERR_LAUNCH; }
+
+// Checks shared by both writes; es = element size of key / value.
+int check_write(const void* key, const void* value, int64_t key_row_stride, int64_t value_row_stride,
+                const void* k_pool, const void* v_pool, int64_t num_blocks, int64_t block_stride,
+                int64_t token_stride, int64_t head_stride, const int64_t* slot_mapping, int64_t num_tokens,
+                int num_kv_heads, int head_size, int block_size, int es) {
+  if (!es || num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      block_stride <= 0 || token_stride <= 0 || head_stride <= 0 || key_row_stride < 0 || value_row_stride < 0)
+    return PC_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PC_OK;
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PC_ERR_INVALID_ARG;
+  if ((int64_t)num_kv_heads * head_size > key_row_stride && num_tokens > 1) return PC_ERR_INVALID_ARG;
+  if ((int64_t)num_kv_heads * head_size > value_row_stride && num_tokens > 1) return PC_ERR_INVALID_ARG;
+  if (num_tokens > INT_MAX || num_blocks > INT64_MAX / block_size) return PC_ERR_UNSUPPORTED;
+  return PC_OK;
+}
+
+// Both decodes; kv8 = the pool holds E4M3 codes (1 byte per element) with per-head
+// scales, else the pool has q's storage type.
+int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool, int64_t num_blocks,
+                int64_t block_stride, int64_t token_stride, int64_t head_stride, const int32_t* block_tables,
+                int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
+                int num_kv_heads, int head_size, int block_size, float scale, int partition_size, float* exp_sums,
+                float* max_logits, float* tmp_out, const float* k_scale, const float* v_scale,
+                int64_t kv_scale_stride, int dtype, bool kv8, void* stream) {
+  const int es = esize(dtype);
+  if (!es || num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_size <= 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0 || (kv8 && kv_scale_stride < 0))
+    return PC_ERR_INVALID_ARG;
+  const bool split = partition_size != 0;
+  if (split && partition_size != PC_PARTITION_SIZE) return partition_size < 0 ? PC_ERR_INVALID_ARG : PC_ERR_UNSUPPORTED;
+  if (split) {
+    if (!exp_sums || !max_logits || !tmp_out) return PC_ERR_INVALID_ARG;
+  } else if (exp_sums || max_logits || tmp_out) {
+    return PC_ERR_INVALID_ARG;
+  }
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return PC_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PC_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || (!split && !out)) return PC_ERR_INVALID_ARG;
+  if (kv8 && (!k_scale || !v_scale)) return PC_ERR_INVALID_ARG;
+  if (num_blocks <= 0 || block_stride <= 0 || token_stride <= 0 || head_stride <= 0) return PC_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PC_ERR_INVALID_ARG;
+  if (block_size != kBlockTokens) return PC_ERR_UNSUPPORTED;
+  if (kv8 && dtype == PC_F32) return PC_ERR_UNSUPPORTED;
+  if (!pcache::decode_supported(dtype, head_size, num_q_heads / num_kv_heads)) return PC_ERR_UNSUPPORTED;
+  const int pes = kv8 ? 1 : es;  // pool bytes per element
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !strides16(pes, {block_stride, token_stride, head_stride, (int64_t)head_size}))
+    return PC_ERR_UNSUPPORTED;
+  // a block's 16 token rows of one head are addressed with 32-bit byte offsets
+  if (token_stride > INT_MAX / (kBlockTokens * pes)) return PC_ERR_UNSUPPORTED;
+  const int parts = split ? (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE : 1;
+  if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX) return PC_ERR_UNSUPPORTED;
+  if (split && parts == 0) return PC_OK;  // every sequence is empty: no partials exist
+  pcache::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_blocks = num_blocks;
+  a.block_stride = block_stride;
+  a.token_stride = token_stride;
+  a.head_stride = head_stride;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.max_partitions = parts;
+  a.exp_sums = exp_sums;
+  a.max_logits = max_logits;
+  a.tmp_out = tmp_out;
+  a.kv8 = kv8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.scale_stride = kv_scale_stride;
+  return status_of(pcache::launch_decode(a, dtype, head_size, split, static_cast<hipStream_t>(stream)));
+}
 
 }  // namespace
 
@@ -75,21 +155,41 @@ int pc_reshape_and_cache(const void* key, const void* value, int64_t key_row_str
                          int64_t head_stride, const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
                          int head_size, int block_size, int dtype, void* stream) {
   const int es = esize(dtype);
-  if (!es || num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks <= 0 ||
-      block_stride <= 0 || token_stride <= 0 || head_stride <= 0 || key_row_stride < 0 || value_row_stride < 0)
-    return PC_ERR_INVALID_ARG;
-  if (num_tokens == 0) return PC_OK;
-  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PC_ERR_INVALID_ARG;
-  if ((int64_t)num_kv_heads * head_size > key_row_stride && num_tokens > 1) return PC_ERR_INVALID_ARG;
-  if ((int64_t)num_kv_heads * head_size > value_row_stride && num_tokens > 1) return PC_ERR_INVALID_ARG;
-  if (num_tokens > INT_MAX || num_blocks > INT64_MAX / block_size) return PC_ERR_UNSUPPORTED;
+  const int rc = check_write(key, value, key_row_stride, value_row_stride, k_pool, v_pool, num_blocks, block_stride,
+                             token_stride, head_stride, slot_mapping, num_tokens, num_kv_heads, head_size, block_size,
+                             es);
+  if (rc != PC_OK || num_tokens == 0) return rc;
   const bool vec16 = aligned16(key) && aligned16(value) && aligned16(k_pool) && aligned16(v_pool) &&
                      strides16(es, {key_row_stride, value_row_stride, block_stride, token_stride, head_stride,
                                     (int64_t)head_size});
   pcache::WriteArgs a{key,        value,        key_row_stride, value_row_stride, k_pool,     v_pool,
                       num_blocks, block_stride, token_stride,   head_stride,      slot_mapping, num_tokens,
-                      num_kv_heads, head_size,  block_size};
+                      num_kv_heads, head_size,  block_size,     nullptr,          nullptr,      0};
   return status_of(pcache::launch_write(a, dtype, vec16, static_cast<hipStream_t>(stream)));
+}
+
+int pc_reshape_and_cache_fp8(const void* key, const void* value, int64_t key_row_stride, int64_t value_row_stride,
+                             uint8_t* k_pool, uint8_t* v_pool, int64_t num_blocks, int64_t block_stride,
+                             int64_t token_stride, int64_t head_stride, const int64_t* slot_mapping,
+                             int64_t num_tokens, int num_kv_heads, int head_size, int block_size,
+                             const float* k_scale, const float* v_scale, int64_t kv_scale_stride, int dtype,
+                             void* stream) {
+  const int es = esize(dtype);
+  const int rc = check_write(key, value, key_row_stride, value_row_stride, k_pool, v_pool, num_blocks, block_stride,
+                             token_stride, head_stride, slot_mapping, num_tokens, num_kv_heads, head_size, block_size,
+                             es);
+  if (rc != PC_OK) return rc;
+  if (kv_scale_stride < 0) return PC_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PC_OK;
+  if (!k_scale || !v_scale) return PC_ERR_INVALID_ARG;
+  // four codes per 32-bit store
+  if (head_size % 4 != 0 || ((uintptr_t)k_pool | (uintptr_t)v_pool) % 4 != 0 ||
+      (block_stride | token_stride | head_stride) % 4 != 0)
+    return PC_ERR_UNSUPPORTED;
+  pcache::WriteArgs a{key,        value,        key_row_stride, value_row_stride, k_pool,     v_pool,
+                      num_blocks, block_stride, token_stride,   head_stride,      slot_mapping, num_tokens,
+                      num_kv_heads, head_size,  block_size,     k_scale,          v_scale,      kv_scale_stride};
+  return status_of(pcache::launch_write_fp8(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int pc_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool, int64_t num_blocks,
@@ -98,53 +198,23 @@ int pc_paged_attention_decode(void* out, const void* q, const void* k_pool, cons
                               int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
                               int block_size, float scale, int partition_size, float* exp_sums, float* max_logits,
                               float* tmp_out, int dtype, void* stream) {
-  const int es = esize(dtype);
-  if (!es || num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      head_size <= 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0)
-    return PC_ERR_INVALID_ARG;
-  const bool split = partition_size != 0;
-  if (split && partition_size != PC_PARTITION_SIZE) return partition_size < 0 ? PC_ERR_INVALID_ARG : PC_ERR_UNSUPPORTED;
-  if (split) {
-    if (!exp_sums || !max_logits || !tmp_out) return PC_ERR_INVALID_ARG;
-  } else if (exp_sums || max_logits || tmp_out) {
-    return PC_ERR_INVALID_ARG;
-  }
-  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return PC_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PC_OK;
-  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || (!split && !out)) return PC_ERR_INVALID_ARG;
-  if (num_blocks <= 0 || block_stride <= 0 || token_stride <= 0 || head_stride <= 0) return PC_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || !std::isfinite(scale)) return PC_ERR_INVALID_ARG;
-  if (block_size != kBlockTokens) return PC_ERR_UNSUPPORTED;
-  if (!pcache::decode_supported(dtype, head_size, num_q_heads / num_kv_heads)) return PC_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
-      !strides16(es, {block_stride, token_stride, head_stride, (int64_t)head_size}))
-    return PC_ERR_UNSUPPORTED;
-  // a block's 16 token rows of one head are addressed with 32-bit byte offsets
-  if (token_stride > INT_MAX / (kBlockTokens * es)) return PC_ERR_UNSUPPORTED;
-  const int parts = split ? (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE : 1;
-  if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX) return PC_ERR_UNSUPPORTED;
-  if (split && parts == 0) return PC_OK;  // every sequence is empty: no partials exist
-  pcache::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.num_blocks = num_blocks;
-  a.block_stride = block_stride;
-  a.token_stride = token_stride;
-  a.head_stride = head_stride;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.seq_lens = seq_lens;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.max_partitions = parts;
-  a.exp_sums = exp_sums;
-  a.max_logits = max_logits;
-  a.tmp_out = tmp_out;
-  return status_of(pcache::launch_decode(a, dtype, head_size, split, static_cast<hipStream_t>(stream)));
+  return decode_impl(out, q, k_pool, v_pool, num_blocks, block_stride, token_stride, head_stride, block_tables,
+                     max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
+                     block_size, scale, partition_size, exp_sums, max_logits, tmp_out, nullptr, nullptr, 0, dtype,
+                     false, stream);
+}
+
+int pc_paged_attention_decode_fp8(void* out, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                                  int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                  const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+                                  int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
+                                  int block_size, float scale, int partition_size, float* exp_sums,
+                                  float* max_logits, float* tmp_out, const float* k_scale, const float* v_scale,
+                                  int64_t kv_scale_stride, int dtype, void* stream) {
+  return decode_impl(out, q, k_pool, v_pool, num_blocks, block_stride, token_stride, head_stride, block_tables,
+                     max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
+                     block_size, scale, partition_size, exp_sums, max_logits, tmp_out, k_scale, v_scale,
+                     kv_scale_stride, dtype, true, stream);
 }
 
 int pc_paged_attention_reduce(void* out, const float* exp_sums, const float* max_logits, const float* tmp_out,

@@ -305,6 +305,7 @@ bool decode_supported(int dtype, int head_size, int group) {
 
 // fp32 storage runs the VALU kernel above; fp16 / bf16 take the matrix-core kernel.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream) {
+  if (a.kv8 && dtype != 1 && dtype != 2) return hipErrorInvalidValue;  // 8-bit pools: 16-bit queries only
   switch (dtype) {
     case 0: return launch_dim<F32>(a, head_size, split, stream);
     case 1:

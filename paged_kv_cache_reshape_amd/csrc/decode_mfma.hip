@@ -36,6 +36,17 @@
 // * A unit's block ids are staged in LDS by the whole workgroup, which checks them
 //   against the pool once; each wave reads its ids from there one block ahead.
 //
+// 8-bit (OCP E4M3) pools ("Inside vLLM CUDA Kernels", Part 2, "Why Layout and
+// Quantization Scale Produce Two Copy Paths": the stored code times the kv head's
+// scale stands for the value): the ring holds the raw codes -- half the bytes in
+// flight per block -- and each block is widened to the query's 16-bit type just
+// before the same two MFMA stages.  Every E4M3 value is exact in bf16 and fp16, so
+// the widening (v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 1) loses nothing; the
+// head's k_scale is folded into the score scale and v_scale multiplies the final
+// output.  The q.k contraction runs over the dims in a permuted order (the same for
+// K and q, so the dot product is unchanged): k-step k of lane row group rg covers
+// dims rg*(D/4) + 8k .. +8, which makes each lane's K bytes one contiguous run.
+//
 // Work distribution:
 // * Split path: one workgroup per (sequence, kv head, 512-token partition); the
 //   partitions are equal-sized, so the grid balances itself.
@@ -142,6 +153,20 @@ __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// four E4M3 codes (one dword) widened exactly to two dwords of the 16-bit type
+template <class ST>
+__device__ __forceinline__ uint2 widen4(uint32_t codes);
+template <>
+__device__ __forceinline__ uint2 widen4<BF16>(uint32_t codes) {
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true)));
+}
+template <>
+__device__ __forceinline__ uint2 widen4<F16>(uint32_t codes) {
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, true)));
+}
+
 // a lane's slice of one V row: 8 (head_size 128) or 4 (64) 16-bit values
 template <int N>
 struct VRowOf;
@@ -155,6 +180,27 @@ struct VRowOf<4> {
 };
 __device__ __forceinline__ uint32_t vword(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 __device__ __forceinline__ uint32_t vword(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
+
+// the same slice as E4M3 codes: 8 bytes (head_size 128) or 4 (64)
+template <int N>
+struct VRow8Of;
+template <>
+struct VRow8Of<8> {
+  using type = uint2;
+};
+template <>
+struct VRow8Of<4> {
+  using type = uint32_t;
+};
+template <class ST>
+__device__ __forceinline__ uint4 widen_row(const uint2& c) {
+  const uint2 lo = widen4<ST>(c.x), hi = widen4<ST>(c.y);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+template <class ST>
+__device__ __forceinline__ uint2 widen_row(uint32_t c) {
+  return widen4<ST>(c);
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -172,8 +218,8 @@ struct UnitLds {
 
 // One unit: kv head `kvh` of sequence `s`, tokens [t_begin, t_end).  All waves of
 // the workgroup call it together (it uses block-wide barriers).  Writes out (one
-// pass) or the partition's partials (split).
-template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT>
+// pass) or the partition's partials (split).  KV8: the pool holds E4M3 codes.
+template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT, bool KV8>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, G, TABLE>& sm, int s, int kvh,
                                             int part) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
@@ -186,6 +232,9 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   constexpr int NT = DPL;
   constexpr int kThreads = NW * kWave;
   using VRow = typename VRowOf<DPL>::type;
+  using VRow8 = typename VRow8Of<DPL>::type;
+  constexpr int EB = KV8 ? 1 : 2;  // pool bytes per element
+  constexpr int K8 = KS / 2;        // 16-byte K loads per block and lane (8-bit pool)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -194,24 +243,31 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const int col = lane & 15;  // score column: query head of the group
 
   const int L = a.seq_lens[s];
+  // 8-bit pool: the kv head's dequantisation scales (k_scale folded into the score scale)
+  const float ksc = KV8 ? a.k_scale[(int64_t)kvh * a.scale_stride] : 1.f;
+  const float vsc = KV8 ? a.v_scale[(int64_t)kvh * a.scale_stride] : 1.f;
+  const float cs_raw = a.scale_log2 * ksc;
+  const bool bad_scale = KV8 && !(cs_raw >= 0x1p-120f && cs_raw <= 0x1p120f && vsc > 0.f && vsc <= 3.4e38f);
   bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
-             (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition);
+             (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition) || bad_scale;
   const int t_begin = SPLIT ? part * kPartition : 0;
   const int t_end = bad ? t_begin : (SPLIT ? min(L, t_begin + kPartition) : L);
   const int b_begin = t_begin / kBlockTokens;
   const int b_end = (t_end + kBlockTokens - 1) / kBlockTokens;
   const int h0 = kvh * G;
-  const float cs = a.scale_log2;  // > 0 (validated on the host)
+  const float cs = bad_scale ? 1.f : cs_raw;  // > 0 (scale validated on the host, k_scale here)
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
-  // B operand: query head `col` (zero for col >= G), dims 32*k + 8*rg .. +8
+  // B operand: query head `col` (zero for col >= G), dims 32*k + 8*rg .. +8 (16-bit
+  // pool) or rg*(D/4) + 8*k .. +8 (8-bit pool, the order its K rows are read in)
   uint4 qb[KS];
   {
     const int qh = col < G ? col : G - 1;  // keep the address inside q for the zero columns
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.num_q_heads + h0 + qh) * D + 8 * rg;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.num_q_heads + h0 + qh) * D +
+                           (KV8 ? rg * (D / 4) : 8 * rg);
 #pragma unroll
     for (int k = 0; k < KS; ++k)
-      qb[k] = col < G ? *reinterpret_cast<const uint4*>(qrow + 32 * k) : make_uint4(0, 0, 0, 0);
+      qb[k] = col < G ? *reinterpret_cast<const uint4*>(qrow + (KV8 ? 8 : 32) * k) : make_uint4(0, 0, 0, 0);
   }
 
   // softmax state of head `col` (meaningful for col < G): the four row-group lanes
@@ -221,32 +277,46 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t head_bytes = (int64_t)kvh * a.head_stride * 2;
+  const int64_t head_bytes = (int64_t)kvh * a.head_stride * EB;
   const char* kpool = static_cast<const char*>(a.k_pool) + head_bytes;
   const char* vpool = static_cast<const char*>(a.v_pool) + head_bytes;
-  const int64_t block_bytes = a.block_stride * 2;
-  const int tok_bytes = (int)(a.token_stride * 2);                   // < 2^27 (validated on the host)
+  const int64_t block_bytes = a.block_stride * EB;
+  const int tok_bytes = (int)(a.token_stride * EB);                  // 16 * tok_bytes < 2^31 (validated on the host)
   const uint32_t tile_bytes = (uint32_t)(kBlockTokens * tok_bytes);  // extent of one tile's rows
-  const int k_off = col * tok_bytes + 16 * rg;                       // + 64*k per MFMA step
-  const int v_off = 4 * rg * tok_bytes + col * (2 * DPL);            // + e*tok_bytes for row 4*rg + e
+  // 16-bit: + 64*k per MFMA step; 8-bit: the lane's D/4 contiguous codes, 16 bytes per load
+  const int k_off = col * tok_bytes + (KV8 ? rg * (D / 4) : 16 * rg);
+  const int v_off = 4 * rg * tok_bytes + col * (EB * DPL);  // + e*tok_bytes for row 4*rg + e
   const float lazy_raw = kLazy / cs;
 
-  uint4 kb[STAGES][KS];
+  uint4 kb[STAGES][KS];  // 16-bit pool ring
   VRow vb[STAGES][4];
+  uint4 kq[STAGES][K8];  // 8-bit pool ring (raw codes)
+  VRow8 vq[STAGES][4];
 
-  // K/V of the block with id BID into ring slot KD / VD
-#define PC_LOAD(KD, VD, BID)                                                                         \
+  // K/V of the block with id BID into ring slot ST
+#define PC_LOAD(ST, BID)                                                                             \
   do {                                                                                               \
     const int64_t boff_ = (int64_t)(BID) * block_bytes;                                              \
     const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, tile_bytes);                         \
     const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                         \
-    _Pragma("unroll") for (int k = 0; k < KS; ++k) KD[k] =                                          \
-        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 64 * k, 0, 0)); \
-    _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                 \
-      if constexpr (DPL == 8)                                                                        \
-        VD[e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b128(vr_, v_off, e * tok_bytes, 0)); \
-      else                                                                                           \
-        VD[e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+    if constexpr (KV8) {                                                                             \
+      _Pragma("unroll") for (int k = 0; k < K8; ++k) kq[ST][k] =                                    \
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 16 * k, 0, 0)); \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                               \
+        if constexpr (DPL == 8)                                                                      \
+          vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+        else                                                                                         \
+          vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b32(vr_, v_off, e * tok_bytes, 0)); \
+      }                                                                                              \
+    } else {                                                                                         \
+      _Pragma("unroll") for (int k = 0; k < KS; ++k) kb[ST][k] =                                    \
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 64 * k, 0, 0)); \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                               \
+        if constexpr (DPL == 8)                                                                      \
+          vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b128(vr_, v_off, e * tok_bytes, 0)); \
+        else                                                                                         \
+          vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+      }                                                                                              \
     }                                                                                                \
   } while (0)
 
@@ -308,7 +378,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     if (nwc == 0) continue;
     auto id_of = [&](int j) -> int { return sm.ids[w + min(j, nwc - 1) * NW]; };
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) PC_LOAD(kb[st], vb[st], __builtin_amdgcn_readfirstlane(id_of(st)));
+    for (int st = 0; st < STAGES - 1; ++st) PC_LOAD(st, __builtin_amdgcn_readfirstlane(id_of(st)));
     int id_next = id_of(STAGES - 1);
     // The ring turns a whole number of times: a step past the wave's last block in
     // the chunk consumes a repeat of that block (fetched again from cache) with
@@ -318,13 +388,28 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 #pragma unroll
       for (int st = 0; st < STAGES; ++st) {
         const int it = it0 + st;
-        PC_LOAD(kb[(st + STAGES - 1) % STAGES], vb[(st + STAGES - 1) % STAGES],
-                __builtin_amdgcn_readfirstlane(id_next));
+        PC_LOAD((st + STAGES - 1) % STAGES, __builtin_amdgcn_readfirstlane(id_next));
         id_next = id_of(it + STAGES);
         // keep the scheduler from sinking the prefetch below the wait for this block
         __builtin_amdgcn_sched_barrier(0);
         // a step past the wave's last block of this chunk sees no token
-        PC_BLOCK(kb[st], vb[st], it < nwc ? (cb + w + it * NW) * kBlockTokens : t_end);
+        const int tok0 = it < nwc ? (cb + w + it * NW) * kBlockTokens : t_end;
+        if constexpr (KV8) {
+          // widen the block's codes to the query's type (exact)
+          uint4 kw[KS];
+          VRow vw[4];
+#pragma unroll
+          for (int k = 0; k < KS; ++k) {
+            const uint4 r = kq[st][k >> 1];
+            const uint2 lo = widen4<ST>((k & 1) ? r.z : r.x), hi = widen4<ST>((k & 1) ? r.w : r.y);
+            kw[k] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vw[e] = widen_row<ST>(vq[st][e]);
+          PC_BLOCK(kw, vw, tok0);
+        } else {
+          PC_BLOCK(kb[st], vb[st], tok0);
+        }
       }
       it0 += STAGES;
     } while (it0 < nwc);
@@ -370,7 +455,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
         os = fmaf(sm.acc[ww][g][d], fw, os);
       }
     }
-    float res = M == -INFINITY ? 0.f : os / ls;
+    float res = M == -INFINITY ? 0.f : os / ls * vsc;
     if (any_bad) res = NAN;
     const int64_t sh = (int64_t)s * a.num_q_heads + h0 + g;
     if constexpr (SPLIT) {
@@ -387,7 +472,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 }
 
 // Split path: workgroup = (kv head, sequence, partition), fastest-varying first.
-template <class ST, int D, int G>
+template <class ST, int D, int G, bool KV8>
 __global__ __launch_bounds__(PCACHE_SPLIT_WAVES* kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int NW = PCACHE_SPLIT_WAVES;
@@ -402,11 +487,11 @@ void decode_split_kernel(DecodeArgs a) {
   const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
                    (int64_t)L > (int64_t)a.max_partitions * kPartition;
   if (!bad && part * kPartition >= L) return;  // a partition past the sequence writes nothing
-  decode_unit<ST, D, G, NW, PCACHE_SPLIT_STAGES, TABLE, true>(a, sm, s, kvh, part);
+  decode_unit<ST, D, G, NW, PCACHE_SPLIT_STAGES, TABLE, true, KV8>(a, sm, s, kvh, part);
 }
 
 // One-pass path: persistent workgroups, units longest first, dealt in snake order.
-template <class ST, int D, int G>
+template <class ST, int D, int G, bool KV8>
 __global__ __launch_bounds__(onepass_waves<D>() * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_ONEPASS_OCC)))
 void decode_onepass_kernel(DecodeArgs a) {
   constexpr int NW = onepass_waves<D>();
@@ -440,17 +525,17 @@ void decode_onepass_kernel(DecodeArgs a) {
     const int rank = (int)(pos / a.num_kv_heads);
     const int kvh = (int)(pos % a.num_kv_heads);
     const int s = ranked ? order_lds[rank] : rank;
-    decode_unit<ST, D, G, NW, PCACHE_ONEPASS_STAGES, PCACHE_ONEPASS_TABLE, false>(a, sm, s, kvh, 0);
+    decode_unit<ST, D, G, NW, PCACHE_ONEPASS_STAGES, PCACHE_ONEPASS_TABLE, false, KV8>(a, sm, s, kvh, 0);
   }
 }
 
 // Resident workgroups per CU for the one-pass kernel, queried once per instance.
-template <class ST, int D, int G>
+template <class ST, int D, int G, bool KV8>
 int onepass_blocks_per_cu() {
   static int cached = 0;
   if (!cached) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8>,
                                                      onepass_waves<D>() * kWave, 0) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
@@ -461,12 +546,12 @@ int onepass_blocks_per_cu() {
   return cached;
 }
 
-template <class ST, int D, int G>
+template <class ST, int D, int G, bool KV8>
 hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
   if (split) {
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_split_kernel<ST, D, G>), dim3((unsigned)units), dim3(PCACHE_SPLIT_WAVES * kWave), 0,
+    hipLaunchKernelGGL((decode_split_kernel<ST, D, G, KV8>), dim3((unsigned)units), dim3(PCACHE_SPLIT_WAVES * kWave), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -475,21 +560,21 @@ hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
 #ifdef PCACHE_ONEPASS_BLOCKS_PER_CU
   const int64_t slots = (int64_t)device_compute_units() * PCACHE_ONEPASS_BLOCKS_PER_CU;
 #else
-  const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G>();
+  const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G, KV8>();
 #endif
   const int64_t grid = units < slots ? units : slots;
-  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G>), dim3((unsigned)grid), dim3(onepass_waves<D>() * kWave), 0,
+  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, KV8>), dim3((unsigned)grid), dim3(onepass_waves<D>() * kWave), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-template <class ST, int D>
+template <class ST, int D, bool KV8>
 hipError_t launch_group(const DecodeArgs& a, bool split, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_typed<ST, D, 1>(a, split, stream);
-    case 2: return launch_typed<ST, D, 2>(a, split, stream);
-    case 4: return launch_typed<ST, D, 4>(a, split, stream);
-    case 8: return launch_typed<ST, D, 8>(a, split, stream);
+    case 1: return launch_typed<ST, D, 1, KV8>(a, split, stream);
+    case 2: return launch_typed<ST, D, 2, KV8>(a, split, stream);
+    case 4: return launch_typed<ST, D, 4, KV8>(a, split, stream);
+    case 8: return launch_typed<ST, D, 8, KV8>(a, split, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -497,8 +582,9 @@ hipError_t launch_group(const DecodeArgs& a, bool split, hipStream_t stream) {
 template <class ST>
 hipError_t launch_dim(const DecodeArgs& a, int head_size, bool split, hipStream_t stream) {
   switch (head_size) {
-    case 64: return launch_group<ST, 64>(a, split, stream);
-    case 128: return launch_group<ST, 128>(a, split, stream);
+    case 64: return a.kv8 ? launch_group<ST, 64, true>(a, split, stream) : launch_group<ST, 64, false>(a, split, stream);
+    case 128:
+      return a.kv8 ? launch_group<ST, 128, true>(a, split, stream) : launch_group<ST, 128, false>(a, split, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,6 +16,10 @@ struct WriteArgs {
   const int64_t* slot_mapping;
   int64_t num_tokens;
   int num_kv_heads, head_size, block_size;
+  // 8-bit cache only: head h of K divides by k_scale[h * scale_stride], V likewise
+  const float* k_scale;
+  const float* v_scale;
+  int64_t scale_stride;
 };
 
 struct DecodeArgs {
@@ -34,6 +38,11 @@ struct DecodeArgs {
   float* exp_sums;
   float* max_logits;
   float* tmp_out;
+  // 8-bit (OCP E4M3) pool: codes times k_scale / v_scale of the kv head
+  int kv8;
+  const float* k_scale;
+  const float* v_scale;
+  int64_t scale_stride;
 };
 
 struct ReduceArgs {
@@ -47,6 +56,8 @@ struct ReduceArgs {
 
 // Each returns hipSuccess or the launch error; `vec16` selects the 16-byte copy path.
 hipError_t launch_write(const WriteArgs& a, int dtype, bool vec16, hipStream_t stream);
+// The write into an 8-bit (OCP E4M3) pool; `dtype` is the type of key / value.
+hipError_t launch_write_fp8(const WriteArgs& a, int dtype, hipStream_t stream);
 // Returns hipErrorInvalidValue for a (dtype, head_size, group) this build has no kernel for.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
 // 16-bit storage: q.k on the matrix cores (decode_mfma.hip).

@@ -31,15 +31,24 @@ def to_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
 
 
 class DevicePool:
-    """The workload's pool in device memory, filled with its quiet-NaN pattern."""
+    """The workload's pool in device memory, filled with its quiet-NaN pattern (an
+    8-bit cache: uint8 codes, NaN 0x7F, plus its per-head scales on the device)."""
 
     def __init__(self, wl, device="cuda"):
         self.wl = wl
-        _, ti = INT_VIEW[wl.dtype]
-        fill = nan_bits(wl.dtype)  # 0x7FC00000 / 0x7E00 / 0x7FC0: positive in the signed view
+        self.fp8 = bool(getattr(wl, "fp8", False))
+        if self.fp8:
+            def make():
+                return torch.full((wl.pool_elems,), 0x7F, dtype=torch.uint8, device=device)
 
-        def make():
-            return torch.full((wl.pool_elems,), fill, dtype=ti, device=device).view(TORCH_DT[wl.dtype])
+            self.k_scale = torch.from_numpy(np.ascontiguousarray(wl.k_scale, np.float32)).to(device)
+            self.v_scale = torch.from_numpy(np.ascontiguousarray(wl.v_scale, np.float32)).to(device)
+        else:
+            _, ti = INT_VIEW[wl.dtype]
+            fill = nan_bits(wl.dtype)  # 0x7FC00000 / 0x7E00 / 0x7FC0: positive in the signed view
+
+            def make():
+                return torch.full((wl.pool_elems,), fill, dtype=ti, device=device).view(TORCH_DT[wl.dtype])
 
         self.k = make()
         self.v = self.k if wl.layout == "combined" else make()
@@ -53,6 +62,16 @@ class DevicePool:
     def arrays(self):
         return (self.k,) if self.v is self.k else (self.k, self.v)
 
+    def scale_kwargs(self):
+        return dict(kv_scale_stride=int(self.wl.scale_stride)) if self.fp8 else {}
+
+    def bits(self):
+        """Host copies of the pool buffers as stored bits (uint8 codes for an 8-bit cache)."""
+        torch.cuda.synchronize()
+        if self.fp8:
+            return [a.cpu().numpy() for a in self.arrays()]
+        return [to_bits(a, self.wl.dtype) for a in self.arrays()]
+
 
 def write(pool: DevicePool, key_bits, value_bits, slots, chunk: int = 1 << 16):
     """pc_reshape_and_cache of host rows, uploaded in chunks of ``chunk`` tokens."""
@@ -63,7 +82,11 @@ def write(pool: DevicePool, key_bits, value_bits, slots, chunk: int = 1 << 16):
         key = to_dev(key_bits[t0:t1], wl.dtype)
         value = to_dev(value_bits[t0:t1], wl.dtype)
         sm = torch.from_numpy(np.ascontiguousarray(slots[t0:t1], dtype=np.int64)).cuda()
-        pc.reshape_and_cache(key, value, pool.k, pool.v, sm, **pool.layout_kwargs())
+        if pool.fp8:
+            pc.reshape_and_cache_fp8(key, value, pool.k, pool.v, sm, pool.k_scale, pool.v_scale,
+                                     **pool.layout_kwargs(), **pool.scale_kwargs())
+        else:
+            pc.reshape_and_cache(key, value, pool.k, pool.v, sm, **pool.layout_kwargs())
 
 
 def filled_pool(wl, step_write: bool = True) -> DevicePool:
@@ -96,18 +119,34 @@ def decode(pool: DevicePool, inp: DecodeInputs, path: str = "plan", max_seq_len:
         ps, _, _ = pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, TORCH_DT[wl.dtype])
         path = "split" if ps else "single"
     out = torch.empty_like(inp.q)
-    common = dict(num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pool.layout_kwargs())
     if path == "single":
-        pc.paged_attention_decode(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl, **common)
+        decode_call(pool, inp, out, msl)
         return out, path
+    es, ml, tmp = partials_call(pool, inp, msl)
+    pc.paged_attention_reduce(out, es, ml, tmp, inp.seq_lens)
+    return out, path
+
+
+def decode_call(pool: DevicePool, inp: DecodeInputs, out, msl: int, **kw):
+    """One pc_paged_attention_decode(_fp8) call on the pool (``kw``: split-path partials)."""
+    wl = pool.wl
+    common = dict(num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pool.layout_kwargs(), **kw)
+    if pool.fp8:
+        pc.paged_attention_decode_fp8(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl, pool.k_scale,
+                                      pool.v_scale, **pool.scale_kwargs(), **common)
+    else:
+        pc.paged_attention_decode(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl, **common)
+
+
+def partials_call(pool: DevicePool, inp: DecodeInputs, msl: int):
+    """The split path's decode: (exp_sums, max_logits, tmp_out), NaN where unwritten."""
+    S, Hq, D = inp.q.shape
     P = max(1, -(-msl // pc.PARTITION_SIZE))
     es = torch.full((S, Hq, P), float("nan"), device="cuda")
     ml = torch.full((S, Hq, P), float("nan"), device="cuda")
     tmp = torch.full((S, Hq, P, D), float("nan"), device="cuda")
-    pc.paged_attention_decode(None, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
-                              partition_size=pc.PARTITION_SIZE, exp_sums=es, max_logits=ml, tmp_out=tmp, **common)
-    pc.paged_attention_reduce(out, es, ml, tmp, inp.seq_lens)
-    return out, path
+    decode_call(pool, inp, None, msl, partition_size=pc.PARTITION_SIZE, exp_sums=es, max_logits=ml, tmp_out=tmp)
+    return es, ml, tmp
 
 
 def out_f64(out: torch.Tensor) -> np.ndarray:

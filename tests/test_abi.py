@@ -35,13 +35,13 @@ def declared_symbols():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
     assert {"pc_reshape_and_cache", "pc_paged_attention_decode", "pc_paged_attention_reduce",
-            "pc_paged_attention_plan"} <= set(names)
+            "pc_paged_attention_plan", "pc_reshape_and_cache_fp8", "pc_paged_attention_decode_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert pc.abi_version() == 1
+    assert pc.abi_version() == 2
     assert pc.status_string(0) == "ok"
     assert "invalid" in pc.status_string(-1)
     assert "unsupported" in pc.status_string(-2)
@@ -100,6 +100,57 @@ def test_write_validation(lib):
     for bad in (dict(dt=3), dict(T=-1), dict(Hkv=0), dict(D=0), dict(B=0), dict(nb=0), dict(key=None),
                 dict(sm=None), dict(krs=100), dict(ts=0)):
         assert call(**bad) == -1, bad
+
+
+def _decode_fp8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=100, bs=8 * 16 * 128, ts=128, hs=16 * 128, bt=FAKE, W=128,
+             sl=FAKE, S=4, msl=2048, Hq=32, Hkv=8, D=128, B=16, scale=0.088, ps=0, es=None, ml=None, tmp=None,
+             ksc=FAKE, vsc=FAKE, sst=1, dt=2, stream=None)
+    a.update(kw)
+    return lib.pc_paged_attention_decode_fp8(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"],
+                                             a["bt"], a["W"], a["sl"], a["S"], a["msl"], a["Hq"], a["Hkv"], a["D"],
+                                             a["B"], a["scale"], a["ps"], a["es"], a["ml"], a["tmp"], a["ksc"],
+                                             a["vsc"], a["sst"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), -1),
+    (dict(ksc=None), -1),                  # scales are required
+    (dict(vsc=None), -1),
+    (dict(sst=-1), -1),
+    (dict(out=None), -1),
+    (dict(ps=512), -1),
+    (dict(dt=0), -2),                      # fp32 queries have no 8-bit kernel
+    (dict(ts=72), -2),                     # byte stride not a multiple of 16
+    (dict(D=96, bs=8 * 16 * 96, hs=16 * 96, ts=96), -2),
+    (dict(B=32, W=64), -2),
+    (dict(ts=1 << 27), -2),                # 16 token rows span 2 GiB
+])
+def test_decode_fp8_validation(lib, kw, status):
+    assert _decode_fp8(lib, **kw) == status
+
+
+def test_decode_fp8_empty_batch_is_a_noop(lib):
+    assert _decode_fp8(lib, S=0) == 0
+
+
+def test_write_fp8_validation(lib):
+    f = lib.pc_reshape_and_cache_fp8
+    ok = dict(key=FAKE, value=FAKE, krs=1024, vrs=1024, k=FAKE, v=FAKE, nb=10, bs=16384, ts=128, hs=2048,
+              sm=FAKE, T=3, Hkv=8, D=128, B=16, ksc=FAKE, vsc=FAKE, sst=1, dt=2)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["key"], a["value"], a["krs"], a["vrs"], a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"],
+                 a["sm"], a["T"], a["Hkv"], a["D"], a["B"], a["ksc"], a["vsc"], a["sst"], a["dt"], None)
+
+    assert call(T=0) == 0
+    assert call(T=0, ksc=None, vsc=None) == 0
+    for bad in (dict(dt=3), dict(T=-1), dict(Hkv=0), dict(ksc=None), dict(vsc=None), dict(sst=-1), dict(key=None),
+                dict(krs=100), dict(nb=0)):
+        assert call(**bad) == -1, bad
+    for unsup in (dict(D=126, krs=1008, vrs=1008, hs=2016), dict(ts=130), dict(k=ctypes.c_void_p(0x10002))):
+        assert call(**unsup) == -2, unsup
 
 
 def test_reduce_validation(lib):
