@@ -102,6 +102,13 @@ constexpr int onepass_waves() {
 #ifndef PCACHE_SPLIT_STAGES
 #define PCACHE_SPLIT_STAGES 2
 #endif
+// 8-bit pools: a block is half the bytes, so more blocks go in flight per wave
+#ifndef PCACHE_ONEPASS_STAGES_KV8
+#define PCACHE_ONEPASS_STAGES_KV8 2
+#endif
+#ifndef PCACHE_SPLIT_STAGES_KV8
+#define PCACHE_SPLIT_STAGES_KV8 2
+#endif
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -192,15 +199,7 @@ template <>
 struct VRow8Of<4> {
   using type = uint32_t;
 };
-template <class ST>
-__device__ __forceinline__ uint4 widen_row(const uint2& c) {
-  const uint2 lo = widen4<ST>(c.x), hi = widen4<ST>(c.y);
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-template <class ST>
-__device__ __forceinline__ uint2 widen_row(uint32_t c) {
-  return widen4<ST>(c);
-}
+__device__ __forceinline__ uint32_t vword(uint32_t v, int) { return v; }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -320,17 +319,29 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     }                                                                                                \
   } while (0)
 
-  // consume the block in KC/VC whose first token is TOK0
-#define PC_BLOCK(KC, VC, TOK0)                                                                       \
+  // consume the block in ring slot SL whose first token is TOK0
+#define PC_BLOCK(SL, TOK0)                                                                           \
   do {                                                                                               \
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};                                                                \
-    _Pragma("unroll") for (int k = 0; k < KS; ++k) c = mfma16<ST>(KC[k], qb[k], c);                 \
+    if constexpr (KV8) {                                                                             \
+      /* each k-step's 8 codes widened to the query's type just before its MFMA */                   \
+      _Pragma("unroll") for (int k = 0; k < KS; ++k) {                                              \
+        const uint4 r_ = kq[SL][k >> 1];                                                             \
+        const uint2 lo_ = widen4<ST>((k & 1) ? r_.z : r_.x), hi_ = widen4<ST>((k & 1) ? r_.w : r_.y); \
+        c = mfma16<ST>(make_uint4(lo_.x, lo_.y, hi_.x, hi_.y), qb[k], c);                           \
+      }                                                                                              \
+    } else {                                                                                         \
+      _Pragma("unroll") for (int k = 0; k < KS; ++k) c = mfma16<ST>(kb[SL][k], qb[k], c);           \
+    }                                                                                                \
     const int visible = t_end - (TOK0);                                                              \
     if (visible < kBlockTokens) {                                                                    \
       _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                               \
         const bool keep = 4 * rg + e < visible;                                                      \
         c[e] = keep ? c[e] : -INFINITY;                                                              \
-        VC[e] = keep ? VC[e] : VRow{};                                                               \
+        if constexpr (KV8)                                                                           \
+          vq[SL][e] = keep ? vq[SL][e] : VRow8{};                                                    \
+        else                                                                                         \
+          vb[SL][e] = keep ? vb[SL][e] : VRow{};                                                     \
       }                                                                                              \
     }                                                                                                \
     const float lm = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));                                    \
@@ -349,12 +360,25 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     _Pragma("unroll") for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(fmaf(c[e], cs, -ref));          \
     lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);                                                       \
     const uint2 pb = make_uint2(pack2<ST>(pr[0], pr[1]), pack2<ST>(pr[2], pr[3]));                   \
-    _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                \
-      /* element j of each of the four rows: tokens 4*rg .. 4*rg+3 at dim DPL*col + j */             \
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;                                      \
-      const uint2 va = make_uint2(__builtin_amdgcn_perm(vword(VC[1], j >> 1), vword(VC[0], j >> 1), sel), \
-                                  __builtin_amdgcn_perm(vword(VC[3], j >> 1), vword(VC[2], j >> 1), sel)); \
-      acc[j] = mfma_pv<ST>(va, pb, acc[j]);                                                          \
+    if constexpr (KV8) {                                                                             \
+      /* tiles j, j+1 (j even): bytes j, j+1 of the four rows gathered pairwise into two */         \
+      /* dwords of codes, each widened into one operand dword of either tile */                      \
+      _Pragma("unroll") for (int j = 0; j < NT; j += 2) {                                           \
+        const uint32_t sel = (j & 2) ? 0x07030602u : 0x05010400u;                                    \
+        const uint32_t x_ = __builtin_amdgcn_perm(vword(vq[SL][1], j >> 2), vword(vq[SL][0], j >> 2), sel); \
+        const uint32_t y_ = __builtin_amdgcn_perm(vword(vq[SL][3], j >> 2), vword(vq[SL][2], j >> 2), sel); \
+        const uint2 xw_ = widen4<ST>(x_), yw_ = widen4<ST>(y_);                                      \
+        acc[j] = mfma_pv<ST>(make_uint2(xw_.x, yw_.x), pb, acc[j]);                                  \
+        acc[j + 1] = mfma_pv<ST>(make_uint2(xw_.y, yw_.y), pb, acc[j + 1]);                          \
+      }                                                                                              \
+    } else {                                                                                         \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                              \
+        /* element j of each of the four rows: tokens 4*rg .. 4*rg+3 at dim DPL*col + j */           \
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;                                    \
+        const uint2 va = make_uint2(__builtin_amdgcn_perm(vword(vb[SL][1], j >> 1), vword(vb[SL][0], j >> 1), sel), \
+                                    __builtin_amdgcn_perm(vword(vb[SL][3], j >> 1), vword(vb[SL][2], j >> 1), sel)); \
+        acc[j] = mfma_pv<ST>(va, pb, acc[j]);                                                        \
+      }                                                                                              \
     }                                                                                                \
   } while (0)
 
@@ -363,6 +387,16 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   for (int cb = b_begin; cb < b_end; cb += TABLE) {
     const int cn = min(TABLE, b_end - cb);  // blocks in this chunk
     if (cb != b_begin) __syncthreads();     // every wave has read the previous chunk's ids
+    // this wave: chunk blocks w, w + NW, ...
+    const int nwc = __builtin_amdgcn_readfirstlane(w < cn ? (cn - w + NW - 1) / NW : 0);
+    // The wave's first block is read from the table directly and its loads issued
+    // before the workgroup's staging of the chunk's ids completes, so the first K/V
+    // bytes are on their way one table round trip earlier.  An id outside the pool is
+    // replaced by block 0 here; the staged check below then discards the unit.
+    if (nwc > 0) {
+      const int id0 = __builtin_amdgcn_readfirstlane(table[cb + w]);
+      PC_LOAD(0, (id0 >= 0 && (int64_t)id0 < a.num_blocks) ? id0 : 0);
+    }
     int anybad = 0;
     for (int i = tid; i < cn; i += kThreads) {
       const int v = table[cb + i];
@@ -373,12 +407,10 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       bad = true;  // a block id outside the pool: nothing more is read, the outputs become NaN
       break;
     }
-    // this wave: chunk blocks w, w + NW, ...
-    const int nwc = __builtin_amdgcn_readfirstlane(w < cn ? (cn - w + NW - 1) / NW : 0);
     if (nwc == 0) continue;
     auto id_of = [&](int j) -> int { return sm.ids[w + min(j, nwc - 1) * NW]; };
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) PC_LOAD(st, __builtin_amdgcn_readfirstlane(id_of(st)));
+    for (int st = 1; st < STAGES - 1; ++st) PC_LOAD(st, __builtin_amdgcn_readfirstlane(id_of(st)));
     int id_next = id_of(STAGES - 1);
     // The ring turns a whole number of times: a step past the wave's last block in
     // the chunk consumes a repeat of that block (fetched again from cache) with
@@ -393,23 +425,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
         // keep the scheduler from sinking the prefetch below the wait for this block
         __builtin_amdgcn_sched_barrier(0);
         // a step past the wave's last block of this chunk sees no token
-        const int tok0 = it < nwc ? (cb + w + it * NW) * kBlockTokens : t_end;
-        if constexpr (KV8) {
-          // widen the block's codes to the query's type (exact)
-          uint4 kw[KS];
-          VRow vw[4];
-#pragma unroll
-          for (int k = 0; k < KS; ++k) {
-            const uint4 r = kq[st][k >> 1];
-            const uint2 lo = widen4<ST>((k & 1) ? r.z : r.x), hi = widen4<ST>((k & 1) ? r.w : r.y);
-            kw[k] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vw[e] = widen_row<ST>(vq[st][e]);
-          PC_BLOCK(kw, vw, tok0);
-        } else {
-          PC_BLOCK(kb[st], vb[st], tok0);
-        }
+        PC_BLOCK(st, it < nwc ? (cb + w + it * NW) * kBlockTokens : t_end);
       }
       it0 += STAGES;
     } while (it0 < nwc);
@@ -487,45 +503,82 @@ void decode_split_kernel(DecodeArgs a) {
   const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
                    (int64_t)L > (int64_t)a.max_partitions * kPartition;
   if (!bad && part * kPartition >= L) return;  // a partition past the sequence writes nothing
-  decode_unit<ST, D, G, NW, PCACHE_SPLIT_STAGES, TABLE, true, KV8>(a, sm, s, kvh, part);
+  constexpr int STAGES = KV8 ? PCACHE_SPLIT_STAGES_KV8 : PCACHE_SPLIT_STAGES;
+  decode_unit<ST, D, G, NW, STAGES, TABLE, true, KV8>(a, sm, s, kvh, part);
 }
 
-// One-pass path: persistent workgroups, units longest first, dealt in snake order.
+// One-pass path: persistent workgroups.  Round 0 takes units in index order (unit u =
+// kv head u % Hkv of sequence u / Hkv), so no ranking stands between the launch and the
+// first loads.  While round 0 runs, the sequence lengths are fetched; after it, the
+// remaining units are ranked longest first and dealt in snake order, and the workgroup
+// whose round-0 unit was the r-th longest receives the r-th shortest unit of round 1,
+// which evens out the sums across workgroups.
 template <class ST, int D, int G, bool KV8>
 __global__ __launch_bounds__(onepass_waves<D>() * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_ONEPASS_OCC)))
 void decode_onepass_kernel(DecodeArgs a) {
   constexpr int NW = onepass_waves<D>();
   constexpr int kThreads = NW * kWave;
+  constexpr int STAGES = KV8 ? PCACHE_ONEPASS_STAGES_KV8 : PCACHE_ONEPASS_STAGES;
   __shared__ UnitLds<NW, D, G, PCACHE_ONEPASS_TABLE> sm;
-  __shared__ int order_lds[kMaxRankedSeqs];  // order_lds[rank] = sequence of that length rank
+  __shared__ int order_lds[kMaxRankedSeqs];  // order_lds[rank] = later-round sequence of that length rank
   __shared__ int len_lds[kMaxRankedSeqs];
+  __shared__ int rank0_lds;                  // length rank of this workgroup's round-0 sequence
 
   const int S = a.num_seqs;
-  const bool ranked = a.longest_first && S <= kMaxRankedSeqs;
-  if (ranked) {
+  const int Hkv = a.num_kv_heads;
+  const int64_t units = (int64_t)S * Hkv;
+  const int64_t W = gridDim.x;
+  const int64_t k = blockIdx.x;
+  // ranking needs whole sequences in round 0 (W a multiple of Hkv) and a later round
+  const bool ranked = a.longest_first && S <= kMaxRankedSeqs && units > W && W % Hkv == 0;
+  const int S0 = (int)(W / Hkv);  // sequences of round 0 when ranked
+  if (ranked)  // read here, used after round 0 (its barriers publish the stores)
     for (int t = threadIdx.x; t < S; t += kThreads) len_lds[t] = a.seq_lens[t];
-    __syncthreads();
-    for (int t = threadIdx.x; t < S; t += kThreads) {
+
+  if (k < units) decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8>(a, sm, (int)(k / Hkv),
+                                                                                    (int)(k % Hkv), 0);
+  if (units <= W) return;
+  if (ranked) {
+    // sequences S0 .. S-1 by length, longest first (ties by index)
+    for (int t = S0 + (int)threadIdx.x; t < S; t += kThreads) {
       const int lt = len_lds[t];
       int rank = 0;
-      for (int u = 0; u < S; ++u) {
+      for (int u = S0; u < S; ++u) {
         const int lu = len_lds[u];
         rank += (lu > lt) || (lu == lt && u < t);
       }
       order_lds[rank] = t;
     }
+    // rank of this workgroup's round-0 sequence among sequences 0 .. S0-1
+    if (threadIdx.x < kWave) {
+      const int s0 = (int)(k / Hkv);
+      const int l0 = len_lds[s0];
+      int c = 0;
+      for (int u = threadIdx.x; u < S0; u += kWave) {
+        const int lu = len_lds[u];
+        c += (lu > l0) || (lu == l0 && u < s0);
+      }
+      for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+      if (threadIdx.x == 0) rank0_lds = c;
+    }
     __syncthreads();
   }
-  const int64_t units = (int64_t)S * a.num_kv_heads;
-  const int64_t W = gridDim.x;
-  const int64_t k = blockIdx.x;
-  for (int64_t round = 0; round * W < units; ++round) {
-    const int64_t pos = round * W + ((round & 1) ? W - 1 - k : k);
-    if (pos >= units) continue;  // the last round is partial
-    const int rank = (int)(pos / a.num_kv_heads);
-    const int kvh = (int)(pos % a.num_kv_heads);
-    const int s = ranked ? order_lds[rank] : rank;
-    decode_unit<ST, D, G, NW, PCACHE_ONEPASS_STAGES, PCACHE_ONEPASS_TABLE, false, KV8>(a, sm, s, kvh, 0);
+  // unit rank of the round-0 unit: the Hkv units of one sequence are consecutive
+  const int64_t r0 = ranked ? (int64_t)rank0_lds * Hkv + k % Hkv : k;
+  const int64_t rest = units - W;
+  for (int64_t round = 1; (round - 1) * W < rest; ++round) {
+    const int64_t f = (round & 1) ? W - 1 - r0 : r0;  // snake, shortest first for the longest round-0 unit
+    const int64_t q = (round - 1) * W + f;            // position among the later units
+    if (q >= rest) continue;                          // the last round is partial
+    int s, kvh;
+    if (ranked) {
+      s = order_lds[(int)(q / Hkv)];
+      kvh = (int)(q % Hkv);
+    } else {
+      s = (int)((W + q) / Hkv);
+      kvh = (int)((W + q) % Hkv);
+    }
+    decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8>(a, sm, s, kvh, 0);
   }
 }
 

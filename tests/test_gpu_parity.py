@@ -120,6 +120,27 @@ def test_variant_parity(dt, D, G, layout, path):
     check_attention(gh.out_f64(out), oracle.decode(wl, hpool), dt, f"{dt} D{D} G{G} {layout} {path}")
 
 
+MANY_UNITS = [
+    ("ranked, partial second round", 40, 8, 8, 128),    # 320 units over 256 workgroups
+    ("kv heads not dividing the grid", 200, 12, 3, 128),  # 600 units, rounds in index order
+    ("more sequences than ranked", 600, 2, 1, 128),       # S > 512: rounds in index order
+    ("ranked, several rounds, D=64", 300, 16, 4, 64),     # 1200 units
+]
+
+
+@pytest.mark.parametrize("what,S,Hq,Hkv,D", MANY_UNITS, ids=[m[0] for m in MANY_UNITS])
+def test_onepass_unit_dealing(what, S, Hq, Hkv, D):
+    """More (sequence, kv head) units than persistent workgroups: every unit must be
+    computed exactly once, whichever way the later rounds are dealt."""
+    rng = np.random.default_rng(S + Hq)
+    lengths = rng.integers(1, 400, size=S)
+    lengths[::7] = 0
+    wl = custom(20 + S, "bf16", Hq, Hkv, D, lengths)
+    out, _ = gh.decode(gh.filled_pool(wl), gh.DecodeInputs(wl), "single")
+    got = gh.out_f64(out)
+    check_attention(got, oracle.decode(wl, oracle.filled_pool(wl)), "bf16", f"one pass, {what}")
+
+
 @pytest.mark.parametrize("path", ["single", "split"])
 def test_zero_length_sequences(path):
     wl = custom(7, "bf16", 8, 2, 128, [0, 37, 0, 600])
