@@ -55,10 +55,10 @@ def _bind(lib):
     lib.oracle_write.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, i64, i64, vp, i64, i32, i32, i32, i32]
     lib.oracle_decode.restype = i32
     lib.oracle_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32, i32, i32,
-                                  f32, i32, i32]
+                                  f32, vp, i32, i32]
     lib.oracle_partials.restype = i32
     lib.oracle_partials.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32,
-                                    i32, i32, f32, i32, i32, i32, i32]
+                                    i32, i32, f32, vp, i32, i32, i32, i32]
     lib.oracle_merge.restype = i32
     lib.oracle_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32]
     lib.oracle_write_kv8.restype = i32
@@ -66,10 +66,10 @@ def _bind(lib):
                                      vp, vp, i64]
     lib.oracle_decode_kv8.restype = i32
     lib.oracle_decode_kv8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32, i32, i32,
-                                      f32, i32, vp, vp, i64, i32]
+                                      f32, vp, i32, vp, vp, i64, i32]
     lib.oracle_partials_kv8.restype = i32
     lib.oracle_partials_kv8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32,
-                                        i32, i32, f32, i32, i32, i32, vp, vp, i64, i32]
+                                        i32, i32, f32, vp, i32, i32, i32, vp, vp, i64, i32]
     lib.oracle_e4m3_decode.restype = None
     lib.oracle_e4m3_decode.argtypes = [vp, vp, i64]
     lib.oracle_e4m3_encode.restype = None
@@ -160,6 +160,17 @@ def _scales(wl):
             int(wl.scale_stride))
 
 
+def _slopes(wl, alibi_slopes):
+    """ALiBi slopes (float32, one per query head) passed explicitly, else the workload's, else None."""
+    a = alibi_slopes if alibi_slopes is not None else getattr(wl, "alibi_slopes", None)
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if a.shape != (wl.num_q_heads,):
+        raise ValueError("alibi_slopes must hold one float per query head")
+    return a
+
+
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     """Values (float64) of OCP E4M3 codes."""
     c = np.ascontiguousarray(codes, dtype=np.uint8)
@@ -209,9 +220,10 @@ def filled_pool(wl, step_write: bool = True) -> Pool:
 
 
 def decode(wl, pool: Pool, q: np.ndarray | None = None, seq_lens=None, block_tables=None, scale=None,
-           nthreads: int | None = None) -> np.ndarray:
-    """fp64 decode attention, [S, Hq, D]."""
+           nthreads: int | None = None, alibi_slopes=None) -> np.ndarray:
+    """fp64 decode attention, [S, Hq, D] (with ALiBi when the workload or the call gives slopes)."""
     lib = load()
+    al = _slopes(wl, alibi_slopes)
     q = np.ascontiguousarray(wl.q if q is None else q)
     sl = np.ascontiguousarray(wl.seq_lens if seq_lens is None else seq_lens, dtype=np.int32)
     bt = np.ascontiguousarray(wl.block_tables if block_tables is None else block_tables, dtype=np.int32)
@@ -222,23 +234,25 @@ def decode(wl, pool: Pool, q: np.ndarray | None = None, seq_lens=None, block_tab
         rc = lib.oracle_decode_kv8(_ptr(out), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound, wl.num_blocks,
                                    wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt), int(bt.shape[1]),
                                    _ptr(sl), S, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size,
-                                   float(wl.scale if scale is None else scale), _FMT[wl.dtype], _ptr(ks), _ptr(vs),
-                                   st, _nthreads(nthreads))
+                                   float(wl.scale if scale is None else scale), _ptr(al), _FMT[wl.dtype], _ptr(ks),
+                                   _ptr(vs), st, _nthreads(nthreads))
         _check(rc, "oracle_decode_kv8")
         return out
     rc = lib.oracle_decode(_ptr(out), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound, wl.num_blocks,
                            wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt), int(bt.shape[1]), _ptr(sl), S,
                            wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size,
-                           float(wl.scale if scale is None else scale), _FMT[wl.dtype], _nthreads(nthreads))
+                           float(wl.scale if scale is None else scale), _ptr(al), _FMT[wl.dtype],
+                           _nthreads(nthreads))
     _check(rc, "oracle_decode")
     return out
 
 
 def partials(wl, pool: Pool, partition_size: int, max_partitions: int | None = None, q=None, seq_lens=None,
-             block_tables=None, nthreads: int | None = None, fill: float = np.nan):
+             block_tables=None, nthreads: int | None = None, fill: float = np.nan, alibi_slopes=None):
     """Per-partition (tmp_out [S,Hq,P,D], max_logits [S,Hq,P], exp_sums [S,Hq,P]); slots of
     partitions that hold no token keep ``fill``."""
     lib = load()
+    al = _slopes(wl, alibi_slopes)
     q = np.ascontiguousarray(wl.q if q is None else q)
     sl = np.ascontiguousarray(wl.seq_lens if seq_lens is None else seq_lens, dtype=np.int32)
     bt = np.ascontiguousarray(wl.block_tables if block_tables is None else block_tables, dtype=np.int32)
@@ -254,14 +268,14 @@ def partials(wl, pool: Pool, partition_size: int, max_partitions: int | None = N
         rc = lib.oracle_partials_kv8(_ptr(tmp), _ptr(ml), _ptr(es), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound,
                                      wl.num_blocks, wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt),
                                      int(bt.shape[1]), _ptr(sl), S, H, wl.num_kv_heads, D, wl.block_size,
-                                     float(wl.scale), partition_size, max_partitions, _FMT[wl.dtype], _ptr(ks),
-                                     _ptr(vs), st, _nthreads(nthreads))
+                                     float(wl.scale), _ptr(al), partition_size, max_partitions, _FMT[wl.dtype],
+                                     _ptr(ks), _ptr(vs), st, _nthreads(nthreads))
         _check(rc, "oracle_partials_kv8")
         return tmp, ml, es
     rc = lib.oracle_partials(_ptr(tmp), _ptr(ml), _ptr(es), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound,
                              wl.num_blocks, wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt),
                              int(bt.shape[1]), _ptr(sl), S, H, wl.num_kv_heads, D, wl.block_size, float(wl.scale),
-                             partition_size, max_partitions, _FMT[wl.dtype], _nthreads(nthreads))
+                             _ptr(al), partition_size, max_partitions, _FMT[wl.dtype], _nthreads(nthreads))
     _check(rc, "oracle_partials")
     return tmp, ml, es
 

@@ -30,6 +30,11 @@
  *                    x_t = scale * q.k_t, m = max x, p_t = exp(x_t - m),
  *                    out = sum p_t v_t / sum p_t, all in double.  No epsilon in the
  *                    denominator; scale is the caller's float widened to double.
+ *                    With ALiBi (alibi_slopes non-NULL, one slope a_h per query
+ *                    head; same page, section 第一步): x_t = scale * q.k_t +
+ *                    a_h * (t - (L_s - 1)) -- zero at the newest position, the
+ *                    negative distance times the slope before it, added before
+ *                    the softmax.
  *
  *  oracle_partials, oracle_merge -- the split-context form of "vLLM 源码完全拆解
  *                    （七）", section V1与V2 (512-token partitions; a partition past
@@ -228,6 +233,7 @@ typedef struct {
     const int32_t *seq_lens;
     int num_seqs, num_q_heads, num_kv_heads, head_size, block_size;
     double scale;
+    const float *alibi_slopes;       /* NULL, or one slope per query head */
     int fmt;                         /* q (and out) */
     int kv_fmt;                      /* the pool */
     const float *k_scale, *v_scale;  /* E4M3 pool: head kv uses scale[kv * scale_stride] */
@@ -277,16 +283,18 @@ static int gather_rows(const job_t *j, int s, int kv, int t0, int t1, double *K,
     return OR_OK;
 }
 
-/* Dense softmax attention of one query over n materialised rows.
+/* Dense softmax attention of one query over n materialised rows; row t sits at
+ * position pos0 + t relative to the newest token (so pos0 + t <= 0), which the ALiBi
+ * term slope * (pos0 + t) uses (slope 0 without ALiBi).
  * Writes o[D] = sum p_t v_t / sum p_t, *m = max x_t, *l = sum p_t. */
 static void dense_attention(const double *qv, const double *K, const double *V, int n, int D, double scale,
-                            double *x, double *o, double *m_out, double *l_out) {
+                            double slope, int64_t pos0, double *x, double *o, double *m_out, double *l_out) {
     double m = -INFINITY;
     for (int t = 0; t < n; ++t) {
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
             dot += qv[d] * K[(int64_t)t * D + d];
-        x[t] = scale * dot;
+        x[t] = scale * dot + slope * (double)(pos0 + t);
         if (x[t] > m)
             m = x[t];
     }
@@ -319,6 +327,7 @@ static int run_item(job_t *j, int64_t item, double *K, double *V, double *x, dou
         s = (int)(item / j->num_q_heads);
     }
     int kv = h / G;
+    double slope = j->alibi_slopes ? (double)j->alibi_slopes[h] : 0.0;
     int L = j->seq_lens[s];
     if (L < 0 || (int64_t)L > (int64_t)j->max_blocks_per_seq * j->block_size)
         return OR_ERANGE;
@@ -336,7 +345,7 @@ static int run_item(job_t *j, int64_t item, double *K, double *V, double *x, dou
         if (rc)
             return rc;
         double m, l;
-        dense_attention(qv, K, V, L, D, j->scale, x, o, &m, &l);
+        dense_attention(qv, K, V, L, D, j->scale, slope, -(int64_t)(L - 1), x, o, &m, &l);
         return OR_OK;
     }
 
@@ -350,7 +359,8 @@ static int run_item(job_t *j, int64_t item, double *K, double *V, double *x, dou
     if (rc)
         return rc;
     int64_t sp = ((int64_t)s * j->num_q_heads + h) * j->max_partitions + p;
-    dense_attention(qv, K, V, t1 - t0, D, j->scale, x, j->tmp_out + sp * D, &j->max_logits[sp], &j->exp_sums[sp]);
+    dense_attention(qv, K, V, t1 - t0, D, j->scale, slope, (int64_t)t0 - (L - 1), x, j->tmp_out + sp * D,
+                    &j->max_logits[sp], &j->exp_sums[sp]);
     return OR_OK;
 }
 
@@ -439,8 +449,8 @@ static int check_common(const void *q, const void *k_pool, const void *v_pool, c
 int oracle_decode(double *out, const void *q, const void *k_pool, const void *v_pool, int64_t pool_elems,
                   int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
                   const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens, int num_seqs,
-                  int num_q_heads, int num_kv_heads, int head_size, int block_size, float scale, int fmt,
-                  int nthreads) {
+                  int num_q_heads, int num_kv_heads, int head_size, int block_size, float scale,
+                  const float *alibi_slopes, int fmt, int nthreads) {
     int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
                           head_size, block_size, max_blocks_per_seq, fmt);
     if (rc)
@@ -466,6 +476,7 @@ int oracle_decode(double *out, const void *q, const void *k_pool, const void *v_
     j.head_size = head_size;
     j.block_size = block_size;
     j.scale = (double)scale;
+    j.alibi_slopes = alibi_slopes;
     j.fmt = fmt;
     j.kv_fmt = fmt;
     j.out = out;
@@ -477,7 +488,8 @@ int oracle_partials(double *tmp_out, double *max_logits, double *exp_sums, const
                     const void *v_pool, int64_t pool_elems, int64_t num_blocks, int64_t block_stride,
                     int64_t token_stride, int64_t head_stride, const int32_t *block_tables, int max_blocks_per_seq,
                     const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
-                    int block_size, float scale, int partition_size, int max_partitions, int fmt, int nthreads) {
+                    int block_size, float scale, const float *alibi_slopes, int partition_size, int max_partitions,
+                    int fmt, int nthreads) {
     int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
                           head_size, block_size, max_blocks_per_seq, fmt);
     if (rc)
@@ -503,6 +515,7 @@ int oracle_partials(double *tmp_out, double *max_logits, double *exp_sums, const
     j.head_size = head_size;
     j.block_size = block_size;
     j.scale = (double)scale;
+    j.alibi_slopes = alibi_slopes;
     j.fmt = fmt;
     j.kv_fmt = fmt;
     j.partition_size = partition_size;
@@ -559,8 +572,9 @@ int oracle_merge(double *out, const double *tmp_out, const double *max_logits, c
 int oracle_decode_kv8(double *out, const void *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t pool_elems,
                       int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
                       const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens, int num_seqs,
-                      int num_q_heads, int num_kv_heads, int head_size, int block_size, float scale, int fmt,
-                      const float *k_scale, const float *v_scale, int64_t scale_stride, int nthreads) {
+                      int num_q_heads, int num_kv_heads, int head_size, int block_size, float scale,
+                      const float *alibi_slopes, int fmt, const float *k_scale, const float *v_scale,
+                      int64_t scale_stride, int nthreads) {
     int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
                           head_size, block_size, max_blocks_per_seq, fmt);
     if (rc)
@@ -586,6 +600,7 @@ int oracle_decode_kv8(double *out, const void *q, const uint8_t *k_pool, const u
     j.head_size = head_size;
     j.block_size = block_size;
     j.scale = (double)scale;
+    j.alibi_slopes = alibi_slopes;
     j.fmt = fmt;
     j.kv_fmt = 3;
     j.k_scale = k_scale;
@@ -600,9 +615,9 @@ int oracle_partials_kv8(double *tmp_out, double *max_logits, double *exp_sums, c
                         const uint8_t *v_pool, int64_t pool_elems, int64_t num_blocks, int64_t block_stride,
                         int64_t token_stride, int64_t head_stride, const int32_t *block_tables,
                         int max_blocks_per_seq, const int32_t *seq_lens, int num_seqs, int num_q_heads,
-                        int num_kv_heads, int head_size, int block_size, float scale, int partition_size,
-                        int max_partitions, int fmt, const float *k_scale, const float *v_scale,
-                        int64_t scale_stride, int nthreads) {
+                        int num_kv_heads, int head_size, int block_size, float scale, const float *alibi_slopes,
+                        int partition_size, int max_partitions, int fmt, const float *k_scale,
+                        const float *v_scale, int64_t scale_stride, int nthreads) {
     int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
                           head_size, block_size, max_blocks_per_seq, fmt);
     if (rc)
@@ -629,6 +644,7 @@ int oracle_partials_kv8(double *tmp_out, double *max_logits, double *exp_sums, c
     j.head_size = head_size;
     j.block_size = block_size;
     j.scale = (double)scale;
+    j.alibi_slopes = alibi_slopes;
     j.fmt = fmt;
     j.kv_fmt = 3;
     j.k_scale = k_scale;

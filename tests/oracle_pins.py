@@ -10,7 +10,9 @@ the oracle disagrees with something it does not compute itself:
   history, a tile-wise online softmax, a pure-Python per-token brute force);
 * the split identity (per-partition partials merged = the whole sequence);
 * for the 8-bit cache: the OCP E4M3 landmarks and torch's float8_e4m3fn converter,
-  and dense attention on dequantised rows.
+  and dense attention on dequantised rows;
+* for ALiBi: zero slopes change nothing, torch's attention with the bias as an
+  additive mask, the geometric weights of q = 0, and the partials' maxima.
 
 ``tests/test_oracle_pins.py`` runs them; ``tests/test_oracle_mutants.py`` plants
 mistakes in copies of the oracle and requires some pin to fail for each.
@@ -29,7 +31,7 @@ import numpy as np
 import brute
 import oracle
 from helpers import GOLDEN, bits_to_f64, dense_numpy, f64_to_bits, online_tiles_numpy
-from workloads import custom, fp8_variant, make_config, nan_bits
+from workloads import alibi_variant, custom, fp8_variant, make_config, nan_bits
 
 B = 16
 
@@ -569,11 +571,92 @@ def pin_kv8_decode():
         assert np.abs(oracle.merge(tmp, ml, es, w.seq_lens, P) - out).max() < 1e-13
 
 
+# ---------------------------------------------------------------------------------
+# ALiBi ("vLLM 源码完全拆解（七）", 第一步: score of token t gains a_h * (t - (L - 1)))
+# ---------------------------------------------------------------------------------
+
+def _alibi_wl(dtype="bf16", lengths=(1, 2, 17, 300, 700), Hq=8, Hkv=2, D=64, seed=30):
+    w = custom(seed, dtype, Hq, Hkv, D, list(lengths))
+    # slopes of both signs and sizes, one per query head (distinct within a kv group)
+    slopes = np.linspace(-0.05, 0.4, Hq).astype(np.float32)[::-1].copy()
+    return alibi_variant(w, slopes)
+
+
+def pin_alibi_zero_slopes():
+    """All slopes 0: bit-identical to the decode without ALiBi (and the partials)."""
+    w = custom(31, "f16", 8, 4, 128, [1, 33, 520])
+    z = alibi_variant(w, np.zeros(8, np.float32))
+    pool = oracle.filled_pool(w)
+    assert np.array_equal(oracle.decode(z, pool), oracle.decode(w, pool))
+    a, b = oracle.partials(z, pool, 512), oracle.partials(w, pool, 512)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True)
+
+
+def pin_alibi_torch_sdpa():
+    """torch scaled_dot_product_attention in float64 with the bias a_h * (t - (L - 1))
+    as an additive float mask agrees to 1e-12 (query head h uses slope a_h)."""
+    import torch
+    w = _alibi_wl()
+    out = oracle.decode(w, oracle.filled_pool(w))
+    G = w.num_q_heads // w.num_kv_heads
+    q = torch.from_numpy(bits_to_f64(w.q, w.dtype))
+    a = torch.from_numpy(w.alibi_slopes.astype(np.float64))
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        K = torch.from_numpy(bits_to_f64(w.logical_k(s), w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        V = torch.from_numpy(bits_to_f64(w.logical_v(s), w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        dist = torch.arange(L, dtype=torch.float64) - (L - 1)  # <= 0, 0 at the newest token
+        mask = (a[:, None] * dist[None, :]).unsqueeze(1)         # [Hq, 1, L]
+        ref = torch.nn.functional.scaled_dot_product_attention(q[s].unsqueeze(1), K, V, attn_mask=mask,
+                                                               scale=float(w.scale))
+        assert (ref[:, 0, :].numpy() - out[s]).__abs__().max() < 1e-12, s
+
+
+def pin_alibi_geometric_weights():
+    """q = 0 leaves only the bias: token t weighs r^(L-1-t) with r = e^(-a_h), so the
+    output is that geometric average of V (numpy, written from the powers)."""
+    w = _alibi_wl(dtype="f32", lengths=(1, 5, 64, 129))
+    pool = oracle.filled_pool(w)
+    out = oracle.decode(w, pool, q=np.zeros_like(w.q))
+    G = w.num_q_heads // w.num_kv_heads
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        V = bits_to_f64(w.logical_v(s), w.dtype)
+        for h in range(w.num_q_heads):
+            r = math.exp(-float(w.alibi_slopes[h]))
+            wts = np.array([r ** (L - 1 - t) for t in range(L)])
+            ref = wts @ V[:, h // G] / wts.sum()
+            assert np.abs(out[s, h] - ref).max() < 1e-12, (s, h)
+
+
+def pin_alibi_partials():
+    """With q = 0 the max score of partition p is a_h * (last position of p - (L - 1))
+    (a_h >= 0) or a_h * (first position of p - (L - 1)) (a_h < 0), exactly; the partials
+    merge to the whole-sequence result."""
+    w = _alibi_wl(dtype="bf16", lengths=(1, 511, 512, 513, 1500))
+    pool = oracle.filled_pool(w)
+    zq = np.zeros_like(w.q)
+    dense = oracle.decode(w, pool, q=zq)
+    for P in (16, 512):
+        tmp, ml, es = oracle.partials(w, pool, P, q=zq)
+        for s in range(w.num_seqs):
+            L = int(w.seq_lens[s])
+            for p in range(-(-L // P)):
+                first, last = p * P, min(L, (p + 1) * P) - 1
+                for h in range(w.num_q_heads):
+                    a = float(w.alibi_slopes[h])
+                    want = a * ((last if a >= 0 else first) - (L - 1))
+                    assert abs(ml[s, h, p] - want) < 1e-12, (P, s, p, h)
+        assert np.abs(oracle.merge(tmp, ml, es, w.seq_lens, P) - dense).max() < 1e-13, P
+
+
 PINS = [
     pin_slot_write, pin_slot_read, pin_invariant_line, pin_gqa_mapping, pin_worked_decode,
     pin_combined_block_layout, pin_one_token_exact, pin_special_values_exact, pin_zero_query_mean,
     pin_equal_keys_mean, pin_two_tokens_sigmoid, pin_huge_logits, pin_placement_invariance,
     pin_negative_slot_skipped, pin_unread_memory, pin_table_padding, pin_write_out_of_range,
     pin_numpy_dense, pin_torch_sdpa, pin_online_tiles, pin_brute_force, pin_split_identity,
-    pin_e4m3_values, pin_e4m3_rounding, pin_kv8_write, pin_kv8_decode,
+    pin_e4m3_values, pin_e4m3_rounding, pin_kv8_write, pin_kv8_decode, pin_alibi_zero_slopes,
+    pin_alibi_torch_sdpa, pin_alibi_geometric_weights, pin_alibi_partials,
 ]

@@ -28,11 +28,10 @@ MUTANTS = {
                             "load_elem(j->k_pool, base + d, j->kv_fmt) * vs;"),
     "query_head_swapped": ("qv[d] = load_elem(j->q, ((int64_t)s * j->num_q_heads + h) * D + d, j->fmt);",
                            "qv[d] = load_elem(j->q, ((int64_t)s * j->num_q_heads + (h ^ 1)) * D + d, j->fmt);"),
-    "scale_dropped": ("x[t] = scale * dot;", "x[t] = dot;"),
+    "scale_dropped": ("x[t] = scale * dot + slope", "x[t] = dot + slope"),
     "max_not_subtracted": ("x[t] = exp(x[t] - m);", "x[t] = exp(x[t]);"),
     "epsilon_denominator": ("o[d] = acc / l;", "o[d] = acc / (l + 1e-6);"),
-    "last_token_dropped": ("dense_attention(qv, K, V, L, D, j->scale, x, o, &m, &l);",
-                           "dense_attention(qv, K, V, L > 1 ? L - 1 : L, D, j->scale, x, o, &m, &l);"),
+    "last_token_dropped": ("dense_attention(qv, K, V, L, D, j->scale,", "dense_attention(qv, K, V, L > 1 ? L - 1 : L, D, j->scale,"),
     "partition_not_clipped": ("int t1 = t0 + j->partition_size < L ? t0 + j->partition_size : L;",
                               "int t1 = t0 + j->partition_size;"),
     "merge_without_rescale": (
@@ -50,6 +49,10 @@ MUTANTS = {
     "kv8_read_scale_dropped": ("ks = (double)j->k_scale[(int64_t)kv * j->scale_stride];", "ks = 1.0;"),
     "kv8_read_v_scale_from_k": ("vs = (double)j->v_scale[(int64_t)kv * j->scale_stride];",
                                 "vs = (double)j->k_scale[(int64_t)kv * j->scale_stride];"),
+    "alibi_sign_flipped": ("+ slope * (double)(pos0 + t);", "- slope * (double)(pos0 + t);"),
+    "alibi_slope_of_kv_head": ("j->alibi_slopes[h]", "j->alibi_slopes[kv]"),
+    "alibi_partition_origin": ("(int64_t)t0 - (L - 1)", "-(int64_t)(L - 1)"),
+    "alibi_partials_off_by_one": ("(int64_t)t0 - (L - 1)", "(int64_t)t0 - L"),
 }
 
 

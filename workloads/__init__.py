@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     BLOCK_SIZE,
     CONFIG_NAMES,
     Workload,
+    alibi_variant,
     custom,
     dtype_nbytes,
     fp8_variant,

@@ -158,6 +158,8 @@ class Workload:
     k_scale: np.ndarray = field(repr=False, default=None)  # float32
     v_scale: np.ndarray = field(repr=False, default=None)
     scale_stride: int = 0
+    # ALiBi: one float32 slope per query head (None: no positional bias)
+    alibi_slopes: np.ndarray = field(repr=False, default=None)
 
     # ----- sizes -------------------------------------------------------------------
     @property
@@ -497,3 +499,16 @@ def fp8_variant(wl: Workload, per_head: bool = True, lo: float = 0.008, hi: floa
     vs = rng.uniform(lo, hi, size=n).astype(np.float32)
     name = wl.name.replace(wl.dtype, f"{wl.dtype}q_fp8e4m3", 1) if wl.dtype in wl.name else wl.name + "_fp8e4m3"
     return replace(wl, name=name, kv_dtype="fp8", k_scale=ks, v_scale=vs, scale_stride=1 if per_head else 0)
+
+
+def alibi_variant(wl: Workload, slopes=None) -> Workload:
+    """The same workload with an ALiBi bias.  ``slopes`` (one per query head) default
+    to the geometric sequence 2^(-8 (h + 1) / Hq), the usual recipe for Hq heads;
+    they are inputs here, not part of the method."""
+    H = wl.num_q_heads
+    if slopes is None:
+        slopes = 2.0 ** (-8.0 * (np.arange(H) + 1) / H)
+    slopes = np.ascontiguousarray(slopes, dtype=np.float32)
+    if slopes.shape != (H,):
+        raise ValueError("one slope per query head")
+    return replace(wl, name=wl.name + "_alibi", alibi_slopes=slopes)
