@@ -151,6 +151,12 @@ int pc_reshape_and_cache(const void *key, const void *value, int64_t key_row_str
  *                     and the normalised partial output [.., P, head_size].
  *                     Partitions past a sequence's length are not written.
  *                     All three must be NULL when partition_size == 0.
+ *   alibi_slopes      NULL (no positional bias) or device fp32 [num_q_heads]: the
+ *                     ALiBi bias of "vLLM 源码完全拆解（七）", section 第一步 -- the
+ *                     score of token t of query head h becomes scale * q.k_t +
+ *                     alibi_slopes[h] * (t - (seq_len - 1)) before the softmax (zero
+ *                     at the newest token, the negative distance times the slope
+ *                     before it).  The split partials' max_logits include the bias.
  * A sequence with seq_len 0 gets zeros (one pass) or no partials (split).
  * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
  */
@@ -159,7 +165,8 @@ int pc_paged_attention_decode(void *out, const void *q, const void *k_pool, cons
                               int64_t head_stride, const int32_t *block_tables, int max_blocks_per_seq,
                               const int32_t *seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
                               int num_kv_heads, int head_size, int block_size, float scale, int partition_size,
-                              float *exp_sums, float *max_logits, float *tmp_out, int dtype, void *stream);
+                              float *exp_sums, float *max_logits, float *tmp_out, const float *alibi_slopes,
+                              int dtype, void *stream);
 
 /*
  * pc_reshape_and_cache_fp8 -- write new K/V rows into an 8-bit (OCP E4M3) pool.
@@ -213,8 +220,8 @@ int pc_paged_attention_decode_fp8(void *out, const void *q, const uint8_t *k_poo
                                   const int32_t *seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
                                   int num_kv_heads, int head_size, int block_size, float scale,
                                   int partition_size, float *exp_sums, float *max_logits, float *tmp_out,
-                                  const float *k_scale, const float *v_scale, int64_t kv_scale_stride, int dtype,
-                                  void *stream);
+                                  const float *alibi_slopes, const float *k_scale, const float *v_scale,
+                                  int64_t kv_scale_stride, int dtype, void *stream);
 
 /*
  * pc_paged_attention_reduce -- merge the split path's partials.

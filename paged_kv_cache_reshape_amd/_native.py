@@ -44,14 +44,14 @@ def _load():
                                              i32, vp]
         lib.pc_paged_attention_decode.restype = i32
         lib.pc_paged_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32,
-                                                  i32, i32, i32, f32, i32, vp, vp, vp, i32, vp]
+                                                  i32, i32, i32, f32, i32, vp, vp, vp, vp, i32, vp]
         lib.pc_reshape_and_cache_fp8.restype = i32
         lib.pc_reshape_and_cache_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, i64, i64, vp, i64, i32, i32,
                                                  i32, vp, vp, i64, i32, vp]
         lib.pc_paged_attention_decode_fp8.restype = i32
         lib.pc_paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32,
-                                                      i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, i64, i32,
-                                                      vp]
+                                                      i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, i64,
+                                                      i32, vp]
         lib.pc_paged_attention_reduce.restype = i32
         lib.pc_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.pc_paged_attention_plan.restype = i32
@@ -140,11 +140,12 @@ def paged_attention_decode(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
                            block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, *,
                            num_kv_heads: int, scale: float, num_blocks: int, block_stride: int, token_stride: int,
                            head_stride: int, block_size: int = 16, v_offset: int = 0, partition_size: int = 0,
-                           exp_sums=None, max_logits=None, tmp_out=None, stream=None) -> None:
+                           exp_sums=None, max_logits=None, tmp_out=None, alibi_slopes=None, stream=None) -> None:
     """Decode attention of ``q`` [S, Hq, D] over the paged pool.  ``partition_size`` 0 writes
     ``out``; 512 writes only the partials (``exp_sums``, ``max_logits`` [S, Hq, P], ``tmp_out``
-    [S, Hq, P, D], fp32)."""
-    _same_device(out, q, k_pool, v_pool, block_tables, seq_lens, exp_sums, max_logits, tmp_out)
+    [S, Hq, P, D], fp32).  ``alibi_slopes``: optional fp32 [Hq] ALiBi slopes."""
+    _same_device(out, q, k_pool, v_pool, block_tables, seq_lens, exp_sums, max_logits, tmp_out, alibi_slopes)
+    _check_alibi(alibi_slopes, q)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [S, Hq, D]")
     if out is not None and (out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype):
@@ -163,9 +164,15 @@ def paged_attention_decode(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
     st = _load().pc_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
         head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads,
-        D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), dt,
-        _stream(q, stream))
+        D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(alibi_slopes),
+        dt, _stream(q, stream))
     _check("pc_paged_attention_decode", st)
+
+
+def _check_alibi(alibi_slopes, q):
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_contiguous()
+                                     or alibi_slopes.numel() != q.shape[1]):
+        raise ValueError("alibi_slopes must be a contiguous float32 [num_q_heads]")
 
 
 def _check_kv_scales(k_scale, v_scale, num_kv_heads: int, kv_scale_stride: int):
@@ -208,10 +215,12 @@ def paged_attention_decode_fp8(out, q: torch.Tensor, k_pool: torch.Tensor, v_poo
                                num_blocks: int, block_stride: int, token_stride: int, head_stride: int,
                                kv_scale_stride: int = 1, block_size: int = 16, v_offset: int = 0,
                                partition_size: int = 0, exp_sums=None, max_logits=None, tmp_out=None,
-                               stream=None) -> None:
+                               alibi_slopes=None, stream=None) -> None:
     """``paged_attention_decode`` over uint8 pools of E4M3 codes (strides in bytes); K and V are
     the codes times the kv head's ``k_scale`` / ``v_scale``.  ``q`` is fp16 or bf16."""
-    _same_device(out, q, k_pool, v_pool, block_tables, seq_lens, exp_sums, max_logits, tmp_out, k_scale, v_scale)
+    _same_device(out, q, k_pool, v_pool, block_tables, seq_lens, exp_sums, max_logits, tmp_out, k_scale, v_scale,
+                 alibi_slopes)
+    _check_alibi(alibi_slopes, q)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [S, Hq, D]")
     if out is not None and (out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype):
@@ -231,8 +240,8 @@ def paged_attention_decode_fp8(out, q: torch.Tensor, k_pool: torch.Tensor, v_poo
     st = _load().pc_paged_attention_decode_fp8(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
         head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads,
-        D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(k_scale),
-        _ptr(v_scale), kv_scale_stride, dt, _stream(q, stream))
+        D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(alibi_slopes),
+        _ptr(k_scale), _ptr(v_scale), kv_scale_stride, dt, _stream(q, stream))
     _check("pc_paged_attention_decode_fp8", st)
 
 

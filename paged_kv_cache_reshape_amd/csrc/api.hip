@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kBlockTokens = 16;
 
 int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
@@ -50,8 +50,8 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
                 int64_t block_stride, int64_t token_stride, int64_t head_stride, const int32_t* block_tables,
                 int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
                 int num_kv_heads, int head_size, int block_size, float scale, int partition_size, float* exp_sums,
-                float* max_logits, float* tmp_out, const float* k_scale, const float* v_scale,
-                int64_t kv_scale_stride, int dtype, bool kv8, void* stream) {
+                float* max_logits, float* tmp_out, const float* alibi_slopes, const float* k_scale,
+                const float* v_scale, int64_t kv_scale_stride, int dtype, bool kv8, void* stream) {
   const int es = esize(dtype);
   if (!es || num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_size <= 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0 || (kv8 && kv_scale_stride < 0))
@@ -102,6 +102,7 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   a.max_logits = max_logits;
   a.tmp_out = tmp_out;
   a.kv8 = kv8;
+  a.alibi_slopes = alibi_slopes;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.scale_stride = kv_scale_stride;
@@ -197,11 +198,11 @@ int pc_paged_attention_decode(void* out, const void* q, const void* k_pool, cons
                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
                               int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
                               int block_size, float scale, int partition_size, float* exp_sums, float* max_logits,
-                              float* tmp_out, int dtype, void* stream) {
+                              float* tmp_out, const float* alibi_slopes, int dtype, void* stream) {
   return decode_impl(out, q, k_pool, v_pool, num_blocks, block_stride, token_stride, head_stride, block_tables,
                      max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
-                     block_size, scale, partition_size, exp_sums, max_logits, tmp_out, nullptr, nullptr, 0, dtype,
-                     false, stream);
+                     block_size, scale, partition_size, exp_sums, max_logits, tmp_out, alibi_slopes, nullptr,
+                     nullptr, 0, dtype, false, stream);
 }
 
 int pc_paged_attention_decode_fp8(void* out, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
@@ -209,12 +210,13 @@ int pc_paged_attention_decode_fp8(void* out, const void* q, const uint8_t* k_poo
                                   const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
                                   int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
                                   int block_size, float scale, int partition_size, float* exp_sums,
-                                  float* max_logits, float* tmp_out, const float* k_scale, const float* v_scale,
-                                  int64_t kv_scale_stride, int dtype, void* stream) {
+                                  float* max_logits, float* tmp_out, const float* alibi_slopes,
+                                  const float* k_scale, const float* v_scale, int64_t kv_scale_stride, int dtype,
+                                  void* stream) {
   return decode_impl(out, q, k_pool, v_pool, num_blocks, block_stride, token_stride, head_stride, block_tables,
                      max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
-                     block_size, scale, partition_size, exp_sums, max_logits, tmp_out, k_scale, v_scale,
-                     kv_scale_stride, dtype, true, stream);
+                     block_size, scale, partition_size, exp_sums, max_logits, tmp_out, alibi_slopes, k_scale,
+                     v_scale, kv_scale_stride, dtype, true, stream);
 }
 
 int pc_paged_attention_reduce(void* out, const float* exp_sums, const float* max_logits, const float* tmp_out,

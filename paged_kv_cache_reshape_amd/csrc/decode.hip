@@ -84,6 +84,12 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_kernel(DecodeArgs a) {
     for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(qb + (int64_t)g * D * EB);
   }
 
+  // ALiBi slopes of the group's query heads, in the base-2 score domain
+  const bool alibi = a.alibi_slopes != nullptr;
+  float ab[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) ab[g] = alibi ? a.alibi_slopes[h0 + g] * kLog2e : 0.f;
+
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -152,6 +158,14 @@ __global__ __launch_bounds__(kWaves* kWave) void decode_kernel(DecodeArgs a) {
     for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int g = 0; g < G; ++g) sc[j][g] = group_sum<LPR>(dot16<ST>(kc[j], qv[g], 0.f)) * a.scale_log2;
+    if (alibi) {  // signed distance of the row's token to the newest position, times the slope
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const float dist = (float)(b * kBlockTokens + j * TPI + lr - (L - 1));
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[j][g] = fmaf(ab[g], dist, sc[j][g]);
+      }
+    }
 
     const int visible = t_end - b * kBlockTokens;
     if (visible < kBlockTokens) {  // last block: positions >= seq_len take no part

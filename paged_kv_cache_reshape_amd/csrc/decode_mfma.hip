@@ -203,6 +203,15 @@ __device__ __forceinline__ uint32_t vword(uint32_t v, int) { return v; }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wave-uniform reads of data the kernel never writes (lengths, block tables, slopes),
+// through the scalar data cache: they count on their own counter, so waiting for one
+// does not also wait for the vector loads issued before it.
+template <class T>
+__device__ __forceinline__ T uniform_load(const T* p, int64_t i) {
+  typedef const __attribute__((address_space(4))) T cT;
+  return ((cT*)p)[i];
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
@@ -213,7 +222,16 @@ struct UnitLds {
   float mw[NW][G];
   float lw[NW][G];
   int ids[TABLE];  // block ids of the unit's current chunk
+  int bad;         // some id of the unit lies outside the pool
 };
+
+// Barrier that orders LDS only: vector loads in flight stay in flight across it
+// (__syncthreads() also waits for every outstanding global access of the wave).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // One unit: kv head `kvh` of sequence `s`, tokens [t_begin, t_end).  All waves of
 // the workgroup call it together (it uses block-wide barriers).  Writes out (one
@@ -241,10 +259,10 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const int rg = lane >> 4;   // row group of the score tile: tokens 4*rg .. 4*rg+3
   const int col = lane & 15;  // score column: query head of the group
 
-  const int L = a.seq_lens[s];
+  const int L = uniform_load(a.seq_lens, s);
   // 8-bit pool: the kv head's dequantisation scales (k_scale folded into the score scale)
-  const float ksc = KV8 ? a.k_scale[(int64_t)kvh * a.scale_stride] : 1.f;
-  const float vsc = KV8 ? a.v_scale[(int64_t)kvh * a.scale_stride] : 1.f;
+  const float ksc = KV8 ? uniform_load(a.k_scale, (int64_t)kvh * a.scale_stride) : 1.f;
+  const float vsc = KV8 ? uniform_load(a.v_scale, (int64_t)kvh * a.scale_stride) : 1.f;
   const float cs_raw = a.scale_log2 * ksc;
   const bool bad_scale = KV8 && !(cs_raw >= 0x1p-120f && cs_raw <= 0x1p120f && vsc > 0.f && vsc <= 3.4e38f);
   bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
@@ -286,6 +304,19 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const int k_off = col * tok_bytes + (KV8 ? rg * (D / 4) : 16 * rg);
   const int v_off = 4 * rg * tok_bytes + col * (EB * DPL);  // + e*tok_bytes for row 4*rg + e
   const float lazy_raw = kLazy / cs;
+  // ALiBi: the bias of head `col` in raw q.k units (times cs it is slope * log2 e per
+  // token).  The slope is loaded here and converted after the first K/V loads are out.
+  const bool alibi = a.alibi_slopes != nullptr;
+  float slope = 0.f;
+  if (alibi) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sg = uniform_load(a.alibi_slopes, h0 + g);
+      slope = col == g ? sg : slope;
+    }
+  }
+  float ab = 0.f;
+  const int last_pos = L - 1;
 
   uint4 kb[STAGES][KS];  // 16-bit pool ring
   VRow vb[STAGES][4];
@@ -332,6 +363,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       }                                                                                              \
     } else {                                                                                         \
       _Pragma("unroll") for (int k = 0; k < KS; ++k) c = mfma16<ST>(kb[SL][k], qb[k], c);           \
+    }                                                                                                \
+    if (alibi) {                                                                                     \
+      /* signed distance of token 4*rg + e to the newest position, times the slope */                \
+      const int d0_ = (TOK0) + 4 * rg - last_pos;                                                    \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) c[e] = fmaf(ab, (float)(d0_ + e), c[e]);        \
     }                                                                                                \
     const int visible = t_end - (TOK0);                                                              \
     if (visible < kBlockTokens) {                                                                    \
@@ -383,31 +419,47 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   } while (0)
 
   // ---- the unit's blocks, TABLE ids at a time -----------------------------------------
-  __syncthreads();  // the previous unit's readers of sm are done
+  // the previous unit read sm.bad before its merge barrier, so it can be cleared here
+  if (tid == 0) sm.bad = 0;
+  lds_barrier();  // the previous unit's readers of sm are done
   for (int cb = b_begin; cb < b_end; cb += TABLE) {
     const int cn = min(TABLE, b_end - cb);  // blocks in this chunk
     if (cb != b_begin) __syncthreads();     // every wave has read the previous chunk's ids
     // this wave: chunk blocks w, w + NW, ...
     const int nwc = __builtin_amdgcn_readfirstlane(w < cn ? (cn - w + NW - 1) / NW : 0);
-    // The wave's first block is read from the table directly and its loads issued
-    // before the workgroup's staging of the chunk's ids completes, so the first K/V
-    // bytes are on their way one table round trip earlier.  An id outside the pool is
-    // replaced by block 0 here; the staged check below then discards the unit.
-    if (nwc > 0) {
-      const int id0 = __builtin_amdgcn_readfirstlane(table[cb + w]);
+    // the chunk's ids, kStage per thread, requested before anything else of the chunk
+    constexpr int kStage = (TABLE + kThreads - 1) / kThreads;
+    int staged[kStage];
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) {
+      const int i = tid + r * kThreads;
+      staged[r] = i < cn ? table[cb + i] : 0;
+    }
+    // The wave's first block is read from the table directly (scalar cache) and its
+    // loads issued before the workgroup's staging of the chunk's ids completes, so the
+    // first K/V bytes are on their way one table round trip earlier.  An id outside the
+    // pool is replaced by block 0 here; the staged check below then discards the unit.
+    // (issued by every wave, so that the wait for the staged ids below is exact; a wave
+    // with no block in the chunk fetches the chunk's last one and never reads it)
+    {
+      const int id0 = uniform_load(table, cb + min(w, cn - 1));
       PC_LOAD(0, (id0 >= 0 && (int64_t)id0 < a.num_blocks) ? id0 : 0);
     }
-    int anybad = 0;
-    for (int i = tid; i < cn; i += kThreads) {
-      const int v = table[cb + i];
-      sm.ids[i] = v;
-      anybad |= v < 0 || (int64_t)v >= a.num_blocks;
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) {
+      const int i = tid + r * kThreads;
+      if (i < cn) {
+        sm.ids[i] = staged[r];
+        if (staged[r] < 0 || (int64_t)staged[r] >= a.num_blocks) sm.bad = 1;
+      }
     }
-    if (__syncthreads_or(anybad)) {
+    lds_barrier();
+    if (__builtin_amdgcn_readfirstlane(sm.bad)) {
       bad = true;  // a block id outside the pool: nothing more is read, the outputs become NaN
       break;
     }
     if (nwc == 0) continue;
+    if (alibi) ab = slope * kLog2e / cs;
     auto id_of = [&](int j) -> int { return sm.ids[w + min(j, nwc - 1) * NW]; };
 #pragma unroll
     for (int st = 1; st < STAGES - 1; ++st) PC_LOAD(st, __builtin_amdgcn_readfirstlane(id_of(st)));
@@ -499,7 +551,7 @@ void decode_split_kernel(DecodeArgs a) {
   id /= a.num_kv_heads;
   const int s = (int)(id % a.num_seqs);
   const int part = (int)(id / a.num_seqs);
-  const int L = a.seq_lens[s];
+  const int L = uniform_load(a.seq_lens, s);
   const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
                    (int64_t)L > (int64_t)a.max_partitions * kPartition;
   if (!bad && part * kPartition >= L) return;  // a partition past the sequence writes nothing

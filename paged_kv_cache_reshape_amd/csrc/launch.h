@@ -40,6 +40,8 @@ struct DecodeArgs {
   float* tmp_out;
   // 8-bit (OCP E4M3) pool: codes times k_scale / v_scale of the kv head
   int kv8;
+  // ALiBi: score of token t for query head h gains alibi_slopes[h] * (t - (L - 1)); NULL: none
+  const float* alibi_slopes;
   const float* k_scale;
   const float* v_scale;
   int64_t scale_stride;

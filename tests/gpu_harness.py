@@ -108,6 +108,8 @@ class DecodeInputs:
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(sl, dtype=np.int32)).cuda()
         self.block_tables = torch.from_numpy(np.ascontiguousarray(bt, dtype=np.int32)).cuda()
         self.max_seq_len = int(self.seq_lens_host.max()) if len(self.seq_lens_host) else 0
+        al = getattr(wl, "alibi_slopes", None)
+        self.alibi = None if al is None else torch.from_numpy(np.ascontiguousarray(al, np.float32)).cuda()
 
 
 def decode(pool: DevicePool, inp: DecodeInputs, path: str = "plan", max_seq_len: int | None = None):
@@ -130,7 +132,8 @@ def decode(pool: DevicePool, inp: DecodeInputs, path: str = "plan", max_seq_len:
 def decode_call(pool: DevicePool, inp: DecodeInputs, out, msl: int, **kw):
     """One pc_paged_attention_decode(_fp8) call on the pool (``kw``: split-path partials)."""
     wl = pool.wl
-    common = dict(num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pool.layout_kwargs(), **kw)
+    common = dict(num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), alibi_slopes=inp.alibi,
+                  **pool.layout_kwargs(), **kw)
     if pool.fp8:
         pc.paged_attention_decode_fp8(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl, pool.k_scale,
                                       pool.v_scale, **pool.scale_kwargs(), **common)

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert pc.abi_version() == 2
+    assert pc.abi_version() == 3
     assert pc.status_string(0) == "ok"
     assert "invalid" in pc.status_string(-1)
     assert "unsupported" in pc.status_string(-2)
@@ -51,12 +51,12 @@ def test_version_and_status_strings(lib):
 def _decode(lib, **kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=100, bs=8 * 16 * 128, ts=128, hs=16 * 128, bt=FAKE, W=128,
              sl=FAKE, S=4, msl=2048, Hq=32, Hkv=8, D=128, B=16, scale=0.088, ps=0, es=None, ml=None, tmp=None,
-             dt=2, stream=None)
+             alibi=None, dt=2, stream=None)
     a.update(kw)
     return lib.pc_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"],
                                          a["bt"], a["W"], a["sl"], a["S"], a["msl"], a["Hq"], a["Hkv"], a["D"],
-                                         a["B"], a["scale"], a["ps"], a["es"], a["ml"], a["tmp"], a["dt"],
-                                         a["stream"])
+                                         a["B"], a["scale"], a["ps"], a["es"], a["ml"], a["tmp"], a["alibi"],
+                                         a["dt"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -105,12 +105,12 @@ def test_write_validation(lib):
 def _decode_fp8(lib, **kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=100, bs=8 * 16 * 128, ts=128, hs=16 * 128, bt=FAKE, W=128,
              sl=FAKE, S=4, msl=2048, Hq=32, Hkv=8, D=128, B=16, scale=0.088, ps=0, es=None, ml=None, tmp=None,
-             ksc=FAKE, vsc=FAKE, sst=1, dt=2, stream=None)
+             alibi=None, ksc=FAKE, vsc=FAKE, sst=1, dt=2, stream=None)
     a.update(kw)
     return lib.pc_paged_attention_decode_fp8(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"],
                                              a["bt"], a["W"], a["sl"], a["S"], a["msl"], a["Hq"], a["Hkv"], a["D"],
-                                             a["B"], a["scale"], a["ps"], a["es"], a["ml"], a["tmp"], a["ksc"],
-                                             a["vsc"], a["sst"], a["dt"], a["stream"])
+                                             a["B"], a["scale"], a["ps"], a["es"], a["ml"], a["tmp"], a["alibi"],
+                                             a["ksc"], a["vsc"], a["sst"], a["dt"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
