@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--path", choices=["plan", "single", "split"], default="plan")
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="cache element type: the query's type, or OCP E4M3 codes with per-kv-head scales")
+    ap.add_argument("--alibi", action="store_true", help="add the ALiBi bias (geometric slopes, one per query head)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -127,7 +128,7 @@ def main():
 
     import gpu_harness as gh
     import paged_kv_cache_reshape_amd as pc
-    from workloads import fp8_variant, make_config
+    from workloads import alibi_variant, fp8_variant, make_config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -136,6 +137,8 @@ def main():
     wl = make_config(args.config)
     if args.kv == "fp8":
         wl = fp8_variant(wl)
+    if args.alibi:
+        wl = alibi_variant(wl)
     S, Hq, D = wl.q.shape
     per_copy = (2 if wl.layout != "combined" else 1) * wl.pool_elems * wl.kv_esize
     copies = args.copies or max(1, min(8, -(-(1 << 30) // max(1, wl.kv_bytes())) + 1))
@@ -179,12 +182,12 @@ def main():
         if fp8:
             pc.paged_attention_decode_fp8(o, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
                                           pool.k_scale, pool.v_scale, num_kv_heads=wl.num_kv_heads,
-                                          scale=float(wl.scale), **pool.layout_kwargs(), **pool.scale_kwargs(),
-                                          **split_kw)
+                                          scale=float(wl.scale), alibi_slopes=inp.alibi, **pool.layout_kwargs(),
+                                          **pool.scale_kwargs(), **split_kw)
         else:
             pc.paged_attention_decode(o, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
-                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pool.layout_kwargs(),
-                                      **split_kw)
+                                      num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), alibi_slopes=inp.alibi,
+                                      **pool.layout_kwargs(), **split_kw)
 
     def step(i, ev=None):
         pool = pools[i % copies]
@@ -268,6 +271,7 @@ def main():
         "config": {"workload": wl.name, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads,
                    "head_size": D, "block_size": wl.block_size, "layout": wl.layout, "path": path,
                    "kv_cache": "fp8_e4m3 (per-kv-head scales)" if fp8 else wl.dtype,
+                   "alibi": bool(args.alibi),
                    "max_seq_len": msl, "kv_bytes_per_step": wl.kv_bytes(), "effective_bytes_per_step": eff,
                    "pool_copies": copies},
         "tokens_per_s": round(S / (ms * 1e-3), 1),
