@@ -59,6 +59,9 @@ def _bind(lib):
     lib.oracle_partials.restype = i32
     lib.oracle_partials.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32,
                                     i32, i32, f32, vp, i32, i32, i32, i32]
+    lib.oracle_varlen.restype = i32
+    lib.oracle_varlen.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i32, vp, vp, i32, i64, i32, i32, i32,
+                                  i32, f32, i32, vp, i32, i32]
     lib.oracle_merge.restype = i32
     lib.oracle_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32]
     lib.oracle_write_kv8.restype = i32
@@ -278,6 +281,27 @@ def partials(wl, pool: Pool, partition_size: int, max_partitions: int | None = N
                              _ptr(al), partition_size, max_partitions, _FMT[wl.dtype], _nthreads(nthreads))
     _check(rc, "oracle_partials")
     return tmp, ml, es
+
+
+def varlen(wl, pool: Pool, vq, q=None, causal=None, alibi_slopes=None, seq_lens=None, query_start_loc=None,
+           nthreads: int | None = None) -> np.ndarray:
+    """fp64 attention of the packed multi-token queries of ``vq`` (a VarlenStep) over
+    the pool, [total_q, Hq, D]."""
+    lib = load()
+    q = np.ascontiguousarray(vq.q if q is None else q)
+    qs = np.ascontiguousarray(vq.query_start_loc if query_start_loc is None else query_start_loc, dtype=np.int32)
+    sl = np.ascontiguousarray(wl.seq_lens if seq_lens is None else seq_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(wl.block_tables, dtype=np.int32)
+    al = _slopes(wl, alibi_slopes)
+    total = int(qs[-1])
+    out = np.zeros((total, wl.num_q_heads, wl.head_size), dtype=np.float64)
+    rc = lib.oracle_varlen(_ptr(out), _ptr(q), pool.k_ptr(), pool.v_ptr(), pool.bound, wl.num_blocks,
+                           wl.block_stride, wl.token_stride, wl.head_stride, _ptr(bt), int(bt.shape[1]), _ptr(qs),
+                           _ptr(sl), int(sl.shape[0]), total, wl.num_q_heads, wl.num_kv_heads, wl.head_size,
+                           wl.block_size, float(wl.scale), int(vq.causal if causal is None else causal), _ptr(al),
+                           _FMT[wl.dtype], _nthreads(nthreads))
+    _check(rc, "oracle_varlen")
+    return out
 
 
 def merge(tmp_out: np.ndarray, max_logits: np.ndarray, exp_sums: np.ndarray, seq_lens,

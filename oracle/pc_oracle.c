@@ -45,6 +45,17 @@
  *                    output o_p; the merge forms M = max m_p, w_p = l_p e^(m_p - M),
  *                    out = sum w_p o_p / sum w_p.
  *
+ *  oracle_varlen  -- several query tokens per request over the paged history
+ *                    ("Inside vLLM CUDA Kernels", Part 3, "How Metadata Connects a
+ *                    Q Tile to Paged K/V": query_start_loc delimits each request's
+ *                    rows of the packed query, seq_lens its visible KV length,
+ *                    block_table its pages).  Request r owns packed rows
+ *                    [qs[r], qs[r+1]), n = qs[r+1] - qs[r] <= L_r of them; these are
+ *                    the request's newest tokens, so token i sits at position
+ *                    p = L_r - n + i.  Causal: it attends positions t <= p; else all
+ *                    of [0, L_r).  Scores, softmax and ALiBi as for the decode, the
+ *                    bias measured from p.  With n = 1 this is the decode.
+ *
  *  oracle_write_kv8, oracle_decode_kv8, oracle_partials_kv8 -- the same with an
  *                    8-bit floating-point cache ("Inside vLLM CUDA Kernels", Part 2,
  *                    "Why Layout and Quantization Scale Produce Two Copy Paths":
@@ -239,6 +250,8 @@ typedef struct {
     const float *k_scale, *v_scale;  /* E4M3 pool: head kv uses scale[kv * scale_stride] */
     int64_t scale_stride;
     int partition_size; /* 0: whole sequence (decode); > 0: partials */
+    const int32_t *query_start_loc;  /* varlen: [num_seqs + 1] row ranges of the packed q */
+    int varlen, causal;
     int max_partitions;
     /* outputs */
     double *out;                                  /* decode: [S, Hq, D] */
@@ -313,8 +326,45 @@ static void dense_attention(const double *qv, const double *K, const double *V, 
     *l_out = l;
 }
 
+/* Varlen work item = one (packed query row, head). */
+static int run_varlen_item(job_t *j, int64_t item, double *K, double *V, double *x, double *qv) {
+    int D = j->head_size;
+    int G = j->num_q_heads / j->num_kv_heads;
+    int h = (int)(item % j->num_q_heads);
+    int64_t row = item / j->num_q_heads;
+    const int32_t *qs = j->query_start_loc;
+    int lo = 0, hi = j->num_seqs - 1; /* the request r with qs[r] <= row < qs[r + 1] */
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (qs[mid] <= row)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int r = lo;
+    int n = qs[r + 1] - qs[r];
+    int i = (int)(row - qs[r]);
+    int L = j->seq_lens[r];
+    if (L < n || (int64_t)L > (int64_t)j->max_blocks_per_seq * j->block_size)
+        return OR_ERANGE;
+    int p = L - n + i; /* position of this query token */
+    int visible = j->causal ? p + 1 : L;
+    for (int d = 0; d < D; ++d)
+        qv[d] = load_elem(j->q, (row * j->num_q_heads + h) * D + d, j->fmt);
+    int rc = gather_rows(j, r, h / G, 0, visible, K, V);
+    if (rc)
+        return rc;
+    double slope = j->alibi_slopes ? (double)j->alibi_slopes[h] : 0.0;
+    double m, l;
+    dense_attention(qv, K, V, visible, D, j->scale, slope, -(int64_t)p, x, j->out + (row * j->num_q_heads + h) * D,
+                    &m, &l);
+    return OR_OK;
+}
+
 /* One work item = one (s, h) for decode, one (s, h, p) for partials. */
 static int run_item(job_t *j, int64_t item, double *K, double *V, double *x, double *qv) {
+    if (j->varlen)
+        return run_varlen_item(j, item, K, V, x, qv);
     int D = j->head_size;
     int G = j->num_q_heads / j->num_kv_heads;
     int s, h, p = 0;
@@ -569,6 +619,53 @@ int oracle_merge(double *out, const double *tmp_out, const double *max_logits, c
 }
 
 /* The decode and the partials over an E4M3 pool (q, out in fmt). */
+int oracle_varlen(double *out, const void *q, const void *k_pool, const void *v_pool, int64_t pool_elems,
+                  int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                  const int32_t *block_tables, int max_blocks_per_seq, const int32_t *query_start_loc,
+                  const int32_t *seq_lens, int num_reqs, int64_t total_q, int num_q_heads, int num_kv_heads,
+                  int head_size, int block_size, float scale, int causal, const float *alibi_slopes, int fmt,
+                  int nthreads) {
+    int rc = check_common(q, k_pool, v_pool, block_tables, seq_lens, num_reqs, num_q_heads, num_kv_heads,
+                          head_size, block_size, max_blocks_per_seq, fmt);
+    if (rc)
+        return rc;
+    if (!query_start_loc || total_q < 0 || (total_q > 0 && !out))
+        return OR_EINVAL;
+    if (query_start_loc[0] != 0 || (num_reqs >= 0 && query_start_loc[num_reqs] != total_q))
+        return OR_EINVAL;
+    for (int r = 0; r < num_reqs; ++r)
+        if (query_start_loc[r + 1] < query_start_loc[r])
+            return OR_EINVAL;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.q = q;
+    j.k_pool = k_pool;
+    j.v_pool = v_pool;
+    j.pool_elems = pool_elems;
+    j.num_blocks = num_blocks;
+    j.block_stride = block_stride;
+    j.token_stride = token_stride;
+    j.head_stride = head_stride;
+    j.block_tables = block_tables;
+    j.max_blocks_per_seq = max_blocks_per_seq;
+    j.seq_lens = seq_lens;
+    j.num_seqs = num_reqs;
+    j.num_q_heads = num_q_heads;
+    j.num_kv_heads = num_kv_heads;
+    j.head_size = head_size;
+    j.block_size = block_size;
+    j.scale = (double)scale;
+    j.alibi_slopes = alibi_slopes;
+    j.fmt = fmt;
+    j.kv_fmt = fmt;
+    j.out = out;
+    j.query_start_loc = query_start_loc;
+    j.varlen = 1;
+    j.causal = causal != 0;
+    j.n_items = total_q * num_q_heads;
+    return run_job(&j, nthreads);
+}
+
 int oracle_decode_kv8(double *out, const void *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t pool_elems,
                       int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
                       const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens, int num_seqs,

@@ -12,7 +12,10 @@ the oracle disagrees with something it does not compute itself:
 * for the 8-bit cache: the OCP E4M3 landmarks and torch's float8_e4m3fn converter,
   and dense attention on dequantised rows;
 * for ALiBi: zero slopes change nothing, torch's attention with the bias as an
-  additive mask, the geometric weights of q = 0, and the partials' maxima.
+  additive mask, the geometric weights of q = 0, and the partials' maxima;
+* for multi-token (varlen) queries: single tokens reproduce the decode, numpy and
+  torch references with the causal limit written out, prefix means of q = 0, a
+  first token that sees exactly one row, and the non-causal form.
 
 ``tests/test_oracle_pins.py`` runs them; ``tests/test_oracle_mutants.py`` plants
 mistakes in copies of the oracle and requires some pin to fail for each.
@@ -31,7 +34,7 @@ import numpy as np
 import brute
 import oracle
 from helpers import GOLDEN, bits_to_f64, dense_numpy, f64_to_bits, online_tiles_numpy
-from workloads import alibi_variant, custom, fp8_variant, make_config, nan_bits
+from workloads import alibi_variant, custom, fp8_variant, make_config, nan_bits, varlen_variant
 
 B = 16
 
@@ -651,6 +654,106 @@ def pin_alibi_partials():
         assert np.abs(oracle.merge(tmp, ml, es, w.seq_lens, P) - dense).max() < 1e-13, P
 
 
+# ---------------------------------------------------------------------------------
+# multi-token queries ("Inside vLLM CUDA Kernels", Part 3, "How Metadata Connects a Q
+# Tile to Paged K/V"): request r's rows [qs[r], qs[r+1]) are its newest n_r tokens;
+# token i sits at p = L_r - n_r + i and, causally, sees positions t <= p
+# ---------------------------------------------------------------------------------
+
+def _varlen_case(causal=True, alibi=False, dtype="bf16"):
+    w = custom(60, dtype, 8, 2, 64, [1, 5, 16, 17, 40, 300])
+    if alibi:
+        w = alibi_variant(w, np.linspace(0.3, -0.02, 8).astype(np.float32))
+    return w, varlen_variant(w, [1, 5, 3, 17, 1, 33], causal=causal)
+
+
+def _varlen_numpy(w, vq):
+    """Dense attention per packed row from the generator's contiguous history."""
+    q = bits_to_f64(vq.q, w.dtype)
+    G = w.num_q_heads // w.num_kv_heads
+    out = np.zeros(q.shape)
+    qs = vq.query_start_loc
+    for r in range(w.num_seqs):
+        L, n = int(w.seq_lens[r]), int(qs[r + 1] - qs[r])
+        K = bits_to_f64(w.logical_k(r), w.dtype)
+        V = bits_to_f64(w.logical_v(r), w.dtype)
+        for i in range(n):
+            p = L - n + i
+            vis = p + 1 if vq.causal else L
+            for h in range(w.num_q_heads):
+                x = float(w.scale) * (K[:vis, h // G] @ q[qs[r] + i, h])
+                if getattr(w, "alibi_slopes", None) is not None:
+                    x = x + float(w.alibi_slopes[h]) * (np.arange(vis) - p)
+                e = np.exp(x - x.max())
+                out[qs[r] + i, h] = e @ V[:vis, h // G] / e.sum()
+    return out
+
+
+def pin_varlen_single_tokens_are_decode():
+    """One query token per request with the decode's q: bit-identical to the decode."""
+    w = custom(61, "f16", 8, 4, 128, [1, 33, 520])
+    pool = oracle.filled_pool(w)
+    v1 = varlen_variant(w, [1, 1, 1])
+    assert np.array_equal(oracle.varlen(w, pool, v1, q=w.q), oracle.decode(w, pool))
+
+
+def pin_varlen_numpy():
+    """numpy dense attention with the causal limit t <= L - n + i (and without it, and
+    with an ALiBi bias measured from the token's own position) agrees to 1e-12."""
+    for causal, alibi in ((True, False), (False, False), (True, True)):
+        w, vq = _varlen_case(causal, alibi)
+        out = oracle.varlen(w, oracle.filled_pool(w), vq)
+        assert np.abs(out - _varlen_numpy(w, vq)).max() < 1e-12, (causal, alibi)
+
+
+def pin_varlen_torch_sdpa():
+    """torch SDPA in float64 with a boolean mask built from the causal limit."""
+    import torch
+    w, vq = _varlen_case(True, dtype="f32")
+    out = oracle.varlen(w, oracle.filled_pool(w), vq)
+    G = w.num_q_heads // w.num_kv_heads
+    q = torch.from_numpy(bits_to_f64(vq.q, w.dtype))
+    qs = vq.query_start_loc
+    for r in range(w.num_seqs):
+        L, n = int(w.seq_lens[r]), int(qs[r + 1] - qs[r])
+        if n == 0:
+            continue
+        K = torch.from_numpy(bits_to_f64(w.logical_k(r), w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        V = torch.from_numpy(bits_to_f64(w.logical_v(r), w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        allowed = torch.arange(L)[None, :] <= (L - n + torch.arange(n))[:, None]  # [n, L]
+        ref = torch.nn.functional.scaled_dot_product_attention(q[qs[r]:qs[r + 1]].permute(1, 0, 2), K, V,
+                                                               attn_mask=allowed, scale=float(w.scale))
+        assert (ref.permute(1, 0, 2).numpy() - out[qs[r]:qs[r + 1]]).__abs__().max() < 1e-12, r
+
+
+def pin_varlen_prefix_means():
+    """q = 0, causal: token i's output is the plain mean of V over positions 0 .. p."""
+    w, vq = _varlen_case(True, dtype="f32")
+    zq = np.zeros_like(vq.q)
+    out = oracle.varlen(w, oracle.filled_pool(w), vq, q=zq)
+    G = w.num_q_heads // w.num_kv_heads
+    qs = vq.query_start_loc
+    for r in range(w.num_seqs):
+        L, n = int(w.seq_lens[r]), int(qs[r + 1] - qs[r])
+        V = bits_to_f64(w.logical_v(r), w.dtype)
+        for i in range(n):
+            p = L - n + i
+            for h in range(w.num_q_heads):
+                assert np.abs(out[qs[r] + i, h] - V[:p + 1, h // G].mean(axis=0)).max() < 1e-12, (r, i, h)
+
+
+def pin_varlen_first_token_sees_one_row():
+    """A request whose query covers its whole history (n = L): its first token sees only
+    position 0, so its output is that V row exactly, in every format."""
+    for dtype in ("f32", "f16", "bf16"):
+        w = custom(62, dtype, 4, 2, 64, [9, 20])
+        vq = varlen_variant(w, [9, 20])
+        out = oracle.varlen(w, oracle.filled_pool(w), vq)
+        for r, row in ((0, 0), (1, 9)):
+            V0 = bits_to_f64(w.logical_v(r)[0], dtype)  # [Hkv, D]
+            assert np.array_equal(out[row], np.repeat(V0, 2, axis=0)), (dtype, r)
+
+
 PINS = [
     pin_slot_write, pin_slot_read, pin_invariant_line, pin_gqa_mapping, pin_worked_decode,
     pin_combined_block_layout, pin_one_token_exact, pin_special_values_exact, pin_zero_query_mean,
@@ -658,5 +761,6 @@ PINS = [
     pin_negative_slot_skipped, pin_unread_memory, pin_table_padding, pin_write_out_of_range,
     pin_numpy_dense, pin_torch_sdpa, pin_online_tiles, pin_brute_force, pin_split_identity,
     pin_e4m3_values, pin_e4m3_rounding, pin_kv8_write, pin_kv8_decode, pin_alibi_zero_slopes,
-    pin_alibi_torch_sdpa, pin_alibi_geometric_weights, pin_alibi_partials,
+    pin_alibi_torch_sdpa, pin_alibi_geometric_weights, pin_alibi_partials, pin_varlen_single_tokens_are_decode,
+    pin_varlen_numpy, pin_varlen_torch_sdpa, pin_varlen_prefix_means, pin_varlen_first_token_sees_one_row,
 ]

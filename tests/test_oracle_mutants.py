@@ -50,9 +50,16 @@ MUTANTS = {
     "kv8_read_v_scale_from_k": ("vs = (double)j->v_scale[(int64_t)kv * j->scale_stride];",
                                 "vs = (double)j->k_scale[(int64_t)kv * j->scale_stride];"),
     "alibi_sign_flipped": ("+ slope * (double)(pos0 + t);", "- slope * (double)(pos0 + t);"),
-    "alibi_slope_of_kv_head": ("j->alibi_slopes[h]", "j->alibi_slopes[kv]"),
+    "alibi_slope_of_kv_head": ("int kv = h / G;\n    double slope = j->alibi_slopes ? (double)j->alibi_slopes[h]",
+                               "int kv = h / G;\n    double slope = j->alibi_slopes ? (double)j->alibi_slopes[kv]"),
+    "varlen_alibi_slope_of_kv_head": ("(double)j->alibi_slopes[h] : 0.0;\n    double m, l;",
+                                      "(double)j->alibi_slopes[h / G] : 0.0;\n    double m, l;"),
     "alibi_partition_origin": ("(int64_t)t0 - (L - 1)", "-(int64_t)(L - 1)"),
     "alibi_partials_off_by_one": ("(int64_t)t0 - (L - 1)", "(int64_t)t0 - L"),
+    "varlen_causal_off_by_one": ("int visible = j->causal ? p + 1 : L;", "int visible = j->causal ? p : L;"),
+    "varlen_top_left_causal": ("int visible = j->causal ? p + 1 : L;", "int visible = j->causal ? i + 1 : L;"),
+    "varlen_causal_ignored": ("int visible = j->causal ? p + 1 : L;", "int visible = L;"),
+    "varlen_request_lookup": ("if (qs[mid] <= row)", "if (qs[mid] < row)"),
 }
 
 

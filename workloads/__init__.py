@@ -10,6 +10,7 @@ GPU path consume what it produces.
 from .gen import (  # noqa: F401
     BLOCK_SIZE,
     CONFIG_NAMES,
+    VarlenStep,
     Workload,
     alibi_variant,
     custom,
@@ -17,4 +18,5 @@ from .gen import (  # noqa: F401
     fp8_variant,
     make_config,
     nan_bits,
+    varlen_variant,
 )

@@ -512,3 +512,50 @@ def alibi_variant(wl: Workload, slopes=None) -> Workload:
     if slopes.shape != (H,):
         raise ValueError("one slope per query head")
     return replace(wl, name=wl.name + "_alibi", alibi_slopes=slopes)
+
+
+@dataclass
+class VarlenStep:
+    """Several query tokens per request (chunked prefill, speculative decode) over a
+    workload's history.  Request r owns rows [query_start_loc[r], query_start_loc[r+1])
+    of the packed query; they are its newest n_r tokens (positions L_r - n_r .. L_r - 1),
+    whose K/V rows the step writes first (``key``/``value`` through ``slot_mapping``)."""
+    q: np.ndarray = field(repr=False)                  # bits [total_q, Hq, D]
+    query_start_loc: np.ndarray = field(repr=False)    # int32 [R + 1]
+    query_lens: np.ndarray = field(repr=False)         # int32 [R]
+    key: np.ndarray = field(repr=False)                # bits [total_q, Hkv, D]
+    value: np.ndarray = field(repr=False)
+    slot_mapping: np.ndarray = field(repr=False)       # int64 [total_q]
+    causal: bool = True
+
+    @property
+    def total_q(self) -> int:
+        return int(self.query_start_loc[-1])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if len(self.query_lens) else 0
+
+
+def varlen_variant(wl: Workload, query_lens, causal: bool = True) -> VarlenStep:
+    """Queries of ``query_lens[r]`` (<= seq_lens[r]) tokens per request of ``wl``.  The
+    packed q is drawn from stream 6; the step's K/V rows are the requests' own newest
+    logical rows, so writing them leaves the pool unchanged."""
+    n = np.asarray(query_lens, dtype=np.int32)
+    if n.shape != (wl.num_seqs,) or (n < 0).any() or (n > wl.seq_lens).any():
+        raise ValueError("one query length per request, 0 <= n_r <= seq_len_r")
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    total = int(qs[-1])
+    q = _normal_bits(wl.seed, 6, (total, wl.num_q_heads, wl.head_size), wl.dtype)
+    keys, values, slots = [], [], []
+    B = wl.block_size
+    for r in range(wl.num_seqs):
+        L, k = int(wl.seq_lens[r]), int(n[r])
+        pos = np.arange(L - k, L, dtype=np.int64)
+        keys.append(wl.logical_k(r)[L - k:L])
+        values.append(wl.logical_v(r)[L - k:L])
+        slots.append(wl.block_tables[r, pos // B].astype(np.int64) * B + pos % B)
+    shape = (0, wl.num_kv_heads, wl.head_size)
+    cat = lambda xs: np.concatenate(xs) if xs else np.zeros(shape, _BITS_NP[wl.dtype])
+    return VarlenStep(q=q, query_start_loc=qs, query_lens=n, key=cat(keys), value=cat(values),
+                      slot_mapping=np.concatenate(slots) if slots else np.zeros(0, np.int64), causal=causal)
