@@ -11,7 +11,9 @@
  *                              softmax . V -- either in one pass, or per 512-token
  *                              partition writing partial results;
  *   pc_paged_attention_reduce  merge the partitions' partial results (log-sum-exp);
- *   pc_paged_attention_plan    choose between the one-pass and the split path.
+ *   pc_paged_attention_plan    choose between the one-pass and the split path;
+ *   pc_paged_attention_varlen  several query tokens per request (chunked prefill,
+ *                              speculative decode) over the same paged history.
  *
  * The write and the decode also exist for an 8-bit cache (suffix _fp8): the pool
  * holds OCP E4M3 codes with one dequantisation scale per kv head for K and one
@@ -222,6 +224,42 @@ int pc_paged_attention_decode_fp8(void *out, const void *q, const uint8_t *k_poo
                                   int partition_size, float *exp_sums, float *max_logits, float *tmp_out,
                                   const float *alibi_slopes, const float *k_scale, const float *v_scale,
                                   int64_t kv_scale_stride, int dtype, void *stream);
+
+/*
+ * pc_paged_attention_varlen -- attention of several new query tokens per request
+ * over the paged history.
+ *
+ * Defined by "Inside vLLM CUDA Kernels", Part 3, sections "How Metadata Connects a Q
+ * Tile to Paged K/V" (query_start_loc delimits each request's rows of the packed
+ * query, seq_lens its visible KV length, block_table its pages; the kernel resolves
+ * pages as it scans the K dimension) and "How Each K/V Tile Contributes to the
+ * Output" (online softmax over the K/V tiles).  Request r owns rows
+ * [query_start_loc[r], query_start_loc[r+1]) of q and out: its newest n_r tokens,
+ * whose K/V must already be in the cache, so query token i sits at position
+ * p = seq_lens[r] - n_r + i.  causal = 1: it attends positions t <= p; causal = 0:
+ * all of [0, seq_lens[r]).  Scores scale * q.k_t (+ alibi_slopes[h] * (t - p) when
+ * given), softmax, times V, as for the decode; n_r = 1 with causal = 1 is the decode.
+ *
+ *   out, q            device [total_q, num_q_heads, head_size], fp16 or bf16,
+ *                     16-byte aligned (fp32 gives PC_ERR_UNSUPPORTED)
+ *   k_pool ... block_tables, block_size, head_size, groups: as for the decode
+ *   query_start_loc   device int32 [num_reqs + 1], non-decreasing, from 0 to total_q
+ *   seq_lens          device int32 [num_reqs], seq_lens[r] >= n_r
+ *   max_query_len     host upper bound of n_r (sizes the grid; a longer request is
+ *                     still computed, more slowly)
+ *   causal            0 or 1
+ *   alibi_slopes      NULL or device fp32 [num_q_heads]
+ * A request whose row range leaves [0, total_q] or is decreasing has its rows left
+ * unwritten; one with seq_len < n_r, a length past its table row or a block id
+ * outside the pool gets NaN in its rows.
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ */
+int pc_paged_attention_varlen(void *out, const void *q, const void *k_pool, const void *v_pool, int64_t num_blocks,
+                              int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                              const int32_t *block_tables, int max_blocks_per_seq, const int32_t *query_start_loc,
+                              const int32_t *seq_lens, int num_reqs, int64_t total_q, int max_query_len,
+                              int num_q_heads, int num_kv_heads, int head_size, int block_size, float scale,
+                              int causal, const float *alibi_slopes, int dtype, void *stream);
 
 /*
  * pc_paged_attention_reduce -- merge the split path's partials.

@@ -8,7 +8,9 @@ The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
 * ``paged_attention_reduce``   -- log-sum-exp merge of the partials;
 * ``paged_attention_plan``     -- the planner's choice between the two paths;
 * ``reshape_and_cache_fp8`` / ``paged_attention_decode_fp8`` -- the same over an
-  8-bit (OCP E4M3) pool with per-kv-head scales.
+  8-bit (OCP E4M3) pool with per-kv-head scales;
+* ``paged_attention_varlen``   -- several query tokens per request (chunked
+  prefill, speculative decode), causal, over the same pool.
 """
 
 from ._native import (  # noqa: F401
@@ -21,6 +23,7 @@ from ._native import (  # noqa: F401
     paged_attention_decode_fp8,
     paged_attention_plan,
     paged_attention_reduce,
+    paged_attention_varlen,
     reshape_and_cache,
     reshape_and_cache_fp8,
     status_string,

@@ -52,6 +52,9 @@ def _load():
         lib.pc_paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32,
                                                       i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, i64,
                                                       i32, vp]
+        lib.pc_paged_attention_varlen.restype = i32
+        lib.pc_paged_attention_varlen.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, vp, i32, i64, i32,
+                                                  i32, i32, i32, i32, f32, i32, vp, i32, vp]
         lib.pc_paged_attention_reduce.restype = i32
         lib.pc_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.pc_paged_attention_plan.restype = i32
@@ -243,6 +246,39 @@ def paged_attention_decode_fp8(out, q: torch.Tensor, k_pool: torch.Tensor, v_poo
         D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(alibi_slopes),
         _ptr(k_scale), _ptr(v_scale), kv_scale_stride, dt, _stream(q, stream))
     _check("pc_paged_attention_decode_fp8", st)
+
+
+def paged_attention_varlen(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           block_tables: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
+                           max_query_len: int, *, num_kv_heads: int, scale: float, num_blocks: int,
+                           block_stride: int, token_stride: int, head_stride: int, causal: bool = True,
+                           alibi_slopes=None, block_size: int = 16, v_offset: int = 0, stream=None) -> None:
+    """Attention of the packed multi-token queries ``q`` [total_q, Hq, D]: request r owns rows
+    ``query_start_loc[r] .. query_start_loc[r+1]``, its newest tokens (causal by default)."""
+    _same_device(out, q, k_pool, v_pool, block_tables, query_start_loc, seq_lens, alibi_slopes)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [total_q, Hq, D]")
+    if out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous int32 [R, W]")
+    for t, nm in ((query_start_loc, "query_start_loc"), (seq_lens, "seq_lens")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous int32 tensor")
+    R = seq_lens.numel()
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must hold num_reqs + 1 entries")
+    _check_alibi(alibi_slopes, q)
+    dt = _dtype_code(q)
+    if _DTYPES.get(k_pool.dtype) != dt or _DTYPES.get(v_pool.dtype) != dt:
+        raise TypeError("q and the pool must share one storage dtype")
+    T, Hq, D = q.shape
+    st = _load().pc_paged_attention_varlen(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
+        head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(query_start_loc), _ptr(seq_lens), R, T,
+        max_query_len, Hq, num_kv_heads, D, block_size, scale, int(bool(causal)), _ptr(alibi_slopes), dt,
+        _stream(q, stream))
+    _check("pc_paged_attention_varlen", st)
 
 
 def paged_attention_reduce(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kBlockTokens = 16;
 
 int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
@@ -217,6 +217,54 @@ int pc_paged_attention_decode_fp8(void* out, const void* q, const uint8_t* k_poo
                      max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
                      block_size, scale, partition_size, exp_sums, max_logits, tmp_out, alibi_slopes, k_scale,
                      v_scale, kv_scale_stride, dtype, true, stream);
+}
+
+int pc_paged_attention_varlen(void* out, const void* q, const void* k_pool, const void* v_pool, int64_t num_blocks,
+                              int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* query_start_loc,
+                              const int32_t* seq_lens, int num_reqs, int64_t total_q, int max_query_len,
+                              int num_q_heads, int num_kv_heads, int head_size, int block_size, float scale,
+                              int causal, const float* alibi_slopes, int dtype, void* stream) {
+  const int es = esize(dtype);
+  if (!es || num_reqs < 0 || total_q < 0 || max_query_len < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0 ||
+      (causal != 0 && causal != 1))
+    return PC_ERR_INVALID_ARG;
+  if (num_reqs == 0 || total_q == 0) return PC_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !query_start_loc || !seq_lens) return PC_ERR_INVALID_ARG;
+  if (num_blocks <= 0 || block_stride <= 0 || token_stride <= 0 || head_stride <= 0) return PC_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PC_ERR_INVALID_ARG;
+  if (block_size != kBlockTokens || dtype == PC_F32) return PC_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  if ((head_size != 64 && head_size != 128) || (group != 1 && group != 2 && group != 4 && group != 8))
+    return PC_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !strides16(es, {block_stride, token_stride, head_stride, (int64_t)head_size}))
+    return PC_ERR_UNSUPPORTED;
+  if (token_stride > INT_MAX / (kBlockTokens * es)) return PC_ERR_UNSUPPORTED;
+  if (total_q > INT_MAX) return PC_ERR_UNSUPPORTED;
+  pcache::VarlenArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_blocks = num_blocks;
+  a.block_stride = block_stride;
+  a.token_stride = token_stride;
+  a.head_stride = head_stride;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.query_start_loc = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.num_reqs = num_reqs;
+  a.total_q = total_q;
+  a.max_query_len = max_query_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal;
+  a.alibi_slopes = alibi_slopes;
+  return status_of(pcache::launch_varlen(a, dtype, head_size, static_cast<hipStream_t>(stream)));
 }
 
 int pc_paged_attention_reduce(void* out, const float* exp_sums, const float* max_logits, const float* tmp_out,

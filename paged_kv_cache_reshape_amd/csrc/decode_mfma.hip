@@ -60,6 +60,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "mfma_common.h"
 
 namespace pcache {
 namespace {
@@ -68,7 +69,6 @@ constexpr int kBlockTokens = 16;
 constexpr int kPartition = 512;
 constexpr float kLazy = 8.f;            // log2-domain slack before the exponent reference moves
 constexpr int kMaxRankedSeqs = 512;     // sequences ranked by length in-kernel (beyond: index order)
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, dword 3 for gfx9-family parts
 
 // One-pass workgroup: one per CU, as many waves as the register allocation lets a
 // CU hold (3 per SIMD at head_size 128, 4 at 64), so the persistent grid fills the
@@ -110,112 +110,6 @@ constexpr int onepass_waves() {
 #define PCACHE_SPLIT_STAGES_KV8 2
 #endif
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <class ST>
-__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c);
-template <>
-__device__ __forceinline__ f32x4_t mfma16<BF16>(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-template <>
-__device__ __forceinline__ f32x4_t mfma16<F16>(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
-                                                0, 0);
-}
-
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-
-// out^T tile += V^T tile . P^T tile (K = 16 tokens)
-template <class ST>
-__device__ __forceinline__ f32x4_t mfma_pv(const uint2& v, const uint2& p, f32x4_t c);
-template <>
-__device__ __forceinline__ f32x4_t mfma_pv<BF16>(const uint2& v, const uint2& p, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v), __builtin_bit_cast(bf16x4_t, p),
-                                                   c, 0, 0, 0);
-}
-template <>
-__device__ __forceinline__ f32x4_t mfma_pv<F16>(const uint2& v, const uint2& p, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, v), __builtin_bit_cast(f16x4_t, p), c, 0, 0,
-                                               0);
-}
-
-// two floats rounded to nearest-even into one dword of the storage type
-template <class ST>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi);
-template <>
-__device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
-  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-  const bf16x2_v v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-template <>
-__device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
-  typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
-  const f16x2_v v = {(_Float16)lo, (_Float16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// four E4M3 codes (one dword) widened exactly to two dwords of the 16-bit type
-template <class ST>
-__device__ __forceinline__ uint2 widen4(uint32_t codes);
-template <>
-__device__ __forceinline__ uint2 widen4<BF16>(uint32_t codes) {
-  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true)));
-}
-template <>
-__device__ __forceinline__ uint2 widen4<F16>(uint32_t codes) {
-  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, true)));
-}
-
-// a lane's slice of one V row: 8 (head_size 128) or 4 (64) 16-bit values
-template <int N>
-struct VRowOf;
-template <>
-struct VRowOf<8> {
-  using type = uint4;
-};
-template <>
-struct VRowOf<4> {
-  using type = uint2;
-};
-__device__ __forceinline__ uint32_t vword(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
-__device__ __forceinline__ uint32_t vword(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
-
-// the same slice as E4M3 codes: 8 bytes (head_size 128) or 4 (64)
-template <int N>
-struct VRow8Of;
-template <>
-struct VRow8Of<8> {
-  using type = uint2;
-};
-template <>
-struct VRow8Of<4> {
-  using type = uint32_t;
-};
-__device__ __forceinline__ uint32_t vword(uint32_t v, int) { return v; }
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Wave-uniform reads of data the kernel never writes (lengths, block tables, slopes),
-// through the scalar data cache: they count on their own counter, so waiting for one
-// does not also wait for the vector loads issued before it.
-template <class T>
-__device__ __forceinline__ T uniform_load(const T* p, int64_t i) {
-  typedef const __attribute__((address_space(4))) T cT;
-  return ((cT*)p)[i];
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
 template <int NW, int D, int G, int TABLE>
 struct UnitLds {
   __align__(16) float acc[NW][G][D];  // each wave's scaled accumulator
@@ -225,13 +119,6 @@ struct UnitLds {
   int bad;         // some id of the unit lies outside the pool
 };
 
-// Barrier that orders LDS only: vector loads in flight stay in flight across it
-// (__syncthreads() also waits for every outstanding global access of the wave).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // One unit: kv head `kvh` of sequence `s`, tokens [t_begin, t_end).  All waves of
 // the workgroup call it together (it uses block-wide barriers).  Writes out (one

@@ -47,6 +47,25 @@ struct DecodeArgs {
   int64_t scale_stride;
 };
 
+struct VarlenArgs {
+  void* out;
+  const void* q;  // [total_q, num_q_heads, head_size]
+  const void* k_pool;
+  const void* v_pool;
+  int64_t num_blocks, block_stride, token_stride, head_stride;  // elements
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* query_start_loc;  // [num_reqs + 1]
+  const int32_t* seq_lens;         // [num_reqs]
+  int num_reqs;
+  int64_t total_q;
+  int max_query_len;  // sizes the grid; longer requests are still covered
+  int num_q_heads, num_kv_heads;
+  float scale_log2;
+  int causal;
+  const float* alibi_slopes;
+};
+
 struct ReduceArgs {
   void* out;
   const float* exp_sums;
@@ -65,6 +84,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool spl
 // 16-bit storage: q.k on the matrix cores (decode_mfma.hip).
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, hipStream_t stream);
+// Multi-token queries (varlen.hip); 16-bit storage only.
+hipError_t launch_varlen(const VarlenArgs& a, int dtype, int head_size, hipStream_t stream);
 bool decode_supported(int dtype, int head_size, int group);
 bool reduce_supported(int head_size);
 // Compute units of the current device (cached per device; 256, MI355X's count, when

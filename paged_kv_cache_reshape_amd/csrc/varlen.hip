@@ -1,0 +1,335 @@
+// varlen.hip -- attention of several query tokens per request over the paged K/V
+// (chunked prefill, speculative decode), 16-bit storage, on the matrix cores.
+//
+// What is computed ("Inside vLLM CUDA Kernels", Part 3, "How Metadata Connects a Q
+// Tile to Paged K/V" and "How Each K/V Tile Contributes to the Output"): request r
+// owns rows [qs[r], qs[r+1]) of the packed query -- its newest n = qs[r+1] - qs[r]
+// tokens, so query token i sits at position p = L_r - n + i.  Causally it attends
+// positions t <= p, otherwise all of [0, L_r); scores scale * q.k (plus an optional
+// ALiBi bias slope_h * (t - p)), softmax, times V.  With n = 1 this is the decode.
+//
+// gfx950 mapping.  A work unit is (request, kv head, chunk of QT query tokens).  The
+// unit's QC = 16 * NQ (query token, head) pairs are the columns of NQ score tiles
+// computed exactly as the decode's single tile: v_mfma_f32_16x16x32 with A = a
+// 16-token K block and B = the query columns, then a lazy online softmax per column
+// and out^T += V^T . P^T on v_mfma_f32_16x16x16, the V^T operand of each output tile
+// shared by the NQ column tiles.  So each K/V block read from HBM or L2 serves QC
+// query rows.  The unit's visible blocks are dealt to the workgroup's waves
+// round-robin, each with its own softmax state per column; the states meet once, in
+// LDS, at the end.  Causality is a per-column limit applied to the scores; rows past
+// the unit's last visible position are zeroed in V (they may be stale).
+#include <cmath>
+
+#include "device_common.h"
+#include "launch.h"
+#include "mfma_common.h"
+
+namespace pcache {
+namespace {
+
+constexpr int kTok = 16;          // tokens per score tile row block (the block size)
+constexpr int kWaves = 4;         // waves per unit
+constexpr int kTable = 512;       // block ids staged in LDS at once
+constexpr float kLazyV = 8.f;     // log2-domain slack before a column's exponent reference moves
+
+template <int QC, int D>
+struct VarlenLds {
+  __align__(16) float acc[kWaves][QC][D];
+  float mw[kWaves][QC];
+  float lw[kWaves][QC];
+  int ids[kTable];
+  int bad;
+};
+
+template <class ST, int D, int G, int NQ>
+__global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2))) void varlen_kernel(VarlenArgs a) {
+  static_assert(ST::kBytes == 2, "16-bit storage only");
+  constexpr int QC = 16 * NQ;  // (query token, head) columns per unit
+  constexpr int QT = QC / G;   // query tokens per unit
+  constexpr int KS = D / 32;   // q.k k-steps per block
+  constexpr int DPL = D / 16;  // V dims a lane loads per row = output tiles
+  constexpr int NT = DPL;
+  constexpr int kThreads = kWaves * kWave;
+  constexpr int kStage = (kTable + kThreads - 1) / kThreads;
+  using VRow = typename VRowOf<DPL>::type;
+  __shared__ VarlenLds<QC, D> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int rg = lane >> 4;
+  const int col = lane & 15;
+
+  int64_t unit = blockIdx.x;
+  const int kvh = (int)(unit % a.num_kv_heads);
+  unit /= a.num_kv_heads;
+  const int r = (int)(unit % a.num_reqs);
+  const int chunk0 = (int)(unit / a.num_reqs);
+  const int chunks = (int)(gridDim.x / ((int64_t)a.num_kv_heads * a.num_reqs));
+
+  const int q0 = uniform_load(a.query_start_loc, r);
+  const int q1 = uniform_load(a.query_start_loc, r + 1);
+  if (q0 < 0 || q1 < q0 || (int64_t)q1 > a.total_q) return;  // no rows this request may write
+  const int n = q1 - q0;
+  const int L = uniform_load(a.seq_lens, r);
+  const bool bad_len = L < n || (int64_t)L > (int64_t)a.max_blocks_per_seq * kTok;
+  const int h0 = kvh * G;
+  const float cs = a.scale_log2;
+  const float lazy_raw = kLazyV / cs;
+  const bool alibi = a.alibi_slopes != nullptr;
+  const int32_t* table = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
+  const int64_t head_bytes = (int64_t)kvh * a.head_stride * 2;
+  const char* kpool = static_cast<const char*>(a.k_pool) + head_bytes;
+  const char* vpool = static_cast<const char*>(a.v_pool) + head_bytes;
+  const int64_t block_bytes = a.block_stride * 2;
+  const int tok_bytes = (int)(a.token_stride * 2);
+  const uint32_t tile_bytes = (uint32_t)(kTok * tok_bytes);
+  const int k_off = col * tok_bytes + 16 * rg;
+  const int v_off = 4 * rg * tok_bytes + col * (2 * DPL);
+
+  for (int c = chunk0; c * QT < n; c += chunks) {
+    const int i0 = c * QT;                   // first query token of the unit
+    const int i_end = min(n, i0 + QT);       // one past its last
+    // positions this unit may see: up to its last token's (causal) or the whole history
+    const int vis_end = bad_len ? 0 : (a.causal ? L - n + i_end : L);
+    bool bad = bad_len;
+
+    // column 16*q + col of this lane: query token i0 + (16q + col) / G, head (16q + col) % G
+    uint4 qb[NQ][KS];
+    int lim[NQ];    // last visible position of the column (-1: no such column)
+    int pos[NQ];    // position of the column's query token
+    float ab[NQ];   // ALiBi slope in raw q.k units
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int cc = 16 * q + col;
+      const int ti = i0 + cc / G;
+      const bool valid = ti < i_end;
+      const int g = cc % G;
+      pos[q] = L - n + ti;
+      lim[q] = valid ? (a.causal ? pos[q] : L - 1) : -1;
+      const int tq = valid ? ti : i_end - 1;  // keeps the address inside q
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + tq) * a.num_q_heads + h0 + g) * D +
+                             8 * rg;
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        qb[q][k] = valid ? *reinterpret_cast<const uint4*>(qrow + 32 * k) : make_uint4(0, 0, 0, 0);
+      ab[q] = 0.f;
+      if (alibi) {
+        float sl = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          const float v = uniform_load(a.alibi_slopes, h0 + gg);
+          sl = g == gg ? v : sl;
+        }
+        ab[q] = sl * kLog2e / cs;
+      }
+    }
+
+    float m_ref[NQ], m_true[NQ], lsum[NQ];
+    f32x4_t acc[NQ][NT];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      m_ref[q] = -INFINITY;
+      m_true[q] = -INFINITY;
+      lsum[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[q][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    uint4 kb[2][KS];
+    VRow vb[2][4];
+
+#define VL_LOAD(SL, BID)                                                                              \
+  do {                                                                                                \
+    const int64_t boff_ = (int64_t)(BID) * block_bytes;                                               \
+    const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, tile_bytes);                          \
+    const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                          \
+    _Pragma("unroll") for (int k = 0; k < KS; ++k) kb[SL][k] =                                       \
+        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 64 * k, 0, 0));  \
+    _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                  \
+      if constexpr (DPL == 8)                                                                         \
+        vb[SL][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b128(vr_, v_off, e * tok_bytes, 0)); \
+      else                                                                                            \
+        vb[SL][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+    }                                                                                                 \
+  } while (0)
+
+#define VL_BLOCK(SL, TOK0)                                                                            \
+  do {                                                                                                \
+    const int t0_ = (TOK0) + 4 * rg; /* this lane's first token row */                                \
+    if (vis_end - (TOK0) < kTok) { /* rows past the unit's last visible position: stale V */          \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) vb[SL][e] = t0_ + e < vis_end ? vb[SL][e] : VRow{}; \
+    }                                                                                                 \
+    uint2 pb[NQ];                                                                                     \
+    _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                  \
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};                                                               \
+      _Pragma("unroll") for (int k = 0; k < KS; ++k) c = mfma16<ST>(kb[SL][k], qb[q][k], c);          \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                 \
+        if (alibi) c[e] = fmaf(ab[q], (float)(t0_ + e - pos[q]), c[e]);                               \
+        c[e] = t0_ + e <= lim[q] ? c[e] : -INFINITY;                                                  \
+      }                                                                                               \
+      const float lm = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));                                   \
+      m_true[q] = fmaxf(m_true[q], lm);                                                               \
+      if (__builtin_amdgcn_ballot_w64(lm > m_ref[q] + lazy_raw) != 0) {                               \
+        float hm = fmaxf(lm, __shfl_xor(lm, 16));                                                     \
+        hm = fmaxf(hm, __shfl_xor(hm, 32));                                                           \
+        const bool mv = hm > m_ref[q] + lazy_raw;                                                     \
+        const float alpha = mv ? exp2_fast((m_ref[q] - hm) * cs) : 1.f;                               \
+        m_ref[q] = mv ? hm : m_ref[q];                                                                \
+        lsum[q] *= alpha;                                                                             \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) acc[q][j] *= alpha;                           \
+      }                                                                                               \
+      const float ref = m_ref[q] == -INFINITY ? 0.f : m_ref[q] * cs;                                  \
+      float pr[4];                                                                                    \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(fmaf(c[e], cs, -ref));         \
+      lsum[q] += (pr[0] + pr[1]) + (pr[2] + pr[3]);                                                   \
+      pb[q] = make_uint2(pack2<ST>(pr[0], pr[1]), pack2<ST>(pr[2], pr[3]));                           \
+    }                                                                                                 \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                  \
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;                                       \
+      const uint2 va = make_uint2(__builtin_amdgcn_perm(vword(vb[SL][1], j >> 1), vword(vb[SL][0], j >> 1), sel), \
+                                  __builtin_amdgcn_perm(vword(vb[SL][3], j >> 1), vword(vb[SL][2], j >> 1), sel)); \
+      _Pragma("unroll") for (int q = 0; q < NQ; ++q) acc[q][j] = mfma_pv<ST>(va, pb[q], acc[q][j]);   \
+    }                                                                                                 \
+  } while (0)
+
+    if (tid == 0) sm.bad = 0;
+    lds_barrier();  // the previous unit's readers of sm are done
+    const int b_end = (vis_end + kTok - 1) / kTok;
+    for (int cb = 0; cb < b_end; cb += kTable) {
+      const int cn = min(kTable, b_end - cb);
+      if (cb != 0) lds_barrier();  // every wave has read the previous chunk's ids
+      const int nwc = __builtin_amdgcn_readfirstlane(w < cn ? (cn - w + kWaves - 1) / kWaves : 0);
+      int staged[kStage];
+#pragma unroll
+      for (int s = 0; s < kStage; ++s) {
+        const int i = tid + s * kThreads;
+        staged[s] = i < cn ? table[cb + i] : 0;
+      }
+      {  // the wave's first block, loaded before the staging completes (invalid ids: block 0)
+        const int id0 = uniform_load(table, cb + min(w, cn - 1));
+        VL_LOAD(0, (id0 >= 0 && (int64_t)id0 < a.num_blocks) ? id0 : 0);
+      }
+#pragma unroll
+      for (int s = 0; s < kStage; ++s) {
+        const int i = tid + s * kThreads;
+        if (i < cn) {
+          sm.ids[i] = staged[s];
+          if (staged[s] < 0 || (int64_t)staged[s] >= a.num_blocks) sm.bad = 1;
+        }
+      }
+      lds_barrier();
+      if (__builtin_amdgcn_readfirstlane(sm.bad)) {
+        bad = true;
+        break;
+      }
+      if (nwc == 0) continue;
+      auto id_of = [&](int j) -> int { return sm.ids[w + min(j, nwc - 1) * kWaves]; };
+      int id_next = id_of(1);
+      int it0 = 0;
+      do {  // a whole number of two-step turns; a step past the last block is fully masked
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int it = it0 + st;
+          VL_LOAD(st ^ 1, __builtin_amdgcn_readfirstlane(id_next));
+          id_next = id_of(it + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          VL_BLOCK(st, it < nwc ? (cb + w + it * kWaves) * kTok : vis_end);
+        }
+        it0 += 2;
+      } while (it0 < nwc);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // retire the unconsumed prefetch
+    }
+#undef VL_LOAD
+#undef VL_BLOCK
+
+    // ---- this wave's state per column, relative to the column's true max -------------
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float mt = fmaxf(m_true[q], __shfl_xor(m_true[q], 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float f = m_ref[q] == -INFINITY ? 0.f : exp2_fast((m_ref[q] - mt) * cs);
+      float lw = lsum[q];
+      lw += __shfl_xor(lw, 16);
+      lw += __shfl_xor(lw, 32);
+      const int cc = 16 * q + col;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.acc[w][cc][DPL * (4 * rg + i) + j] = acc[q][j][i] * f;
+      if (rg == 0) {
+        sm.mw[w][cc] = mt;
+        sm.lw[w][cc] = lw * f;
+      }
+    }
+    __syncthreads();
+
+    // ---- merge the waves and write the unit's rows ------------------------------------
+    for (int o = tid; o < QC * D; o += kThreads) {
+      const int cc = o / D;
+      const int d = o - cc * D;
+      const int ti = i0 + cc / G;
+      if (ti >= i_end) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.mw[ww][cc]);
+      float ls = 0.f, os = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float fw = sm.mw[ww][cc] == -INFINITY ? 0.f : exp2_fast((sm.mw[ww][cc] - M) * cs);
+          ls = fmaf(sm.lw[ww][cc], fw, ls);
+          os = fmaf(sm.acc[ww][cc][d], fw, os);
+        }
+      }
+      float res = M == -INFINITY ? 0.f : os / ls;
+      if (bad) res = NAN;
+      const int64_t row = (int64_t)(q0 + ti) * a.num_q_heads + h0 + cc % G;
+      static_cast<uint16_t*>(a.out)[row * D + d] = (uint16_t)to_storage<ST>(res);
+    }
+  }
+}
+
+template <class ST, int D, int G>
+hipError_t launch_g(const VarlenArgs& a, hipStream_t stream) {
+  constexpr int NQ = 2;
+  constexpr int QT = 16 * NQ / G;
+  const int64_t chunks = a.max_query_len <= 0 ? 1 : (a.max_query_len + QT - 1) / QT;
+  const int64_t grid = (int64_t)a.num_kv_heads * a.num_reqs * chunks;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((varlen_kernel<ST, D, G, NQ>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class ST, int D>
+hipError_t launch_d(const VarlenArgs& a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_g<ST, D, 1>(a, stream);
+    case 2: return launch_g<ST, D, 2>(a, stream);
+    case 4: return launch_g<ST, D, 4>(a, stream);
+    case 8: return launch_g<ST, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class ST>
+hipError_t launch_st(const VarlenArgs& a, int head_size, hipStream_t stream) {
+  switch (head_size) {
+    case 64: return launch_d<ST, 64>(a, stream);
+    case 128: return launch_d<ST, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_varlen(const VarlenArgs& a, int dtype, int head_size, hipStream_t stream) {
+  switch (dtype) {
+    case 1: return launch_st<F16>(a, head_size, stream);
+    case 2: return launch_st<BF16>(a, head_size, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pcache

@@ -154,3 +154,24 @@ def partials_call(pool: DevicePool, inp: DecodeInputs, msl: int):
 
 def out_f64(out: torch.Tensor) -> np.ndarray:
     return out.double().cpu().numpy()
+
+
+def varlen(pool: DevicePool, vq, wl=None, q_bits=None, causal=None, max_query_len=None, seq_lens=None,
+           block_tables=None):
+    """pc_paged_attention_varlen of a VarlenStep's packed queries; returns out [total_q, Hq, D]."""
+    wl = pool.wl if wl is None else wl
+    q = to_dev(vq.q if q_bits is None else q_bits, wl.dtype)
+    out = torch.full_like(q, float("nan"))
+    qs = torch.from_numpy(np.ascontiguousarray(vq.query_start_loc, np.int32)).cuda()
+    sl = torch.from_numpy(np.ascontiguousarray(wl.seq_lens if seq_lens is None else seq_lens, np.int32)).cuda()
+    bt = torch.from_numpy(np.ascontiguousarray(wl.block_tables if block_tables is None else block_tables,
+                                               np.int32)).cuda()
+    al = getattr(wl, "alibi_slopes", None)
+    al = None if al is None else torch.from_numpy(np.ascontiguousarray(al, np.float32)).cuda()
+    pc.paged_attention_varlen(out, q, pool.k, pool.v, bt, qs, sl,
+                              vq.max_query_len if max_query_len is None else max_query_len,
+                              num_kv_heads=wl.num_kv_heads, scale=float(wl.scale),
+                              causal=vq.causal if causal is None else causal, alibi_slopes=al,
+                              **pool.layout_kwargs())
+    torch.cuda.synchronize()
+    return out

@@ -35,13 +35,14 @@ def declared_symbols():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
     assert {"pc_reshape_and_cache", "pc_paged_attention_decode", "pc_paged_attention_reduce",
-            "pc_paged_attention_plan", "pc_reshape_and_cache_fp8", "pc_paged_attention_decode_fp8"} <= set(names)
+            "pc_paged_attention_plan", "pc_reshape_and_cache_fp8", "pc_paged_attention_decode_fp8",
+            "pc_paged_attention_varlen"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert pc.abi_version() == 3
+    assert pc.abi_version() == 4
     assert pc.status_string(0) == "ok"
     assert "invalid" in pc.status_string(-1)
     assert "unsupported" in pc.status_string(-2)
@@ -151,6 +152,31 @@ def test_write_fp8_validation(lib):
         assert call(**bad) == -1, bad
     for unsup in (dict(D=126, krs=1008, vrs=1008, hs=2016), dict(ts=130), dict(k=ctypes.c_void_p(0x10002))):
         assert call(**unsup) == -2, unsup
+
+
+def _varlen(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=100, bs=8 * 16 * 128, ts=128, hs=16 * 128, bt=FAKE, W=128,
+             qsl=FAKE, sl=FAKE, R=4, T=40, mq=16, Hq=32, Hkv=8, D=128, B=16, scale=0.088, causal=1, alibi=None, dt=2)
+    a.update(kw)
+    return lib.pc_paged_attention_varlen(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"],
+                                         a["bt"], a["W"], a["qsl"], a["sl"], a["R"], a["T"], a["mq"], a["Hq"],
+                                         a["Hkv"], a["D"], a["B"], a["scale"], a["causal"], a["alibi"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), -1), (dict(R=-1), -1), (dict(T=-1), -1), (dict(mq=-1), -1), (dict(causal=2), -1),
+    (dict(qsl=None), -1), (dict(out=None), -1), (dict(Hq=30), -1), (dict(scale=0.0), -1), (dict(nb=0), -1),
+    (dict(dt=0), -2),                                  # fp32: no varlen kernel
+    (dict(B=32, W=64), -2), (dict(D=96, bs=8 * 16 * 96, hs=16 * 96, ts=96), -2), (dict(Hq=128), -2),
+    (dict(out=ctypes.c_void_p(0x10008)), -2), (dict(ts=100), -2),
+])
+def test_varlen_validation(lib, kw, status):
+    assert _varlen(lib, **kw) == status
+
+
+def test_varlen_empty_is_a_noop(lib):
+    assert _varlen(lib, R=0) == 0
+    assert _varlen(lib, T=0, q=None, out=None) == 0
 
 
 def test_reduce_validation(lib):
