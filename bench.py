@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="cache element type: the query's type, or OCP E4M3 codes with per-kv-head scales")
     ap.add_argument("--alibi", action="store_true", help="add the ALiBi bias (geometric slopes, one per query head)")
+    ap.add_argument("--varlen", choices=["prefill", "spec"], default=None,
+                    help="time multi-token queries instead: a chunked-prefill step (512-token chunks) or a "
+                         "speculative-decode step (4 query tokens per request)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -125,6 +128,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
         return
+
+    if args.varlen:
+        return bench_varlen(args)
 
     import gpu_harness as gh
     import paged_kv_cache_reshape_amd as pc
@@ -293,6 +299,122 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def varlen_flops(wl, vq) -> int:
+    """Algorithmic FLOPs of the multi-token attention: per (query row, head, visible
+    token) one D-long multiply-add for q.k and one for P.V."""
+    total = 0
+    qs = vq.query_start_loc
+    for r in range(wl.num_seqs):
+        L, n = int(wl.seq_lens[r]), int(qs[r + 1] - qs[r])
+        vis = sum(L - n + i + 1 for i in range(n)) if vq.causal else n * L
+        total += vis
+    return total * wl.num_q_heads * wl.head_size * 4
+
+
+def bench_varlen(args):
+    """Multi-token step: the write of every request's new rows, then the causal
+    attention of those rows over the whole paged history."""
+    import torch
+    import gpu_harness as gh
+    import paged_kv_cache_reshape_amd as pc
+    from workloads import varlen_config
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating varlen workload {args.varlen}", file=sys.stderr, flush=True)
+    wl, vq = varlen_config(args.varlen)
+    per_copy = 2 * wl.pool_elems * wl.esize
+    copies = args.copies or max(1, min(8, -(-(1 << 30) // max(1, wl.kv_bytes())) + 1))
+    copies = max(1, min(copies, int(64e9 // per_copy)))
+    pools = [gh.filled_pool(wl) for _ in range(copies)]
+    q = gh.to_dev(vq.q, wl.dtype)
+    out = torch.empty_like(q)
+    key, value = gh.to_dev(vq.key, wl.dtype), gh.to_dev(vq.value, wl.dtype)
+    slots = torch.from_numpy(vq.slot_mapping).to(dev)
+    qs = torch.from_numpy(vq.query_start_loc).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def attend(i):
+        pool = pools[i % copies]
+        pc.paged_attention_varlen(out, q, pool.k, pool.v, bt, qs, sl, vq.max_query_len,
+                                  num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), causal=vq.causal,
+                                  **pool.layout_kwargs())
+
+    def step(i):
+        pool = pools[i % copies]
+        pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **pool.layout_kwargs())
+        attend(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        attend(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = e0.elapsed_time(e1) / args.steps
+
+    flops = varlen_flops(wl, vq)
+    kv = wl.kv_bytes()
+    qo = vq.total_q * wl.num_q_heads * wl.head_size * 2 * wl.esize
+    ms = el / args.steps * 1e3
+    toks = vq.total_q / (ms * 1e-3)
+    if args.varlen == "prefill":
+        metric, unit, value = "varlen chunked-prefill attention query tokens/s", "tokens/s", toks
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                "frac": round(achieved / 2500.0, 4), "traffic": None, "kernel": "varlen_kernel",
+                "flops_per_launch": flops, "launch_us": round(kern_ms * 1e3, 2)}
+    else:
+        metric, unit, value = "varlen speculative-decode attention effective GB/s", "GB/s", (kv + qo) / (ms * 1e-3) / 1e9
+        achieved = (kv + qo) / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "varlen_kernel",
+                "bytes_per_launch": kv + qo, "launch_us": round(kern_ms * 1e3, 2)}
+    roof["timing"] = "HIP events around back-to-back launches on the launch stream"
+    res = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+           "config": {"workload": wl.name, "num_reqs": wl.num_seqs, "query_tokens": vq.total_q,
+                      "query_len": vq.max_query_len, "num_q_heads": wl.num_q_heads,
+                      "num_kv_heads": wl.num_kv_heads, "head_size": wl.head_size, "causal": vq.causal,
+                      "kv_bytes_per_step": kv, "attention_flops_per_step": flops, "pool_copies": copies},
+           "tokens_per_s": round(toks, 1), "varlen_kernel_us_batched": round(kern_ms * 1e3, 2),
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        threads = min(os.cpu_count() or 1, 16)
+        pool = oracle.filled_pool(wl)
+        # a bounded sample: the first requests' query rows (the others get empty ranges)
+        k = 1 if args.varlen == "prefill" else wl.num_seqs
+        qs_h = vq.query_start_loc.copy()
+        qs_h[k + 1:] = qs_h[k]
+        rows = int(qs_h[k])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.varlen(wl, pool, vq, q=vq.q[:rows], query_start_loc=qs_h, nthreads=threads)
+            reps += 1
+            el_c = time.perf_counter() - t0
+            if el_c >= args.cpu_seconds or reps >= 1000:
+                break
+        res["cpu_baseline"] = {"value": round(reps * rows / el_c, 3), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{reps} x fp64 attention of the query rows of the first {k} request(s) "
+                                         f"({rows} rows each) in {el_c:.1f} s on {threads} host threads"}
     print(json.dumps(res), flush=True)
 
 

@@ -110,3 +110,32 @@ def test_varlen_bad_request_is_nan_only_there():
     assert np.isnan(out[qs[1]:qs[2]]).all() and np.isnan(out[qs[2]:qs[3]]).all()
     err = np.abs(out[qs[0]:qs[1]] - ref[qs[0]:qs[1]]).max()
     assert err <= TOL
+
+
+@pytest.mark.parametrize("kind,sample", [("spec", None), ("prefill", [0, 5])])
+def test_varlen_bench_workloads(kind, sample):
+    """The benchmark's multi-token workloads at full size, in the configuration it times;
+    for the prefill workload the oracle covers the rows of a sample of requests."""
+    from workloads import varlen_config
+    say(f"[varlen {kind}] generating")
+    wl, vq = varlen_config(kind)
+    dpool = gh.filled_pool(wl)
+    out = gh.out_f64(gh.varlen(dpool, vq))
+    hpool = oracle.filled_pool(wl)
+    qs = vq.query_start_loc
+    if sample is None:
+        check_rows = np.arange(vq.total_q)
+        ref = oracle.varlen(wl, hpool, vq)
+    else:
+        # only the sampled requests keep their rows; the others get empty ranges
+        n = np.zeros(wl.num_seqs, np.int64)
+        for r in sample:
+            n[r] = qs[r + 1] - qs[r]
+        qs_s = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        check_rows = np.concatenate([np.arange(qs[r], qs[r + 1]) for r in sample])
+        ref = oracle.varlen(wl, hpool, vq, q=vq.q[check_rows], query_start_loc=qs_s)
+    got = out[check_rows]
+    assert np.isfinite(out).all()
+    err = np.abs(got - ref)
+    say(f"[varlen {kind}] {len(check_rows)} rows: max|err| {err.max():.3e}, max|o| {np.abs(ref).max():.3f}")
+    assert err.max() <= TOL

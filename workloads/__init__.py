@@ -18,5 +18,6 @@ from .gen import (  # noqa: F401
     fp8_variant,
     make_config,
     nan_bits,
+    varlen_config,
     varlen_variant,
 )

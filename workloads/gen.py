@@ -559,3 +559,21 @@ def varlen_variant(wl: Workload, query_lens, causal: bool = True) -> VarlenStep:
     cat = lambda xs: np.concatenate(xs) if xs else np.zeros(shape, _BITS_NP[wl.dtype])
     return VarlenStep(q=q, query_start_loc=qs, query_lens=n, key=cat(keys), value=cat(values),
                       slot_mapping=np.concatenate(slots) if slots else np.zeros(0, np.int64), causal=causal)
+
+
+VARLEN_CONFIGS = {
+    # chunked prefill: 8 requests whose newest 512 tokens form the query, histories of
+    # 1024..4096 tokens (chunk included), GQA 32/8, D = 128, bf16
+    "prefill": dict(name="chunked_prefill_bf16_r8_q512_l1024_4096", seed=21, S=8, lo=1024, hi=4096, n=512),
+    # speculative decode: 64 requests verifying 4 draft tokens each over 512..2048 tokens
+    "spec": dict(name="spec_decode_bf16_s64_q4_l512_2048", seed=22, S=64, lo=512, hi=2048, n=4),
+}
+
+
+def varlen_config(kind: str, contents: bool = True):
+    """(workload, VarlenStep) of a named multi-token workload (see VARLEN_CONFIGS)."""
+    c = VARLEN_CONFIGS[kind]
+    rng = np.random.Generator(np.random.PCG64(c["seed"]))
+    lengths = rng.integers(c["lo"], c["hi"] + 1, size=c["S"]).astype(np.int32)
+    wl = custom(c["seed"], "bf16", 32, 8, 128, lengths, name=c["name"])
+    return wl, varlen_variant(wl, np.full(c["S"], c["n"], np.int32))
