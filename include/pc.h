@@ -142,7 +142,9 @@ int pc_reshape_and_cache(const void *key, const void *value, int64_t key_row_str
  *   num_q_heads       multiple of num_kv_heads; num_q_heads/num_kv_heads in {1,2,4,8}
  *                     for fp16/bf16, {1,2,4} for fp32
  *   head_size         64 or 128
- *   block_size        16
+ *   block_size        8, 16 or 32 for fp16/bf16 (and the 8-bit cache); 16 for fp32
+ *                     ("vLLM 源码完全拆解（七）", section GQA、向量化加载与 Block Size
+ *                     的联动: the block size trades fragmentation against table reads)
  *   scale             multiplies q.k (typically 1/sqrt(head_size)); positive, finite
  *   partition_size    0: one pass, writes out.  PC_PARTITION_SIZE: split path,
  *                     writes only exp_sums, max_logits and tmp_out; follow with

@@ -69,7 +69,9 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   if (kv8 && (!k_scale || !v_scale)) return PC_ERR_INVALID_ARG;
   if (num_blocks <= 0 || block_stride <= 0 || token_stride <= 0 || head_stride <= 0) return PC_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !std::isfinite(scale)) return PC_ERR_INVALID_ARG;
-  if (block_size != kBlockTokens) return PC_ERR_UNSUPPORTED;
+  // 16-bit and 8-bit pools: blocks of 8, 16 or 32 tokens; fp32 storage: 16
+  if (block_size != 8 && block_size != 16 && block_size != 32) return PC_ERR_UNSUPPORTED;
+  if (dtype == PC_F32 && block_size != kBlockTokens) return PC_ERR_UNSUPPORTED;
   if (kv8 && dtype == PC_F32) return PC_ERR_UNSUPPORTED;
   if (!pcache::decode_supported(dtype, head_size, num_q_heads / num_kv_heads)) return PC_ERR_UNSUPPORTED;
   const int pes = kv8 ? 1 : es;  // pool bytes per element
@@ -96,6 +98,7 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.max_partitions = parts;
   a.exp_sums = exp_sums;

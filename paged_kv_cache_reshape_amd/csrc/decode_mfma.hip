@@ -65,7 +65,7 @@
 namespace pcache {
 namespace {
 
-constexpr int kBlockTokens = 16;
+constexpr int kBlockTokens = 16;  // tokens per score tile (the MFMA's 16 rows); pool blocks hold BS
 constexpr int kPartition = 512;
 constexpr float kLazy = 8.f;            // log2-domain slack before the exponent reference moves
 constexpr int kMaxRankedSeqs = 512;     // sequences ranked by length in-kernel (beyond: index order)
@@ -123,14 +123,17 @@ struct UnitLds {
 // One unit: kv head `kvh` of sequence `s`, tokens [t_begin, t_end).  All waves of
 // the workgroup call it together (it uses block-wide barriers).  Writes out (one
 // pass) or the partition's partials (split).  KV8: the pool holds E4M3 codes.
-template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT, bool KV8>
+template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT, bool KV8, int BS>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, G, TABLE>& sm, int s, int kvh,
                                             int part) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
   static_assert(D == 64 || D == 128, "head size 64 or 128");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group of 1, 2, 4 or 8 query heads");
   static_assert(STAGES >= 2 && STAGES <= 4, "prefetch ring of 2..4 register sets");
-  static_assert(!SPLIT || TABLE >= kPartition / kBlockTokens, "a partition's ids fit the table");
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size 8, 16 or 32");
+  // tiles per staged chunk: the chunk's block ids must fit the TABLE entries
+  constexpr int CT = BS >= 16 ? TABLE * (BS / 16) : TABLE / (16 / BS);
+  static_assert(!SPLIT || CT >= kPartition / kBlockTokens, "a partition's ids fit the table");
   constexpr int KS = D / 32;   // q.k MFMA k-steps per block
   constexpr int DPL = D / 16;  // V dims a lane loads per row = out^T tiles per block
   constexpr int NT = DPL;
@@ -152,7 +155,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const float vsc = KV8 ? uniform_load(a.v_scale, (int64_t)kvh * a.scale_stride) : 1.f;
   const float cs_raw = a.scale_log2 * ksc;
   const bool bad_scale = KV8 && !(cs_raw >= 0x1p-120f && cs_raw <= 0x1p120f && vsc > 0.f && vsc <= 3.4e38f);
-  bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
+  bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * BS ||
              (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition) || bad_scale;
   const int t_begin = SPLIT ? part * kPartition : 0;
   const int t_end = bad ? t_begin : (SPLIT ? min(L, t_begin + kPartition) : L);
@@ -190,6 +193,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   // 16-bit: + 64*k per MFMA step; 8-bit: the lane's D/4 contiguous codes, 16 bytes per load
   const int k_off = col * tok_bytes + (KV8 ? rg * (D / 4) : 16 * rg);
   const int v_off = 4 * rg * tok_bytes + col * (EB * DPL);  // + e*tok_bytes for row 4*rg + e
+  // 8-token blocks: a tile's rows 0-7 lie in one block, 8-15 in the next; a lane's K row
+  // (token col) and V rows (4*rg .. +3) sit at these offsets inside their block
+  const int k_off8 = (col & 7) * tok_bytes + (KV8 ? rg * (D / 4) : 16 * rg);
+  const int v_off8 = 4 * (rg & 1) * tok_bytes + col * (EB * DPL);
+  const int nblk = (t_end + BS - 1) / BS;  // blocks holding the unit's tokens (from block 0)
   const float lazy_raw = kLazy / cs;
   // ALiBi: the bias of head `col` in raw q.k units (times cs it is slope * log2 e per
   // token).  The slope is loaded here and converted after the first K/V loads are out.
@@ -210,29 +218,47 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   uint4 kq[STAGES][K8];  // 8-bit pool ring (raw codes)
   VRow8 vq[STAGES][4];
 
-  // K/V of the block with id BID into ring slot ST
-#define PC_LOAD(ST, BID)                                                                             \
+  // K/V of tile (A, B) into ring slot ST.  16-token blocks: block A.  32: rows 16*B ..
+  // of block A.  8: rows 0-7 from block A, 8-15 from block B (each lane addresses its own
+  // block, so these are global loads with 64-bit lane addresses).
+#define PC_LOAD(ST, A, B)                                                                            \
   do {                                                                                               \
-    const int64_t boff_ = (int64_t)(BID) * block_bytes;                                              \
-    const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, tile_bytes);                         \
-    const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                         \
-    if constexpr (KV8) {                                                                             \
-      _Pragma("unroll") for (int k = 0; k < K8; ++k) kq[ST][k] =                                    \
-          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 16 * k, 0, 0)); \
-      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                               \
-        if constexpr (DPL == 8)                                                                      \
-          vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
-        else                                                                                         \
-          vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b32(vr_, v_off, e * tok_bytes, 0)); \
+    if constexpr (BS == 8) {                                                                         \
+      const int64_t ka_ = (int64_t)((col < 8) ? (A) : (B)) * block_bytes + k_off8;                   \
+      const int64_t va_ = (int64_t)((rg < 2) ? (A) : (B)) * block_bytes + v_off8;                   \
+      if constexpr (KV8) {                                                                           \
+        _Pragma("unroll") for (int k = 0; k < K8; ++k) kq[ST][k] =                                  \
+            *reinterpret_cast<const uint4*>(kpool + ka_ + 16 * k);                                   \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) vq[ST][e] =                                   \
+            *reinterpret_cast<const VRow8*>(vpool + va_ + (int64_t)e * tok_bytes);                   \
+      } else {                                                                                       \
+        _Pragma("unroll") for (int k = 0; k < KS; ++k) kb[ST][k] =                                  \
+            *reinterpret_cast<const uint4*>(kpool + ka_ + 64 * k);                                   \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) vb[ST][e] =                                   \
+            *reinterpret_cast<const VRow*>(vpool + va_ + (int64_t)e * tok_bytes);                    \
       }                                                                                              \
     } else {                                                                                         \
-      _Pragma("unroll") for (int k = 0; k < KS; ++k) kb[ST][k] =                                    \
-          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 64 * k, 0, 0)); \
-      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                               \
-        if constexpr (DPL == 8)                                                                      \
-          vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b128(vr_, v_off, e * tok_bytes, 0)); \
-        else                                                                                         \
-          vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+      const int64_t boff_ = (int64_t)(A) * block_bytes + (BS == 32 ? (int64_t)(B) * tile_bytes : 0); \
+      const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, tile_bytes);                       \
+      const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                       \
+      if constexpr (KV8) {                                                                           \
+        _Pragma("unroll") for (int k = 0; k < K8; ++k) kq[ST][k] =                                  \
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 16 * k, 0, 0)); \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                             \
+          if constexpr (DPL == 8)                                                                    \
+            vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+          else                                                                                       \
+            vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b32(vr_, v_off, e * tok_bytes, 0)); \
+        }                                                                                            \
+      } else {                                                                                       \
+        _Pragma("unroll") for (int k = 0; k < KS; ++k) kb[ST][k] =                                  \
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 64 * k, 0, 0)); \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                             \
+          if constexpr (DPL == 8)                                                                    \
+            vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b128(vr_, v_off, e * tok_bytes, 0)); \
+          else                                                                                       \
+            vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+        }                                                                                            \
       }                                                                                              \
     }                                                                                                \
   } while (0)
@@ -309,10 +335,19 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   // the previous unit read sm.bad before its merge barrier, so it can be cleared here
   if (tid == 0) sm.bad = 0;
   lds_barrier();  // the previous unit's readers of sm are done
-  for (int cb = b_begin; cb < b_end; cb += TABLE) {
-    const int cn = min(TABLE, b_end - cb);  // blocks in this chunk
-    if (cb != b_begin) __syncthreads();     // every wave has read the previous chunk's ids
-    // this wave: chunk blocks w, w + NW, ...
+  for (int cb = b_begin; cb < b_end; cb += CT) {
+    const int cn = min(CT, b_end - cb);  // tiles in this chunk
+    if (cb != b_begin) __syncthreads();  // every wave has read the previous chunk's ids
+    // the chunk's block ids: blocks [blk0, blk0 + nb) (chunk starts are even tiles)
+    const int blk0 = BS >= 16 ? cb / (BS / 16) : cb * (16 / BS);
+    const int nb = BS >= 16 ? (cb + cn - 1) / (BS / 16) - blk0 + 1 : min((cb + cn) * (16 / BS), nblk) - blk0;
+    // tile jl of the chunk as (A, B): (block, 0), (block, 16-row half) or (block, next block)
+    auto tile_of = [&](int jl) -> int2 {
+      if constexpr (BS == 16) return make_int2(sm.ids[jl], 0);
+      else if constexpr (BS == 32) return make_int2(sm.ids[jl >> 1], jl & 1);
+      else return make_int2(sm.ids[2 * jl], sm.ids[min(2 * jl + 1, nb - 1)]);
+    };
+    // this wave: chunk tiles w, w + NW, ...
     const int nwc = __builtin_amdgcn_readfirstlane(w < cn ? (cn - w + NW - 1) / NW : 0);
     // the chunk's ids, kStage per thread, requested before anything else of the chunk
     constexpr int kStage = (TABLE + kThreads - 1) / kThreads;
@@ -320,22 +355,29 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 #pragma unroll
     for (int r = 0; r < kStage; ++r) {
       const int i = tid + r * kThreads;
-      staged[r] = i < cn ? table[cb + i] : 0;
+      staged[r] = i < nb ? table[blk0 + i] : 0;
     }
-    // The wave's first block is read from the table directly (scalar cache) and its
+    // The wave's first tile is read from the table directly (scalar cache) and its
     // loads issued before the workgroup's staging of the chunk's ids completes, so the
     // first K/V bytes are on their way one table round trip earlier.  An id outside the
     // pool is replaced by block 0 here; the staged check below then discards the unit.
     // (issued by every wave, so that the wait for the staged ids below is exact; a wave
-    // with no block in the chunk fetches the chunk's last one and never reads it)
+    // with no tile in the chunk fetches the chunk's last one and never reads it)
     {
-      const int id0 = uniform_load(table, cb + min(w, cn - 1));
-      PC_LOAD(0, (id0 >= 0 && (int64_t)id0 < a.num_blocks) ? id0 : 0);
+      const int jt = cb + min(w, cn - 1);
+      auto valid = [&](int id) { return (id >= 0 && (int64_t)id < a.num_blocks) ? id : 0; };
+      if constexpr (BS == 16) {
+        PC_LOAD(0, valid(uniform_load(table, jt)), 0);
+      } else if constexpr (BS == 32) {
+        PC_LOAD(0, valid(uniform_load(table, jt >> 1)), jt & 1);
+      } else {
+        PC_LOAD(0, valid(uniform_load(table, 2 * jt)), valid(uniform_load(table, min(2 * jt + 1, nblk - 1))));
+      }
     }
 #pragma unroll
     for (int r = 0; r < kStage; ++r) {
       const int i = tid + r * kThreads;
-      if (i < cn) {
+      if (i < nb) {
         sm.ids[i] = staged[r];
         if (staged[r] < 0 || (int64_t)staged[r] >= a.num_blocks) sm.bad = 1;
       }
@@ -347,23 +389,27 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     }
     if (nwc == 0) continue;
     if (alibi) ab = slope * kLog2e / cs;
-    auto id_of = [&](int j) -> int { return sm.ids[w + min(j, nwc - 1) * NW]; };
+    auto ref_of = [&](int j) -> int2 { return tile_of(w + min(j, nwc - 1) * NW); };
 #pragma unroll
-    for (int st = 1; st < STAGES - 1; ++st) PC_LOAD(st, __builtin_amdgcn_readfirstlane(id_of(st)));
-    int id_next = id_of(STAGES - 1);
-    // The ring turns a whole number of times: a step past the wave's last block in
-    // the chunk consumes a repeat of that block (fetched again from cache) with
-    // every token masked, which changes no state.
+    for (int st = 1; st < STAGES - 1; ++st) {
+      const int2 t = ref_of(st);
+      PC_LOAD(st, __builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y));
+    }
+    int2 ref_next = ref_of(STAGES - 1);
+    // The ring turns a whole number of times: a step past the wave's last tile in the
+    // chunk consumes a repeat of that tile (fetched again from cache) with every token
+    // masked, which changes no state.
     int it0 = 0;
     do {
 #pragma unroll
       for (int st = 0; st < STAGES; ++st) {
         const int it = it0 + st;
-        PC_LOAD((st + STAGES - 1) % STAGES, __builtin_amdgcn_readfirstlane(id_next));
-        id_next = id_of(it + STAGES);
-        // keep the scheduler from sinking the prefetch below the wait for this block
+        PC_LOAD((st + STAGES - 1) % STAGES, __builtin_amdgcn_readfirstlane(ref_next.x),
+                __builtin_amdgcn_readfirstlane(ref_next.y));
+        ref_next = ref_of(it + STAGES);
+        // keep the scheduler from sinking the prefetch below the wait for this tile
         __builtin_amdgcn_sched_barrier(0);
-        // a step past the wave's last block of this chunk sees no token
+        // a step past the wave's last tile of this chunk sees no token
         PC_BLOCK(st, it < nwc ? (cb + w + it * NW) * kBlockTokens : t_end);
       }
       it0 += STAGES;
@@ -427,11 +473,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 }
 
 // Split path: workgroup = (kv head, sequence, partition), fastest-varying first.
-template <class ST, int D, int G, bool KV8>
+template <class ST, int D, int G, bool KV8, int BS>
 __global__ __launch_bounds__(PCACHE_SPLIT_WAVES* kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int NW = PCACHE_SPLIT_WAVES;
-  constexpr int TABLE = kPartition / kBlockTokens;
+  constexpr int TABLE = BS >= 16 ? kPartition / kBlockTokens : kPartition / BS;  // a partition's block ids
   __shared__ UnitLds<NW, D, G, TABLE> sm;
   int64_t id = blockIdx.x;
   const int kvh = (int)(id % a.num_kv_heads);
@@ -439,11 +485,11 @@ void decode_split_kernel(DecodeArgs a) {
   const int s = (int)(id % a.num_seqs);
   const int part = (int)(id / a.num_seqs);
   const int L = uniform_load(a.seq_lens, s);
-  const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * kBlockTokens ||
+  const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * BS ||
                    (int64_t)L > (int64_t)a.max_partitions * kPartition;
   if (!bad && part * kPartition >= L) return;  // a partition past the sequence writes nothing
   constexpr int STAGES = KV8 ? PCACHE_SPLIT_STAGES_KV8 : PCACHE_SPLIT_STAGES;
-  decode_unit<ST, D, G, NW, STAGES, TABLE, true, KV8>(a, sm, s, kvh, part);
+  decode_unit<ST, D, G, NW, STAGES, TABLE, true, KV8, BS>(a, sm, s, kvh, part);
 }
 
 // One-pass path: persistent workgroups.  Round 0 takes units in index order (unit u =
@@ -452,7 +498,7 @@ void decode_split_kernel(DecodeArgs a) {
 // remaining units are ranked longest first and dealt in snake order, and the workgroup
 // whose round-0 unit was the r-th longest receives the r-th shortest unit of round 1,
 // which evens out the sums across workgroups.
-template <class ST, int D, int G, bool KV8>
+template <class ST, int D, int G, bool KV8, int BS>
 __global__ __launch_bounds__(onepass_waves<D>() * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_ONEPASS_OCC)))
 void decode_onepass_kernel(DecodeArgs a) {
   constexpr int NW = onepass_waves<D>();
@@ -474,7 +520,7 @@ void decode_onepass_kernel(DecodeArgs a) {
   if (ranked)  // read here, used after round 0 (its barriers publish the stores)
     for (int t = threadIdx.x; t < S; t += kThreads) len_lds[t] = a.seq_lens[t];
 
-  if (k < units) decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8>(a, sm, (int)(k / Hkv),
+  if (k < units) decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8, BS>(a, sm, (int)(k / Hkv),
                                                                                     (int)(k % Hkv), 0);
   if (units <= W) return;
   if (ranked) {
@@ -517,17 +563,17 @@ void decode_onepass_kernel(DecodeArgs a) {
       s = (int)((W + q) / Hkv);
       kvh = (int)((W + q) % Hkv);
     }
-    decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8>(a, sm, s, kvh, 0);
+    decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8, BS>(a, sm, s, kvh, 0);
   }
 }
 
 // Resident workgroups per CU for the one-pass kernel, queried once per instance.
-template <class ST, int D, int G, bool KV8>
+template <class ST, int D, int G, bool KV8, int BS>
 int onepass_blocks_per_cu() {
   static int cached = 0;
   if (!cached) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8, BS>,
                                                      onepass_waves<D>() * kWave, 0) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
@@ -538,12 +584,12 @@ int onepass_blocks_per_cu() {
   return cached;
 }
 
-template <class ST, int D, int G, bool KV8>
+template <class ST, int D, int G, bool KV8, int BS>
 hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
   if (split) {
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_split_kernel<ST, D, G, KV8>), dim3((unsigned)units), dim3(PCACHE_SPLIT_WAVES * kWave), 0,
+    hipLaunchKernelGGL((decode_split_kernel<ST, D, G, KV8, BS>), dim3((unsigned)units), dim3(PCACHE_SPLIT_WAVES * kWave), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -552,21 +598,31 @@ hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
 #ifdef PCACHE_ONEPASS_BLOCKS_PER_CU
   const int64_t slots = (int64_t)device_compute_units() * PCACHE_ONEPASS_BLOCKS_PER_CU;
 #else
-  const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G, KV8>();
+  const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G, KV8, BS>();
 #endif
   const int64_t grid = units < slots ? units : slots;
-  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, KV8>), dim3((unsigned)grid), dim3(onepass_waves<D>() * kWave), 0,
+  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, KV8, BS>), dim3((unsigned)grid), dim3(onepass_waves<D>() * kWave), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-template <class ST, int D, bool KV8>
+template <class ST, int D, bool KV8, int BS>
 hipError_t launch_group(const DecodeArgs& a, bool split, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_typed<ST, D, 1, KV8>(a, split, stream);
-    case 2: return launch_typed<ST, D, 2, KV8>(a, split, stream);
-    case 4: return launch_typed<ST, D, 4, KV8>(a, split, stream);
-    case 8: return launch_typed<ST, D, 8, KV8>(a, split, stream);
+    case 1: return launch_typed<ST, D, 1, KV8, BS>(a, split, stream);
+    case 2: return launch_typed<ST, D, 2, KV8, BS>(a, split, stream);
+    case 4: return launch_typed<ST, D, 4, KV8, BS>(a, split, stream);
+    case 8: return launch_typed<ST, D, 8, KV8, BS>(a, split, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class ST, int D, bool KV8>
+hipError_t launch_bs(const DecodeArgs& a, bool split, hipStream_t stream) {
+  switch (a.block_size) {
+    case 8: return launch_group<ST, D, KV8, 8>(a, split, stream);
+    case 16: return launch_group<ST, D, KV8, 16>(a, split, stream);
+    case 32: return launch_group<ST, D, KV8, 32>(a, split, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -574,9 +630,8 @@ hipError_t launch_group(const DecodeArgs& a, bool split, hipStream_t stream) {
 template <class ST>
 hipError_t launch_dim(const DecodeArgs& a, int head_size, bool split, hipStream_t stream) {
   switch (head_size) {
-    case 64: return a.kv8 ? launch_group<ST, 64, true>(a, split, stream) : launch_group<ST, 64, false>(a, split, stream);
-    case 128:
-      return a.kv8 ? launch_group<ST, 128, true>(a, split, stream) : launch_group<ST, 128, false>(a, split, stream);
+    case 64: return a.kv8 ? launch_bs<ST, 64, true>(a, split, stream) : launch_bs<ST, 64, false>(a, split, stream);
+    case 128: return a.kv8 ? launch_bs<ST, 128, true>(a, split, stream) : launch_bs<ST, 128, false>(a, split, stream);
     default: return hipErrorInvalidValue;
   }
 }

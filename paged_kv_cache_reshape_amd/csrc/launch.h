@@ -32,6 +32,7 @@ struct DecodeArgs {
   int max_blocks_per_seq;
   const int32_t* seq_lens;
   int num_seqs, num_q_heads, num_kv_heads;
+  int block_size;      // tokens per pool block: 8, 16 or 32
   float scale_log2;    // scale * log2(e): scores are kept in the base-2 domain
   int max_partitions;  // split path only
   int longest_first;   // one-pass path: workgroup i takes the i-th longest sequence's units

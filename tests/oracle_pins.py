@@ -387,6 +387,15 @@ def pin_numpy_dense():
         assert np.abs(out - dense_numpy(w)).max() < 1e-12, w.name
 
 
+def pin_block_sizes():
+    """Blocks of 8 and 32 tokens, every layout: numpy dense attention agrees to 1e-12."""
+    for B in (8, 32):
+        for layout in ("hnd", "nhd", "combined"):
+            w = custom(23 + B, "bf16", 8, 2, 64, [1, 7, 8, 9, 31, 33, 300], layout=layout, block_size=B)
+            out = oracle.decode(w, oracle.filled_pool(w))
+            assert np.abs(out - dense_numpy(w)).max() < 1e-12, (B, layout)
+
+
 def pin_torch_sdpa():
     """torch scaled_dot_product_attention in float64 on the CPU agrees to 1e-12."""
     import torch
@@ -759,7 +768,7 @@ PINS = [
     pin_combined_block_layout, pin_one_token_exact, pin_special_values_exact, pin_zero_query_mean,
     pin_equal_keys_mean, pin_two_tokens_sigmoid, pin_huge_logits, pin_placement_invariance,
     pin_negative_slot_skipped, pin_unread_memory, pin_table_padding, pin_write_out_of_range,
-    pin_numpy_dense, pin_torch_sdpa, pin_online_tiles, pin_brute_force, pin_split_identity,
+    pin_numpy_dense, pin_block_sizes, pin_torch_sdpa, pin_online_tiles, pin_brute_force, pin_split_identity,
     pin_e4m3_values, pin_e4m3_rounding, pin_kv8_write, pin_kv8_decode, pin_alibi_zero_slopes,
     pin_alibi_torch_sdpa, pin_alibi_geometric_weights, pin_alibi_partials, pin_varlen_single_tokens_are_decode,
     pin_varlen_numpy, pin_varlen_torch_sdpa, pin_varlen_prefix_means, pin_varlen_first_token_sees_one_row,

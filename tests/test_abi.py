@@ -72,7 +72,8 @@ def _decode(lib, **kw):
     (dict(es=FAKE), -1),                   # partials on the one-pass path
     (dict(ps=256), -2),                    # partition size not offered
     (dict(D=96, bs=8 * 16 * 96, hs=16 * 96, ts=96), -2),
-    (dict(B=8, W=256), -2),
+    (dict(B=64, W=32), -2),                # block sizes 8, 16 and 32 only
+    (dict(B=8, W=256, dt=0), -2),          # fp32 storage: 16-token blocks only
     (dict(Hq=128), -2),                    # group of 16 not built
     (dict(q=ctypes.c_void_p(0x10008)), -2),  # not 16-byte aligned
     (dict(ts=100), -2),                    # stride not a multiple of 16 bytes
@@ -124,7 +125,7 @@ def _decode_fp8(lib, **kw):
     (dict(dt=0), -2),                      # fp32 queries have no 8-bit kernel
     (dict(ts=72), -2),                     # byte stride not a multiple of 16
     (dict(D=96, bs=8 * 16 * 96, hs=16 * 96, ts=96), -2),
-    (dict(B=32, W=64), -2),
+    (dict(B=12, W=171), -2),
     (dict(ts=1 << 27), -2),                # 16 token rows span 2 GiB
 ])
 def test_decode_fp8_validation(lib, kw, status):

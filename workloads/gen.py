@@ -242,7 +242,8 @@ def _layout(layout: str, num_blocks: int, Hkv: int, D: int, B: int):
 # ----------------------------------------------------------------------------------
 
 def _assemble(*, name, seed, rng, dtype, Hq, Hkv, D, layout, num_blocks, seq_lens, block_tables,
-              prefix_blocks=0, pad_count=0, extra_pad_rows=0, notes="", contents=True) -> Workload:
+              prefix_blocks=0, pad_count=0, extra_pad_rows=0, notes="", contents=True,
+              block_size=BLOCK_SIZE) -> Workload:
     """Draw contents and build the write lists for given lengths and block tables.
 
     Bulk draws use streams 0 (q), 1 (K rows), 2 (V rows), 3 (new keys), 4 (new
@@ -252,7 +253,7 @@ def _assemble(*, name, seed, rng, dtype, Hq, Hkv, D, layout, num_blocks, seq_len
     """
     draw = _normal_bits if contents else (lambda seed_, stream_, shape_, dtype_, out=None:
                                            out if out is not None else np.zeros(shape_, _BITS_NP[dtype_]))
-    B = BLOCK_SIZE
+    B = block_size
     S = len(seq_lens)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     block_tables = np.ascontiguousarray(block_tables, dtype=np.int32)
@@ -346,8 +347,8 @@ def _deal(perm: np.ndarray, nblocks, width: int) -> np.ndarray:
     return table
 
 
-def _nblocks(seq_lens):
-    return [-(-int(L) // BLOCK_SIZE) for L in seq_lens]
+def _nblocks(seq_lens, block_size=BLOCK_SIZE):
+    return [-(-int(L) // block_size) for L in seq_lens]
 
 
 # ----------------------------------------------------------------------------------
@@ -442,7 +443,7 @@ def make_config(idx: int, seed: int | None = None, contents: bool = True) -> Wor
 def custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head_size: int, seq_lens,
            layout: str = "hnd", pool_factor: float = 2.0, table_width: int | None = None,
            extra_pad_rows: int = 0, pad_count: int = 0, prefix_blocks: int = 0, name: str = "custom",
-           placement=None) -> Workload:
+           placement=None, block_size: int = BLOCK_SIZE) -> Workload:
     """A workload with given lengths; blocks are a permutation of a pool
     ``pool_factor`` times the blocks needed (at least 1), dealt in order.
 
@@ -461,7 +462,7 @@ def custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head_size
         return np.random.Generator(np.random.PCG64(int(placement))).permutation(n)
 
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
-    nb = _nblocks(seq_lens)
+    nb = _nblocks(seq_lens, block_size)
     width = table_width if table_width is not None else max(max(nb) if len(nb) else 1, 1)
     if prefix_blocks:
         P = prefix_blocks
@@ -485,7 +486,8 @@ def custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head_size
         table = _deal(perm, nb, width)
     return _assemble(name=name, seed=seed, rng=rng, dtype=dtype, Hq=num_q_heads, Hkv=num_kv_heads, D=head_size,
                      layout=layout, num_blocks=num_blocks, seq_lens=seq_lens, block_tables=table,
-                     prefix_blocks=prefix_blocks, pad_count=pad_count, extra_pad_rows=extra_pad_rows)
+                     prefix_blocks=prefix_blocks, pad_count=pad_count, extra_pad_rows=extra_pad_rows,
+                     block_size=block_size)
 
 
 def fp8_variant(wl: Workload, per_head: bool = True, lo: float = 0.008, hi: float = 0.03) -> Workload:
