@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="cache element type: the query's type, or OCP E4M3 codes with per-kv-head scales")
     ap.add_argument("--alibi", action="store_true", help="add the ALiBi bias (geometric slopes, one per query head)")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
+                    help="tokens per pool block (workloads 1 and 3)")
     ap.add_argument("--varlen", choices=["prefill", "spec"], default=None,
                     help="time multi-token queries instead: a chunked-prefill step (512-token chunks) or a "
                          "speculative-decode step (4 query tokens per request)")
@@ -140,7 +142,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
-    wl = make_config(args.config)
+    wl = make_config(args.config, block_size=args.block_size)
     if args.kv == "fp8":
         wl = fp8_variant(wl)
     if args.alibi:

@@ -355,13 +355,19 @@ def _nblocks(seq_lens, block_size=BLOCK_SIZE):
 # the five named workloads
 # ----------------------------------------------------------------------------------
 
-def make_config(idx: int, seed: int | None = None, contents: bool = True) -> Workload:
+def make_config(idx: int, seed: int | None = None, contents: bool = True, block_size: int = BLOCK_SIZE) -> Workload:
     """Build named workload ``idx`` (0..4) with ``seed`` (default: ``idx``).
-    ``contents=False`` skips drawing values (lengths, tables and slots only)."""
+    ``contents=False`` skips drawing values (lengths, tables and slots only).
+    ``block_size`` (workloads 1 and 3 only) stores the same tokens in blocks of that
+    many tokens; 16 draws exactly the named workload."""
     seed = idx if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     name = CONFIG_NAMES[idx]
-    B = BLOCK_SIZE
+    B = block_size
+    if B != BLOCK_SIZE:
+        if idx not in (1, 3):
+            raise ValueError("other block sizes are offered for workloads 1 and 3")
+        name = f"{name}_b{B}"
     if idx == 0:
         # tiny MHA fp32: 2 sequences of 20 and 37 tokens, 16-block pool; both tables
         # come from one permutation (disjoint), the step writes each last token and
@@ -377,13 +383,13 @@ def make_config(idx: int, seed: int | None = None, contents: bool = True) -> Wor
         # GQA 32/8, D=128, bf16; L ~ U{512..2048}; pool = 2x the blocks needed,
         # a permutation of the pool dealt to the sequences in order.
         seq_lens = rng.integers(512, 2048, size=64, endpoint=True).astype(np.int32)
-        nb = _nblocks(seq_lens)
+        nb = _nblocks(seq_lens, B)
         N = sum(nb)
         perm = rng.permutation(2 * N)
         table = _deal(perm, nb, 2048 // B)
         return _assemble(name=name, seed=seed, rng=rng, dtype="bf16", Hq=32, Hkv=8, D=128, layout="hnd",
                          num_blocks=2 * N, seq_lens=seq_lens, block_tables=table, notes="single-pass path",
-                         contents=contents)
+                         contents=contents, block_size=B)
     if idx == 2:
         # combined K-then-V block (8 kv heads x 64 = 512 per token, bf16): a block is
         # 32 KiB, a 2 GiB pool is 65536 blocks; L ~ U{1..2048}; ids drawn without
@@ -398,12 +404,13 @@ def make_config(idx: int, seed: int | None = None, contents: bool = True) -> Wor
     if idx == 3:
         # long context: 4 x 32768 tokens, GQA 32/8, D=128, bf16, exactly 8192 blocks permuted
         seq_lens = np.full(4, 32768, dtype=np.int32)
-        nb = _nblocks(seq_lens)
-        perm = rng.permutation(8192)
+        nb = _nblocks(seq_lens, B)
+        perm = rng.permutation(sum(nb))  # exactly the blocks needed (8192 of 16 tokens)
         table = _deal(perm, nb, 32768 // B)
         return _assemble(name=name, seed=seed, rng=rng, dtype="bf16", Hq=32, Hkv=8, D=128, layout="hnd",
-                         num_blocks=8192, seq_lens=seq_lens, block_tables=table,
-                         notes="split path, 512-token partitions, then the log-sum-exp reduce", contents=contents)
+                         num_blocks=sum(nb), seq_lens=seq_lens, block_tables=table,
+                         notes="split path, 512-token partitions, then the log-sum-exp reduce", contents=contents,
+                         block_size=B)
     if idx == 4:
         # mixed serving step, fp16 MHA 32 heads x 128: L = floor(exp(U[ln 16, ln 8193)))
         # (log-uniform on [16, 8192]); a 1024-token prefix (64 blocks) is shared by all
