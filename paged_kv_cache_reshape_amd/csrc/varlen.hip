@@ -290,8 +290,339 @@ __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
+// ---- many query columns per request: K/V tiles shared through LDS --------------------
+//
+// A unit of 4 waves owns 128 (query token, head) columns -- 32 per wave, two 16-column
+// score tiles each, with the wave's own q, softmax state and accumulator -- and scans
+// the request's visible K/V once.  Tiles go by pairs: the whole workgroup loads a pair
+// of 16-token K/V tiles (each thread a fixed share of 16-byte chunks), writes it to one
+// of two LDS stages and all four waves read it, after one LDS-only barrier per pair.
+// Loads run kPipe - 1 pairs ahead in registers (so the compiler's waits on them stay
+// exact).  A pair gives each column 32 scores: one softmax update, and P.V as one
+// v_mfma_f32_16x16x32 per output tile whose contraction index k = 8 rg + i stands for
+// row 4 rg + i of the first tile (i < 4) or of the second (i >= 4) -- the same map for
+// the V^T operand and for P^T.  Chunk c of token row r is stored at slot c ^ (r mod
+// chunks-per-row), so the row-indexed 16-byte reads of K and V hit distinct banks.
+// Rows past the unit's last visible position are written as zeros (the pool there may
+// hold stale values).  A wave skips pairs that lie wholly past its columns' causal
+// limits.
+#ifndef PCACHE_VARLEN_PIPE
+#define PCACHE_VARLEN_PIPE 2
+#endif
+constexpr int kPipe = PCACHE_VARLEN_PIPE;  // tile pairs in flight per workgroup, the one being used included
+
+template <class ST, int D, int G>
+__global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void varlen_lds_kernel(VarlenArgs a) {
+  static_assert(ST::kBytes == 2, "16-bit storage only");
+  constexpr int NQ = 2;                 // 16-column score tiles per wave
+  constexpr int WC = 16 * NQ;           // columns per wave
+  constexpr int QT = kWaves * WC / G;   // query tokens per unit
+  constexpr int WT = WC / G;            // query tokens per wave
+  constexpr int KS = D / 32;
+  constexpr int DPL = D / 16;
+  constexpr int NT = DPL;
+  constexpr int CPR = D / 8;            // 16-byte chunks per token row
+  constexpr int TCH = kTok * CPR;       // chunks per K (or V) tile
+  constexpr int kThreads = kWaves * kWave;
+  constexpr int LPT = 2 * TCH / kThreads;  // chunks a thread moves per tile (K and V together)
+  static_assert(LPT >= 1 && LPT * kThreads == 2 * TCH, "a tile splits evenly over the threads");
+  using VRow = typename VRowOf<DPL>::type;
+  __shared__ __align__(16) uint4 kvs[2][2][2 * TCH];  // [stage][tile of the pair][K chunks, then V chunks]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int rg = lane >> 4;
+  const int col = lane & 15;
+
+  int64_t unit = blockIdx.x;
+  const int kvh = (int)(unit % a.num_kv_heads);
+  unit /= a.num_kv_heads;
+  const int r = (int)(unit % a.num_reqs);
+  const int chunk0 = (int)(unit / a.num_reqs);
+  const int chunks = (int)(gridDim.x / ((int64_t)a.num_kv_heads * a.num_reqs));
+
+  const int q0 = uniform_load(a.query_start_loc, r);
+  const int q1 = uniform_load(a.query_start_loc, r + 1);
+  if (q0 < 0 || q1 < q0 || (int64_t)q1 > a.total_q) return;  // no rows this request may write
+  const int n = q1 - q0;
+  const int L = uniform_load(a.seq_lens, r);
+  const bool bad_len = L < n || (int64_t)L > (int64_t)a.max_blocks_per_seq * kTok;
+  const int h0 = kvh * G;
+  const float cs = a.scale_log2;
+  const float lazy_raw = kLazyV / cs;
+  const bool alibi = a.alibi_slopes != nullptr;
+  const int32_t* table = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
+  const int64_t head_bytes = (int64_t)kvh * a.head_stride * 2;
+  const char* kpool = static_cast<const char*>(a.k_pool) + head_bytes;
+  const char* vpool = static_cast<const char*>(a.v_pool) + head_bytes;
+  const int64_t block_bytes = a.block_stride * 2;
+  const int tok_bytes = (int)(a.token_stride * 2);
+  const uint32_t tile_bytes = (uint32_t)(kTok * tok_bytes);
+
+  // this thread's chunks of a tile: linear index m = tid + j * kThreads over [K | V]
+  int g_off[LPT];   // byte offset inside the tile of the chunk the thread loads
+  int row_of[LPT];  // its token row
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int m = tid + j * kThreads;
+    const int p = m % TCH;
+    const int row = p / CPR;
+    const int slot = p % CPR;
+    row_of[j] = row;
+    g_off[j] = row * tok_bytes + 16 * (slot ^ (row & (CPR - 1)));
+  }
+
+  for (int c = chunk0; c * QT < n; c += chunks) {
+    const int i0 = c * QT;
+    const int i_end = min(n, i0 + QT);
+    const int vis_end = bad_len ? 0 : (a.causal ? L - n + i_end : L);
+    const int ntile = (vis_end + kTok - 1) / kTok;
+    bool bad = bad_len;
+
+    // this wave's columns: w * WC + 16 q + col -> query token i0 + (w WC + 16 q + col) / G
+    uint4 qb[NQ][KS];
+    int lim[NQ], pos[NQ];
+    float ab[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int cc = w * WC + 16 * q + col;
+      const int ti = i0 + cc / G;
+      const bool valid = ti < i_end;
+      const int g = cc % G;
+      pos[q] = L - n + ti;
+      lim[q] = valid ? (a.causal ? pos[q] : L - 1) : -1;
+      const int tq = valid ? ti : i_end - 1;
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + tq) * a.num_q_heads + h0 + g) * D +
+                             8 * rg;
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        qb[q][k] = valid ? *reinterpret_cast<const uint4*>(qrow + 32 * k) : make_uint4(0, 0, 0, 0);
+      ab[q] = 0.f;
+      if (alibi) {
+        float sl = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          const float v = uniform_load(a.alibi_slopes, h0 + gg);
+          sl = g == gg ? v : sl;
+        }
+        ab[q] = sl * kLog2e / cs;
+      }
+    }
+    // tiles this wave needs scores for: up to its last column's limit
+    const int w_first = i0 + w * WT;
+    const int w_last_pos = w_first >= i_end ? -1 : (a.causal ? L - n + min(i_end, w_first + WT) - 1 : L - 1);
+    const int w_tiles = bad_len || w_last_pos < 0 ? 0 : min(ntile, w_last_pos / kTok + 1);
+    // the smallest limit over this wave's columns (-1 when some column is empty): a pair
+    // wholly at or below it needs no mask
+    const int w_min_lim = (w_first + WT - 1 < i_end) ? (a.causal ? L - n + w_first : L - 1) : -1;
+
+    float m_ref[NQ], m_true[NQ], lsum[NQ];
+    f32x4_t acc[NQ][NT];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      m_ref[q] = -INFINITY;
+      m_true[q] = -INFINITY;
+      lsum[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[q][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // block id of tile t (clamped into the unit's tiles); one outside the pool turns the
+    // unit's rows to NaN and is replaced by block 0 (every thread sees the same ids)
+    auto tile_id = [&](int t) -> int {
+      const int id = uniform_load(table, min(t, ntile - 1));
+      const bool out = id < 0 || (int64_t)id >= a.num_blocks;
+      bad = bad || out;
+      return out ? 0 : id;
+    };
+    // pairs of tiles: p covers tiles 2p (rows k = 8 rg + 0..3 of the P.V contraction) and
+    // 2p + 1 (k = 8 rg + 4..7), so P.V runs on 16x16x32 matrix instructions
+    const int npair = (ntile + 1) / 2;
+    uint4 R[kPipe - 1][2][LPT];
+#define VL_FETCH(DST, ID)                                                                             \
+  do {                                                                                                \
+    const int64_t boff_ = (int64_t)(ID) * block_bytes;                                                \
+    const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, tile_bytes);                          \
+    const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                          \
+    _Pragma("unroll") for (int j = 0; j < LPT; ++j) {                                                 \
+      /* K chunks come first: a wave's chunks are all K or all V */                                   \
+      const bool isv_ = (w * kWave + j * kThreads) >= TCH;                                            \
+      DST[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(isv_ ? vr_ : kr_, g_off[j], 0, 0)); \
+    }                                                                                                 \
+  } while (0)
+
+    if (npair > 0) {
+#pragma unroll
+      for (int p = 0; p < kPipe - 1; ++p) {
+        VL_FETCH(R[p][0], tile_id(2 * p));
+        VL_FETCH(R[p][1], tile_id(2 * p + 1));
+      }
+      int ida_next = tile_id(2 * (kPipe - 1));
+      int idb_next = tile_id(2 * (kPipe - 1) + 1);
+      int p0 = 0;
+      do {  // whole turns of kPipe - 1 pairs, the exit at the bottom (exact waits on R)
+#pragma unroll
+        for (int u = 0; u < kPipe - 1; ++u) {
+          const int pr = p0 + u;  // may pass npair: then repeats of the last tile, never scored
+          uint4(*st)[2 * TCH] = kvs[pr & 1];
+          if ((2 * pr + 2) * kTok <= vis_end) {  // the whole pair is visible
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int j = 0; j < LPT; ++j) st[h][tid + j * kThreads] = R[u][h][j];
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int j = 0; j < LPT; ++j) {
+                const uint32_t keep = (2 * pr + h) * kTok + row_of[j] < vis_end ? 0xffffffffu : 0u;
+                const uint4 v = R[u][h][j];
+                st[h][tid + j * kThreads] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+              }
+          }
+          VL_FETCH(R[u][0], ida_next);
+          VL_FETCH(R[u][1], idb_next);
+          ida_next = tile_id(2 * (pr + kPipe));
+          idb_next = tile_id(2 * (pr + kPipe) + 1);
+          __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of this pair's work
+          lds_barrier();
+          if (2 * pr < w_tiles) {
+            const int tA = 2 * pr * kTok + 4 * rg;  // token of this lane's row 0 in the first tile
+            f32x4_t sc[2][NQ];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint4* Ks = st[h];
+              uint4 kk[KS];
+#pragma unroll
+              for (int k = 0; k < KS; ++k) kk[k] = Ks[col * CPR + ((4 * k + rg) ^ (col & (CPR - 1)))];
+#pragma unroll
+              for (int q = 0; q < NQ; ++q) {
+                f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < KS; ++k) c = mfma16<ST>(kk[k], qb[q][k], c);
+                sc[h][q] = c;
+              }
+            }
+            uint4 pb[NQ];
+            const bool masked = (2 * pr + 2) * kTok - 1 > w_min_lim;  // some score of the pair is masked
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+              float x[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const int tok = tA + (i < 4 ? i : kTok + i - 4);
+                float v = sc[i >> 2][q][i & 3];
+                if (alibi) v = fmaf(ab[q], (float)(tok - pos[q]), v);
+                x[i] = (!masked || tok <= lim[q]) ? v : -INFINITY;
+              }
+              const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+              m_true[q] = fmaxf(m_true[q], lm);
+              if (__builtin_amdgcn_ballot_w64(lm > m_ref[q] + lazy_raw) != 0) {
+                float hm = fmaxf(lm, __shfl_xor(lm, 16));
+                hm = fmaxf(hm, __shfl_xor(hm, 32));
+                const bool mv = hm > m_ref[q] + lazy_raw;
+                const float alpha = mv ? exp2_fast((m_ref[q] - hm) * cs) : 1.f;
+                m_ref[q] = mv ? hm : m_ref[q];
+                lsum[q] *= alpha;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[q][j] *= alpha;
+              }
+              const float ref = m_ref[q] == -INFINITY ? 0.f : m_ref[q] * cs;
+              float pr8[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) pr8[i] = exp2_fast(fmaf(x[i], cs, -ref));
+              lsum[q] += ((pr8[0] + pr8[1]) + (pr8[2] + pr8[3])) + ((pr8[4] + pr8[5]) + (pr8[6] + pr8[7]));
+              pb[q] = make_uint4(pack2<ST>(pr8[0], pr8[1]), pack2<ST>(pr8[2], pr8[3]), pack2<ST>(pr8[4], pr8[5]),
+                                 pack2<ST>(pr8[6], pr8[7]));
+            }
+            // V rows 4 rg .. 4 rg + 3 of both tiles, this lane's DPL dims (DPL * col ..)
+            VRow vv[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint4* Vs = st[h] + TCH;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int row = 4 * rg + e;
+                if constexpr (DPL == 8) {
+                  vv[h][e] = __builtin_bit_cast(VRow, Vs[row * CPR + (col ^ (row & (CPR - 1)))]);
+                } else {
+                  const uint4 ch = Vs[row * CPR + ((col >> 1) ^ (row & (CPR - 1)))];
+                  vv[h][e] = __builtin_bit_cast(VRow, (col & 1) ? make_uint2(ch.z, ch.w) : make_uint2(ch.x, ch.y));
+                }
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+              const int wj = j >> 1;
+              const uint4 va = make_uint4(__builtin_amdgcn_perm(vword(vv[0][1], wj), vword(vv[0][0], wj), sel),
+                                          __builtin_amdgcn_perm(vword(vv[0][3], wj), vword(vv[0][2], wj), sel),
+                                          __builtin_amdgcn_perm(vword(vv[1][1], wj), vword(vv[1][0], wj), sel),
+                                          __builtin_amdgcn_perm(vword(vv[1][3], wj), vword(vv[1][2], wj), sel));
+#pragma unroll
+              for (int q = 0; q < NQ; ++q) acc[q][j] = mfma16<ST>(va, pb[q], acc[q][j]);
+            }
+          }
+        }
+        p0 += kPipe - 1;
+      } while (p0 < npair);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // retire the unconsumed prefetch
+    }
+#undef VL_FETCH
+
+    // ---- this wave's columns: out = acc / sum (both relative to the same reference) -----
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float lw = lsum[q];
+      lw += __shfl_xor(lw, 16);
+      lw += __shfl_xor(lw, 32);
+      const int cc = w * WC + 16 * q + col;
+      const int ti = i0 + cc / G;
+      if (ti < i_end) {
+        const float inv = lw > 0.f ? 1.f / lw : 0.f;
+        const int64_t row = (int64_t)(q0 + ti) * a.num_q_heads + h0 + cc % G;
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + row * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // dims DPL * (4 rg + i) + j, j < DPL: contiguous
+          uint32_t packed[DPL / 2];
+#pragma unroll
+          for (int j = 0; j < DPL; j += 2) {
+            float x0 = acc[q][j][i] * inv, x1 = acc[q][j + 1][i] * inv;
+            if (bad) x0 = x1 = NAN;
+            packed[j / 2] = to_storage<ST>(x0) | (to_storage<ST>(x1) << 16);
+          }
+          uint16_t* dst = orow + DPL * (4 * rg + i);
+          if constexpr (DPL == 8)
+            *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+          else
+            *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+        }
+      }
+    }
+    lds_barrier();  // the next unit's first tile write must not overtake this unit's reads
+  }
+}
+
+template <class ST, int D, int G>
+hipError_t launch_lds_g(const VarlenArgs& a, hipStream_t stream) {
+  constexpr int QT = kWaves * 32 / G;
+  const int64_t chunks = a.max_query_len <= 0 ? 1 : (a.max_query_len + QT - 1) / QT;
+  const int64_t grid = (int64_t)a.num_kv_heads * a.num_reqs * chunks;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((varlen_lds_kernel<ST, D, G>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <class ST, int D, int G>
 hipError_t launch_g(const VarlenArgs& a, hipStream_t stream) {
+  // many columns per request: the LDS-sharing kernel; a few (speculative decode): the
+  // kernel that splits each request's K/V over the waves
+  if ((int64_t)a.max_query_len * G > 32) return launch_lds_g<ST, D, G>(a, stream);
   constexpr int NQ = 2;
   constexpr int QT = 16 * NQ / G;
   const int64_t chunks = a.max_query_len <= 0 ? 1 : (a.max_query_len + QT - 1) / QT;

@@ -49,6 +49,17 @@ def test_varlen_parity(dt, D, G, causal):
     check(out, oracle.varlen(wl, hpool, vq), f"varlen {dt} D{D} G{G} {'causal' if causal else 'full'}")
 
 
+SHORT_QLENS = [1, 2, 4, 3, 0, 4, 1]  # at most 32 (token, head) columns: the K/V-splitting kernel
+
+
+@pytest.mark.parametrize("dt,D,G", CASES, ids=[f"{a}-d{b}-g{c}" for a, b, c in CASES])
+def test_varlen_parity_short_queries(dt, D, G):
+    wl = custom(520 + D + G, dt, 2 * G, 2, D, LENS)
+    vq = varlen_variant(wl, SHORT_QLENS)
+    dpool = gh.filled_pool(wl)
+    check(gh.varlen(dpool, vq), oracle.varlen(wl, oracle.filled_pool(wl), vq), f"varlen short {dt} D{D} G{G}")
+
+
 def test_varlen_alibi():
     wl = alibi_variant(custom(510, "bf16", 16, 4, 128, LENS), np.linspace(0.25, -0.01, 16).astype(np.float32))
     vq = varlen_variant(wl, QLENS)
