@@ -41,7 +41,7 @@ struct VarlenLds {
   int bad;
 };
 
-template <class ST, int D, int G, int NQ>
+template <class ST, int D, int G, int NQ, bool ALIBI>
 __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2))) void varlen_kernel(VarlenArgs a) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
   constexpr int QC = 16 * NQ;  // (query token, head) columns per unit
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2
   const int h0 = kvh * G;
   const float cs = a.scale_log2;
   const float lazy_raw = kLazyV / cs;
-  const bool alibi = a.alibi_slopes != nullptr;
+  constexpr bool alibi = ALIBI;
   const int32_t* table = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
   const int64_t head_bytes = (int64_t)kvh * a.head_stride * 2;
   const char* kpool = static_cast<const char*>(a.k_pool) + head_bytes;
@@ -311,8 +311,55 @@ __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2
 #endif
 constexpr int kPipe = PCACHE_VARLEN_PIPE;  // tile pairs in flight per workgroup, the one being used included
 
-template <class ST, int D, int G>
-__global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2)))
+// The request of rank k when the batch's requests are ordered by history length,
+// longest first (ties by index), for every thread of the workgroup.  lens is
+// kRankMax + 1 ints of LDS; the batch has at most kRankMax requests.
+constexpr int kRankMax = 128;
+__device__ __forceinline__ int request_of_rank(const VarlenArgs& a, int k, int* lens) {
+  const int tid = threadIdx.x;
+  const int R = a.num_reqs;
+  if (tid < R) lens[tid] = a.seq_lens[tid];
+  __syncthreads();
+  if (tid < R) {
+    const int mine = lens[tid];
+    int rk = 0;
+    for (int j = 0; j < R; ++j) {
+      const int o = lens[j];
+      rk += (o > mine || (o == mine && j < tid)) ? 1 : 0;
+    }
+    if (rk == k) lens[kRankMax] = tid;  // ranks are a permutation: exactly one writer
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(lens[kRankMax]);
+}
+
+typedef short tr16x4_t __attribute__((ext_vector_type(4)));
+using lds_bytes = __attribute__((address_space(3))) char*;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives 16-bit element i % 4 of
+// the 8-byte reads of lanes i / 4 + 4 e, e = 0..3 (in that order)
+__device__ __forceinline__ uint2 lds_read_tr16(lds_bytes p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr16x4_t*)p));
+}
+
+// 16-byte chunk c of token row r sits at slot c ^ swizzle(r) of its LDS row.  K rows are
+// read one row per lane (16 rows at once): r mod CPR spreads them over the banks.  V rows
+// are read transposed, four lanes per row and four rows per 16 lanes; for 256-byte rows
+// those rows need swizzles two slots apart (128-byte rows already fall on both halves of
+// the banks).
+template <int CPR>
+__device__ __forceinline__ int k_swizzle(int r) { return r & (CPR - 1); }
+template <int CPR>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return CPR == 16 ? ((2 * r + (r >> 3)) & 15) : (r & (CPR - 1));
+}
+
+#ifndef PCACHE_VARLEN_WPE
+#define PCACHE_VARLEN_WPE 2
+#endif
+
+template <class ST, int D, int G, bool ALIBI>
+__global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_VARLEN_WPE)))
 void varlen_lds_kernel(VarlenArgs a) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
   constexpr int NQ = 2;                 // 16-column score tiles per wave
@@ -320,15 +367,14 @@ void varlen_lds_kernel(VarlenArgs a) {
   constexpr int QT = kWaves * WC / G;   // query tokens per unit
   constexpr int WT = WC / G;            // query tokens per wave
   constexpr int KS = D / 32;
-  constexpr int DPL = D / 16;
-  constexpr int NT = DPL;
+  constexpr int NT = D / 16;            // output tiles of 16 dims
   constexpr int CPR = D / 8;            // 16-byte chunks per token row
   constexpr int TCH = kTok * CPR;       // chunks per K (or V) tile
   constexpr int kThreads = kWaves * kWave;
   constexpr int LPT = 2 * TCH / kThreads;  // chunks a thread moves per tile (K and V together)
   static_assert(LPT >= 1 && LPT * kThreads == 2 * TCH, "a tile splits evenly over the threads");
-  using VRow = typename VRowOf<DPL>::type;
   __shared__ __align__(16) uint4 kvs[2][2][2 * TCH];  // [stage][tile of the pair][K chunks, then V chunks]
+  __shared__ int rank_lens[kRankMax + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -336,12 +382,18 @@ void varlen_lds_kernel(VarlenArgs a) {
   const int rg = lane >> 4;
   const int col = lane & 15;
 
+  // units go request by request -- the longest history first when the batch is small
+  // enough to rank here -- and within a request from its last chunk (the most visible
+  // K/V) down: long units start first and short ones fill the tail.  The kv head is the
+  // fastest index, so all chunks of one (request, kv head) land on the same XCD (and L2)
+  // whenever the number of kv heads is a multiple of 8.
   int64_t unit = blockIdx.x;
   const int kvh = (int)(unit % a.num_kv_heads);
   unit /= a.num_kv_heads;
-  const int r = (int)(unit % a.num_reqs);
-  const int chunk0 = (int)(unit / a.num_reqs);
   const int chunks = (int)(gridDim.x / ((int64_t)a.num_kv_heads * a.num_reqs));
+  const int c = chunks - 1 - (int)(unit % chunks);
+  const int rank = (int)(unit / chunks);
+  const int r = a.num_reqs <= kRankMax ? request_of_rank(a, rank, rank_lens) : rank;
 
   const int q0 = uniform_load(a.query_start_loc, r);
   const int q1 = uniform_load(a.query_start_loc, r + 1);
@@ -352,7 +404,7 @@ void varlen_lds_kernel(VarlenArgs a) {
   const int h0 = kvh * G;
   const float cs = a.scale_log2;
   const float lazy_raw = kLazyV / cs;
-  const bool alibi = a.alibi_slopes != nullptr;
+  constexpr bool alibi = ALIBI;
   const int32_t* table = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
   const int64_t head_bytes = (int64_t)kvh * a.head_stride * 2;
   const char* kpool = static_cast<const char*>(a.k_pool) + head_bytes;
@@ -364,17 +416,30 @@ void varlen_lds_kernel(VarlenArgs a) {
   // this thread's chunks of a tile: linear index m = tid + j * kThreads over [K | V]
   int g_off[LPT];   // byte offset inside the tile of the chunk the thread loads
   int row_of[LPT];  // its token row
+  const char* src[LPT];  // K or V pool (a wave's chunks are all K or all V)
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
     const int m = tid + j * kThreads;
+    const bool is_v = (w * kWave + j * kThreads) >= TCH;
+    src[j] = is_v ? vpool : kpool;
     const int p = m % TCH;
     const int row = p / CPR;
     const int slot = p % CPR;
     row_of[j] = row;
-    g_off[j] = row * tok_bytes + 16 * (slot ^ (row & (CPR - 1)));
+    g_off[j] = row * tok_bytes + 16 * (slot ^ (is_v ? v_swizzle<CPR>(row) : k_swizzle<CPR>(row)));
+  }
+  // this lane's transposed V reads: row 4 rg + col / 4, dims 16 j + 4 (col % 4) .. + 3,
+  // so that it receives dims 16 j + col of rows 4 rg .. 4 rg + 3 (the V^T operand)
+  int v_rd[NT];
+  {
+    const int row = 4 * rg + (col >> 2);
+    const int c4 = col & 3;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) v_rd[j] = 16 * (TCH + row * CPR + ((2 * j + (c4 >> 1)) ^ v_swizzle<CPR>(row))) + 8 * (c4 & 1);
   }
 
-  for (int c = chunk0; c * QT < n; c += chunks) {
+  const uint32_t nb_lim = (uint32_t)min(a.num_blocks, (int64_t)0x7fffffff);
+  if (c * QT < n) {
     const int i0 = c * QT;
     const int i_end = min(n, i0 + QT);
     const int vis_end = bad_len ? 0 : (a.causal ? L - n + i_end : L);
@@ -418,12 +483,15 @@ void varlen_lds_kernel(VarlenArgs a) {
     // wholly at or below it needs no mask
     const int w_min_lim = (w_first + WT - 1 < i_end) ? (a.causal ? L - n + w_first : L - 1) : -1;
 
-    float m_ref[NQ], m_true[NQ], lsum[NQ];
+    // per column: the exponent reference m_ref, the max that moves it (m_ref + slack) and
+    // the offset -m_ref * cs (0 while nothing is visible), updated only when it moves
+    float m_ref[NQ], thr[NQ], noff[NQ], lsum[NQ];
     f32x4_t acc[NQ][NT];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       m_ref[q] = -INFINITY;
-      m_true[q] = -INFINITY;
+      thr[q] = -INFINITY;
+      noff[q] = 0.f;
       lsum[q] = 0.f;
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[q][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -433,7 +501,7 @@ void varlen_lds_kernel(VarlenArgs a) {
     // unit's rows to NaN and is replaced by block 0 (every thread sees the same ids)
     auto tile_id = [&](int t) -> int {
       const int id = uniform_load(table, min(t, ntile - 1));
-      const bool out = id < 0 || (int64_t)id >= a.num_blocks;
+      const bool out = (uint32_t)id >= nb_lim;  // negative ids too
       bad = bad || out;
       return out ? 0 : id;
     };
@@ -444,12 +512,9 @@ void varlen_lds_kernel(VarlenArgs a) {
 #define VL_FETCH(DST, ID)                                                                             \
   do {                                                                                                \
     const int64_t boff_ = (int64_t)(ID) * block_bytes;                                                \
-    const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, tile_bytes);                          \
-    const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                          \
     _Pragma("unroll") for (int j = 0; j < LPT; ++j) {                                                 \
-      /* K chunks come first: a wave's chunks are all K or all V */                                   \
-      const bool isv_ = (w * kWave + j * kThreads) >= TCH;                                            \
-      DST[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(isv_ ? vr_ : kr_, g_off[j], 0, 0)); \
+      const __amdgpu_buffer_rsrc_t r_ = tile_rsrc(src[j] + boff_, tile_bytes);                        \
+      DST[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_, g_off[j], 0, 0));   \
     }                                                                                                 \
   } while (0)
 
@@ -505,63 +570,56 @@ void varlen_lds_kernel(VarlenArgs a) {
                 sc[h][q] = c;
               }
             }
-            uint4 pb[NQ];
-            const bool masked = (2 * pr + 2) * kTok - 1 > w_min_lim;  // some score of the pair is masked
+            // score i of a lane: tile i / 4, row 4 rg + i % 4 -> token tA + (i < 4 ? i : 12 + i)
+            float xs[NQ][8];
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-              float x[8];
+            for (int q = 0; q < NQ; ++q)
 #pragma unroll
               for (int i = 0; i < 8; ++i) {
-                const int tok = tA + (i < 4 ? i : kTok + i - 4);
                 float v = sc[i >> 2][q][i & 3];
-                if (alibi) v = fmaf(ab[q], (float)(tok - pos[q]), v);
-                x[i] = (!masked || tok <= lim[q]) ? v : -INFINITY;
+                if (alibi) v = fmaf(ab[q], (float)(tA + (i < 4 ? i : kTok + i - 4) - pos[q]), v);
+                xs[q][i] = v;
               }
+            if ((2 * pr + 2) * kTok - 1 > w_min_lim) {  // some score of the pair is masked (uniform)
+#pragma unroll
+              for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                  xs[q][i] = tA + (i < 4 ? i : kTok + i - 4) <= lim[q] ? xs[q][i] : -INFINITY;
+            }
+            uint4 pb[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+              const float* x = xs[q];
               const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                                      fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-              m_true[q] = fmaxf(m_true[q], lm);
-              if (__builtin_amdgcn_ballot_w64(lm > m_ref[q] + lazy_raw) != 0) {
+              if (__builtin_amdgcn_ballot_w64(lm > thr[q]) != 0) {
                 float hm = fmaxf(lm, __shfl_xor(lm, 16));
                 hm = fmaxf(hm, __shfl_xor(hm, 32));
-                const bool mv = hm > m_ref[q] + lazy_raw;
+                const bool mv = hm > thr[q];
                 const float alpha = mv ? exp2_fast((m_ref[q] - hm) * cs) : 1.f;
                 m_ref[q] = mv ? hm : m_ref[q];
+                thr[q] = m_ref[q] + lazy_raw;
+                noff[q] = m_ref[q] == -INFINITY ? 0.f : -m_ref[q] * cs;
                 lsum[q] *= alpha;
 #pragma unroll
                 for (int j = 0; j < NT; ++j) acc[q][j] *= alpha;
               }
-              const float ref = m_ref[q] == -INFINITY ? 0.f : m_ref[q] * cs;
               float pr8[8];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) pr8[i] = exp2_fast(fmaf(x[i], cs, -ref));
+              for (int i = 0; i < 8; ++i) pr8[i] = exp2_fast(fmaf(x[i], cs, noff[q]));
               lsum[q] += ((pr8[0] + pr8[1]) + (pr8[2] + pr8[3])) + ((pr8[4] + pr8[5]) + (pr8[6] + pr8[7]));
               pb[q] = make_uint4(pack2<ST>(pr8[0], pr8[1]), pack2<ST>(pr8[2], pr8[3]), pack2<ST>(pr8[4], pr8[5]),
                                  pack2<ST>(pr8[6], pr8[7]));
             }
-            // V rows 4 rg .. 4 rg + 3 of both tiles, this lane's DPL dims (DPL * col ..)
-            VRow vv[2][4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const uint4* Vs = st[h] + TCH;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int row = 4 * rg + e;
-                if constexpr (DPL == 8) {
-                  vv[h][e] = __builtin_bit_cast(VRow, Vs[row * CPR + (col ^ (row & (CPR - 1)))]);
-                } else {
-                  const uint4 ch = Vs[row * CPR + ((col >> 1) ^ (row & (CPR - 1)))];
-                  vv[h][e] = __builtin_bit_cast(VRow, (col & 1) ? make_uint2(ch.z, ch.w) : make_uint2(ch.x, ch.y));
-                }
-              }
-            }
+            // output tile j = dims 16 j .. 16 j + 15; its V^T operand (k = 8 rg + 0..3 from
+            // the first tile, + 4..7 from the second) comes straight from LDS, transposed
+            const lds_bytes sb = (lds_bytes)st[0];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-              const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-              const int wj = j >> 1;
-              const uint4 va = make_uint4(__builtin_amdgcn_perm(vword(vv[0][1], wj), vword(vv[0][0], wj), sel),
-                                          __builtin_amdgcn_perm(vword(vv[0][3], wj), vword(vv[0][2], wj), sel),
-                                          __builtin_amdgcn_perm(vword(vv[1][1], wj), vword(vv[1][0], wj), sel),
-                                          __builtin_amdgcn_perm(vword(vv[1][3], wj), vword(vv[1][2], wj), sel));
+              const uint2 lo = lds_read_tr16(sb + v_rd[j]);
+              const uint2 hi = lds_read_tr16(sb + 2 * TCH * 16 + v_rd[j]);
+              const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
               for (int q = 0; q < NQ; ++q) acc[q][j] = mfma16<ST>(va, pb[q], acc[q][j]);
             }
@@ -586,24 +644,16 @@ void varlen_lds_kernel(VarlenArgs a) {
         const int64_t row = (int64_t)(q0 + ti) * a.num_q_heads + h0 + cc % G;
         uint16_t* orow = static_cast<uint16_t*>(a.out) + row * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // dims DPL * (4 rg + i) + j, j < DPL: contiguous
-          uint32_t packed[DPL / 2];
+        for (int j = 0; j < NT; ++j) {
+          // dims 16 j + 4 rg + i, i < 4: contiguous
+          float x[4];
 #pragma unroll
-          for (int j = 0; j < DPL; j += 2) {
-            float x0 = acc[q][j][i] * inv, x1 = acc[q][j + 1][i] * inv;
-            if (bad) x0 = x1 = NAN;
-            packed[j / 2] = to_storage<ST>(x0) | (to_storage<ST>(x1) << 16);
-          }
-          uint16_t* dst = orow + DPL * (4 * rg + i);
-          if constexpr (DPL == 8)
-            *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-          else
-            *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+          for (int i = 0; i < 4; ++i) x[i] = bad ? NAN : acc[q][j][i] * inv;
+          *reinterpret_cast<uint2*>(orow + 16 * j + 4 * rg) =
+              make_uint2(to_storage<ST>(x[0]) | (to_storage<ST>(x[1]) << 16), to_storage<ST>(x[2]) | (to_storage<ST>(x[3]) << 16));
         }
       }
     }
-    lds_barrier();  // the next unit's first tile write must not overtake this unit's reads
   }
 }
 
@@ -614,7 +664,10 @@ hipError_t launch_lds_g(const VarlenArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.num_kv_heads * a.num_reqs * chunks;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((varlen_lds_kernel<ST, D, G>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a);
+  if (a.alibi_slopes)
+    hipLaunchKernelGGL((varlen_lds_kernel<ST, D, G, true>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((varlen_lds_kernel<ST, D, G, false>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -629,7 +682,10 @@ hipError_t launch_g(const VarlenArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.num_kv_heads * a.num_reqs * chunks;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((varlen_kernel<ST, D, G, NQ>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a);
+  if (a.alibi_slopes)
+    hipLaunchKernelGGL((varlen_kernel<ST, D, G, NQ, true>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((varlen_kernel<ST, D, G, NQ, false>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -60,11 +60,32 @@ def test_varlen_parity_short_queries(dt, D, G):
     check(gh.varlen(dpool, vq), oracle.varlen(wl, oracle.filled_pool(wl), vq), f"varlen short {dt} D{D} G{G}")
 
 
-def test_varlen_alibi():
-    wl = alibi_variant(custom(510, "bf16", 16, 4, 128, LENS), np.linspace(0.25, -0.01, 16).astype(np.float32))
-    vq = varlen_variant(wl, QLENS)
+@pytest.mark.parametrize("R", [8, 128, 130])
+def test_varlen_dispatch_order(R):
+    """Workgroups take requests longest history first (ranked inside the kernel up to 128
+    requests, in index order past that): with tied lengths and either side of that
+    bound, every request's rows are still computed exactly once."""
+    rng = np.random.default_rng(530 + R)
+    if R == 8:
+        lens = np.array([300, 40, 300, 300, 17, 40, 300, 5])
+    else:
+        lens = rng.choice([24, 64, 65, 150], size=R)  # many ties
+    qlens = np.minimum(lens, rng.integers(1, 25, size=R))
+    qlens[0] = min(lens[0], 24)                       # 24 tokens x 4 heads: the LDS-sharing kernel
+    wl = custom(530 + R, "bf16", 16, 4, 128, lens.tolist())
+    vq = varlen_variant(wl, qlens.astype(np.int32))
     dpool = gh.filled_pool(wl)
-    check(gh.varlen(dpool, vq), oracle.varlen(wl, oracle.filled_pool(wl), vq), "varlen + ALiBi")
+    check(gh.varlen(dpool, vq), oracle.varlen(wl, oracle.filled_pool(wl), vq), f"varlen order R{R}")
+
+
+@pytest.mark.parametrize("qlens", ["long", "short"])
+def test_varlen_alibi(qlens):
+    """The bias on both kernels: long queries (K/V shared through LDS) and at most 32
+    (token, head) columns per request (K/V split over the waves)."""
+    wl = alibi_variant(custom(510, "bf16", 16, 4, 128, LENS), np.linspace(0.25, -0.01, 16).astype(np.float32))
+    vq = varlen_variant(wl, QLENS if qlens == "long" else SHORT_QLENS)
+    dpool = gh.filled_pool(wl)
+    check(gh.varlen(dpool, vq), oracle.varlen(wl, oracle.filled_pool(wl), vq), f"varlen + ALiBi, {qlens} queries")
 
 
 def test_varlen_single_tokens_match_decode():
