@@ -297,8 +297,8 @@ __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2
 // the request's visible K/V once.  Tiles go by pairs: the whole workgroup loads a pair
 // of 16-token K/V tiles (each thread a fixed share of 16-byte chunks), writes it to one
 // of two LDS stages and all four waves read it, after one LDS-only barrier per pair.
-// Loads run kPipe - 1 pairs ahead in registers (so the compiler's waits on them stay
-// exact).  A pair gives each column 32 scores: one softmax update, and P.V as one
+// Loads run kPipe - 1 = 2 pairs ahead in registers (so the compiler's waits on them stay
+// exact); one pair ahead leaves the LDS writes waiting on the loads.  A pair gives each column 32 scores: one softmax update, and P.V as one
 // v_mfma_f32_16x16x32 per output tile whose contraction index k = 8 rg + i stands for
 // row 4 rg + i of the first tile (i < 4) or of the second (i >= 4) -- the same map for
 // the V^T operand and for P^T.  Chunk c of token row r is stored at slot c ^ (r mod
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2
 // hold stale values).  A wave skips pairs that lie wholly past its columns' causal
 // limits.
 #ifndef PCACHE_VARLEN_PIPE
-#define PCACHE_VARLEN_PIPE 2
+#define PCACHE_VARLEN_PIPE 3
 #endif
 constexpr int kPipe = PCACHE_VARLEN_PIPE;  // tile pairs in flight per workgroup, the one being used included
 
