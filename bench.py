@@ -41,7 +41,7 @@ for p in (REPO, os.path.join(REPO, "tests")):
 
 METRIC = "paged decode attention effective GB/s and % of MI355X HBM peak; tokens/s"
 HBM_PEAK_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(REPO, "profiles", "decode_traffic.json")
+PROFILE_TRAFFIC = os.path.join(REPO, "profiles", "hbm_traffic.json")
 
 
 def parse():
@@ -68,25 +68,34 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+# the sources each family of kernels is built from: a change to any of them voids the
+# counters recorded for that family
+KERNEL_SOURCES = {
+    "decode": ("api.hip", "decode.hip", "decode_mfma.hip", "reduce.hip", "device_common.h", "launch.h",
+               "mfma_common.h"),
+    "varlen": ("api.hip", "varlen.hip", "device_common.h", "launch.h", "mfma_common.h"),
+}
+
+
+def kernel_source_hash(family: str = "decode") -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(REPO, "paged_kv_cache_reshape_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(KERNEL_SOURCES[family]):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+def stored_traffic(workload: str, family: str = "decode"):
+    """HBM bytes per launch of a workload's dominant kernel from committed rocprofv3
+    counter runs, if they were taken on the current sources of that kernel; else None."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(family):
         return None
     return rec.get("bytes_per_launch")
 
@@ -378,13 +387,15 @@ def bench_varlen(args):
         metric, unit, value = "varlen chunked-prefill attention query tokens/s", "tokens/s", toks
         achieved = flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s",
-                "frac": round(achieved / 2500.0, 4), "traffic": None, "kernel": "varlen_kernel",
+                "frac": round(achieved / 2500.0, 4), "traffic": stored_traffic(wl.name, "varlen"),
+                "kernel": "varlen_lds_kernel",
                 "flops_per_launch": flops, "launch_us": round(kern_ms * 1e3, 2)}
     else:
         metric, unit, value = "varlen speculative-decode attention effective GB/s", "GB/s", (kv + qo) / (ms * 1e-3) / 1e9
         achieved = (kv + qo) / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "varlen_kernel",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(wl.name, "varlen"),
+                "kernel": "varlen_kernel",
                 "bytes_per_launch": kv + qo, "launch_us": round(kern_ms * 1e3, 2)}
     roof["timing"] = "HIP events around back-to-back launches on the launch stream"
     res = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
