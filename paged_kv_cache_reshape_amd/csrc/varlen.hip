@@ -439,8 +439,10 @@ void varlen_lds_kernel(VarlenArgs a) {
   }
 
   const uint32_t nb_lim = (uint32_t)min(a.num_blocks, (int64_t)0x7fffffff);
-  if (c * QT < n) {
-    const int i0 = c * QT;
+  // chunk c, then any chunks that a grid sized from an understated max_query_len left
+  for (int cu = c; cu * QT < n; cu += chunks) {
+    if (cu != c) lds_barrier();  // every wave is done with the previous chunk's tiles
+    const int i0 = cu * QT;
     const int i_end = min(n, i0 + QT);
     const int vis_end = bad_len ? 0 : (a.causal ? L - n + i_end : L);
     const int ntile = (vis_end + kTok - 1) / kTok;

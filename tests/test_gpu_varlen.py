@@ -120,12 +120,15 @@ def test_varlen_chunked_prefill_step():
     check(gh.varlen(dpool, vq), oracle.varlen(wl, hpool, vq), "chunked prefill step")
 
 
-def test_varlen_understated_max_query_len():
-    """A request longer than max_query_len is still computed in full."""
+@pytest.mark.parametrize("mql", [8, 16])
+def test_varlen_understated_max_query_len(mql):
+    """A request longer than max_query_len is still computed in full (8 x 4 columns: the
+    K/V-splitting kernel; 16 x 4: the LDS-sharing kernel, whose grid then holds one
+    32-token chunk per request for a 90-token query)."""
     wl = custom(513, "f16", 8, 2, 64, [100, 300])
     vq = varlen_variant(wl, [90, 7])
     dpool = gh.filled_pool(wl)
-    check(gh.varlen(dpool, vq, max_query_len=8), oracle.varlen(wl, oracle.filled_pool(wl), vq), "short grid")
+    check(gh.varlen(dpool, vq, max_query_len=mql), oracle.varlen(wl, oracle.filled_pool(wl), vq), f"short grid {mql}")
 
 
 def test_varlen_bad_request_is_nan_only_there():
