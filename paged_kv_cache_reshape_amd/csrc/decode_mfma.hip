@@ -110,11 +110,11 @@ constexpr int onepass_waves() {
 #define PCACHE_SPLIT_STAGES_KV8 2
 #endif
 
-template <int NW, int D, int G, int TABLE>
+template <int NW, int D, int NC, int TABLE>
 struct UnitLds {
-  __align__(16) float acc[NW][G][D];  // each wave's scaled accumulator
-  float mw[NW][G];
-  float lw[NW][G];
+  __align__(16) float acc[NW][NC][D];  // each wave's scaled accumulator, per score column
+  float mw[NW][NC];
+  float lw[NW][NC];
   int ids[TABLE];  // block ids of the unit's current chunk
   int bad;         // some id of the unit lies outside the pool
 };
@@ -123,14 +123,20 @@ struct UnitLds {
 // One unit: kv head `kvh` of sequence `s`, tokens [t_begin, t_end).  All waves of
 // the workgroup call it together (it uses block-wide barriers).  Writes out (one
 // pass) or the partition's partials (split).  KV8: the pool holds E4M3 codes.
-template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT, bool KV8, int BS>
-__device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, G, TABLE>& sm, int s, int kvh,
-                                            int part) {
+// Score columns: NC = G is the decode (column c = query head h0 + c of the sequence's
+// one token).  NC = 16 > G takes several query tokens per sequence (query_start_loc):
+// column c = token tok0 + c / G, head h0 + c % G, each with its own causal limit; the
+// call covers tokens tok0 .. tok0 + 16/G - 1 and returns whether more remain.
+template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT, bool KV8, int BS, int NC = G>
+__device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, NC, TABLE>& sm, int s, int kvh,
+                                            int part, int tok0 = 0) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
   static_assert(D == 64 || D == 128, "head size 64 or 128");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group of 1, 2, 4 or 8 query heads");
   static_assert(STAGES >= 2 && STAGES <= 4, "prefetch ring of 2..4 register sets");
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size 8, 16 or 32");
+  constexpr bool MT = NC != G;  // several query tokens per sequence
+  static_assert(NC == G || (NC == 16 && !SPLIT && !KV8), "multi-token units: one pass, 16-bit pools");
   // tiles per staged chunk: the chunk's block ids must fit the TABLE entries
   constexpr int CT = BS >= 16 ? TABLE * (BS / 16) : TABLE / (16 / BS);
   static_assert(!SPLIT || CT >= kPartition / kBlockTokens, "a partition's ids fit the table");
@@ -150,13 +156,29 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const int col = lane & 15;  // score column: query head of the group
 
   const int L = uniform_load(a.seq_lens, s);
+  // the sequence's query rows: q0 .. q0 + n - 1 (the decode: row s alone)
+  int q0 = s, n = 1;
+  if constexpr (MT) {
+    q0 = uniform_load(a.query_start_loc, s);
+    const int q1 = uniform_load(a.query_start_loc, s + 1);
+    if (q0 < 0 || q1 < q0 || (int64_t)q1 > a.total_q) return false;  // no rows this sequence may write
+    n = q1 - q0;
+    if (tok0 >= n) return false;
+  }
+  constexpr int TPC = NC / G;                      // query tokens per call
+  const int C = MT ? min(n - tok0, TPC) * G : G;   // score columns in use
+  const int ci = MT ? tok0 + col / G : 0;          // this lane's query token
+  // the column's own position (the ALiBi origin) and last visible position
+  const int qpos = MT ? L - n + ci : L - 1;
+  const int lim = (MT && !a.causal) ? L - 1 : qpos;
+  const int min_lim = (MT && a.causal) ? L - n + tok0 : L - 1;  // smallest over the call's columns
   // 8-bit pool: the kv head's dequantisation scales (k_scale folded into the score scale)
   const float ksc = KV8 ? uniform_load(a.k_scale, (int64_t)kvh * a.scale_stride) : 1.f;
   const float vsc = KV8 ? uniform_load(a.v_scale, (int64_t)kvh * a.scale_stride) : 1.f;
   const float cs_raw = a.scale_log2 * ksc;
   const bool bad_scale = KV8 && !(cs_raw >= 0x1p-120f && cs_raw <= 0x1p120f && vsc > 0.f && vsc <= 3.4e38f);
   bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * BS ||
-             (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition) || bad_scale;
+             (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition) || bad_scale || (MT && L < n);
   const int t_begin = SPLIT ? part * kPartition : 0;
   const int t_end = bad ? t_begin : (SPLIT ? min(L, t_begin + kPartition) : L);
   const int b_begin = t_begin / kBlockTokens;
@@ -165,16 +187,18 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const float cs = bad_scale ? 1.f : cs_raw;  // > 0 (scale validated on the host, k_scale here)
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
-  // B operand: query head `col` (zero for col >= G), dims 32*k + 8*rg .. +8 (16-bit
+  // B operand: column `col` (zero for col >= C), dims 32*k + 8*rg .. +8 (16-bit
   // pool) or rg*(D/4) + 8*k .. +8 (8-bit pool, the order its K rows are read in)
   uint4 qb[KS];
   {
-    const int qh = col < G ? col : G - 1;  // keep the address inside q for the zero columns
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.num_q_heads + h0 + qh) * D +
+    // keep the address inside q for the zero columns
+    const int qc = col < C ? col : C - 1;
+    const int64_t qr = MT ? (int64_t)(q0 + tok0 + qc / G) : (int64_t)s;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (qr * a.num_q_heads + h0 + (qc & (G - 1))) * D +
                            (KV8 ? rg * (D / 4) : 8 * rg);
 #pragma unroll
     for (int k = 0; k < KS; ++k)
-      qb[k] = col < G ? *reinterpret_cast<const uint4*>(qrow + (KV8 ? 8 : 32) * k) : make_uint4(0, 0, 0, 0);
+      qb[k] = col < C ? *reinterpret_cast<const uint4*>(qrow + (KV8 ? 8 : 32) * k) : make_uint4(0, 0, 0, 0);
   }
 
   // softmax state of head `col` (meaningful for col < G): the four row-group lanes
@@ -207,11 +231,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float sg = uniform_load(a.alibi_slopes, h0 + g);
-      slope = col == g ? sg : slope;
+      slope = (col & (G - 1)) == g ? sg : slope;
     }
   }
   float ab = 0.f;
-  const int last_pos = L - 1;
+  const int last_pos = qpos;  // the bias is zero at the column's own position
 
   uint4 kb[STAGES][KS];  // 16-bit pool ring
   VRow vb[STAGES][4];
@@ -283,10 +307,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       _Pragma("unroll") for (int e = 0; e < 4; ++e) c[e] = fmaf(ab, (float)(d0_ + e), c[e]);        \
     }                                                                                                \
     const int visible = t_end - (TOK0);                                                              \
-    if (visible < kBlockTokens) {                                                                    \
+    if (visible < kBlockTokens || (MT && (TOK0) + kBlockTokens - 1 > min_lim)) {                     \
       _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                               \
         const bool keep = 4 * rg + e < visible;                                                      \
-        c[e] = keep ? c[e] : -INFINITY;                                                              \
+        const bool seen = !MT || (TOK0) + 4 * rg + e <= lim; /* the column's causal limit */         \
+        c[e] = keep && seen ? c[e] : -INFINITY;                                                      \
         if constexpr (KV8)                                                                           \
           vq[SL][e] = keep ? vq[SL][e] : VRow8{};                                                    \
         else                                                                                         \
@@ -295,7 +320,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     }                                                                                                \
     const float lm = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));                                    \
     m_true = fmaxf(m_true, lm);                                                                      \
-    if (__builtin_amdgcn_ballot_w64(col < G && lm > m_ref + lazy_raw) != 0) {                        \
+    if (__builtin_amdgcn_ballot_w64(col < C && lm > m_ref + lazy_raw) != 0) {                        \
       float hm = fmaxf(lm, __shfl_xor(lm, 16));                                                      \
       hm = fmaxf(hm, __shfl_xor(hm, 32));                                                            \
       const bool mv = hm > m_ref + lazy_raw;                                                         \
@@ -427,7 +452,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   float lw = lsum;
   lw += __shfl_xor(lw, 16);
   lw += __shfl_xor(lw, 32);
-  if (col < G) {
+  if (col < C) {
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -441,24 +466,52 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 
   // ---- merge the waves and write ------------------------------------------------------
   const bool any_bad = bad;  // block-uniform (the table check is a block-wide vote)
-  for (int o = tid; o < G * D; o += kThreads) {
-    const int g = o / D;
-    const int d = o - g * D;
-    float M = -INFINITY;
+  if constexpr (MT) {
+    // 16 columns: per column, once (one thread each), the max M over the waves, each
+    // wave's weight exp2((m_w - M) cs) in place of m_w, the merged sum in place of
+    // wave 0's and M in place of wave 1's (both read just before)
+    static_assert(NW > 1, "the merge keeps M in lw[1]");
+    for (int g = tid; g < C; g += kThreads) {
+      float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm.mw[ww][g]);
-    float ls = 0.f, os = 0.f;
-    if (M != -INFINITY) {
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm.mw[ww][g]);
+      float ls = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
-        const float fw = sm.mw[ww][g] == -INFINITY ? 0.f : exp2_fast((sm.mw[ww][g] - M) * cs);
+        const float fw = (M == -INFINITY || sm.mw[ww][g] == -INFINITY) ? 0.f : exp2_fast((sm.mw[ww][g] - M) * cs);
         ls = fmaf(sm.lw[ww][g], fw, ls);
-        os = fmaf(sm.acc[ww][g][d], fw, os);
+        sm.mw[ww][g] = fw;
+      }
+      sm.lw[0][g] = ls;
+      sm.lw[1][g] = M;
+    }
+    __syncthreads();
+  }
+  for (int o = tid; o < C * D; o += kThreads) {
+    const int g = o / D;  // score column
+    const int d = o - g * D;
+    float M = -INFINITY, ls = 0.f, os = 0.f;
+    if constexpr (MT) {
+      M = sm.lw[1][g];
+      ls = sm.lw[0][g];
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) os = fmaf(sm.acc[ww][g][d], sm.mw[ww][g], os);
+    } else {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm.mw[ww][g]);
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          const float fw = sm.mw[ww][g] == -INFINITY ? 0.f : exp2_fast((sm.mw[ww][g] - M) * cs);
+          ls = fmaf(sm.lw[ww][g], fw, ls);
+          os = fmaf(sm.acc[ww][g][d], fw, os);
+        }
       }
     }
     float res = M == -INFINITY ? 0.f : os / ls * vsc;
     if (any_bad) res = NAN;
-    const int64_t sh = (int64_t)s * a.num_q_heads + h0 + g;
+    const int64_t sh = MT ? (int64_t)(q0 + tok0 + g / G) * a.num_q_heads + h0 + (g & (G - 1))
+                          : (int64_t)s * a.num_q_heads + h0 + g;
     if constexpr (SPLIT) {
       const int64_t sp = sh * a.max_partitions + part;
       a.tmp_out[sp * D + d] = res;
@@ -470,6 +523,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       static_cast<uint16_t*>(a.out)[sh * D + d] = (uint16_t)to_storage<ST>(res);
     }
   }
+  return MT && tok0 + TPC < n;
 }
 
 // Split path: workgroup = (kv head, sequence, partition), fastest-varying first.
@@ -497,14 +551,15 @@ void decode_split_kernel(DecodeArgs a) {
 // first loads.  While round 0 runs, the sequence lengths are fetched; after it, the
 // remaining units are ranked longest first and dealt in snake order, and the workgroup
 // whose round-0 unit was the r-th longest receives the r-th shortest unit of round 1,
-// which evens out the sums across workgroups.
-template <class ST, int D, int G, bool KV8, int BS>
+// which evens out the sums across workgroups.  NC > G: several query tokens per
+// sequence, in passes of NC / G tokens (one pass unless max_query_len was understated).
+template <class ST, int D, int G, bool KV8, int BS, int NC = G>
 __global__ __launch_bounds__(onepass_waves<D>() * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_ONEPASS_OCC)))
 void decode_onepass_kernel(DecodeArgs a) {
   constexpr int NW = onepass_waves<D>();
   constexpr int kThreads = NW * kWave;
   constexpr int STAGES = KV8 ? PCACHE_ONEPASS_STAGES_KV8 : PCACHE_ONEPASS_STAGES;
-  __shared__ UnitLds<NW, D, G, PCACHE_ONEPASS_TABLE> sm;
+  __shared__ UnitLds<NW, D, NC, PCACHE_ONEPASS_TABLE> sm;
   __shared__ int order_lds[kMaxRankedSeqs];  // order_lds[rank] = later-round sequence of that length rank
   __shared__ int len_lds[kMaxRankedSeqs];
   __shared__ int rank0_lds;                  // length rank of this workgroup's round-0 sequence
@@ -520,8 +575,12 @@ void decode_onepass_kernel(DecodeArgs a) {
   if (ranked)  // read here, used after round 0 (its barriers publish the stores)
     for (int t = threadIdx.x; t < S; t += kThreads) len_lds[t] = a.seq_lens[t];
 
-  if (k < units) decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8, BS>(a, sm, (int)(k / Hkv),
-                                                                                    (int)(k % Hkv), 0);
+  auto unit = [&](int s, int kvh) __attribute__((always_inline)) {
+    int tok0 = 0;
+    while (decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8, BS, NC>(a, sm, s, kvh, 0, tok0))
+      tok0 += NC / G;
+  };
+  if (k < units) unit((int)(k / Hkv), (int)(k % Hkv));
   if (units <= W) return;
   if (ranked) {
     // sequences S0 .. S-1 by length, longest first (ties by index)
@@ -563,17 +622,17 @@ void decode_onepass_kernel(DecodeArgs a) {
       s = (int)((W + q) / Hkv);
       kvh = (int)((W + q) % Hkv);
     }
-    decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8, BS>(a, sm, s, kvh, 0);
+    unit(s, kvh);
   }
 }
 
 // Resident workgroups per CU for the one-pass kernel, queried once per instance.
-template <class ST, int D, int G, bool KV8, int BS>
+template <class ST, int D, int G, bool KV8, int BS, int NC = G>
 int onepass_blocks_per_cu() {
   static int cached = 0;
   if (!cached) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8, BS>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8, BS, NC>,
                                                      onepass_waves<D>() * kWave, 0) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
@@ -627,6 +686,29 @@ hipError_t launch_bs(const DecodeArgs& a, bool split, hipStream_t stream) {
   }
 }
 
+// several query tokens per sequence: the one-pass kernel with 16 score columns
+template <class ST, int D, int G>
+hipError_t launch_multitoken_typed(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+  if (units == 0) return hipSuccess;
+  const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G, false, 16, 16>();
+  const int64_t grid = units < slots ? units : slots;
+  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, false, 16, 16>), dim3((unsigned)grid),
+                     dim3(onepass_waves<D>() * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class ST, int D>
+hipError_t launch_multitoken_group(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_multitoken_typed<ST, D, 1>(a, stream);
+    case 2: return launch_multitoken_typed<ST, D, 2>(a, stream);
+    case 4: return launch_multitoken_typed<ST, D, 4>(a, stream);
+    case 8: return launch_multitoken_typed<ST, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <class ST>
 hipError_t launch_dim(const DecodeArgs& a, int head_size, bool split, hipStream_t stream) {
   switch (head_size) {
@@ -638,11 +720,44 @@ hipError_t launch_dim(const DecodeArgs& a, int head_size, bool split, hipStream_
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a_in, int dtype, int head_size, bool split, hipStream_t stream) {
-  DecodeArgs a = a_in;
 #ifndef PCACHE_LONGEST_FIRST
 #define PCACHE_LONGEST_FIRST 1
 #endif
+
+hipError_t launch_decode_multitoken(const VarlenArgs& v, int dtype, int head_size, hipStream_t stream) {
+  DecodeArgs a{};
+  a.out = v.out;
+  a.q = v.q;
+  a.k_pool = v.k_pool;
+  a.v_pool = v.v_pool;
+  a.num_blocks = v.num_blocks;
+  a.block_stride = v.block_stride;
+  a.token_stride = v.token_stride;
+  a.head_stride = v.head_stride;
+  a.block_tables = v.block_tables;
+  a.max_blocks_per_seq = v.max_blocks_per_seq;
+  a.seq_lens = v.seq_lens;
+  a.num_seqs = v.num_reqs;
+  a.num_q_heads = v.num_q_heads;
+  a.num_kv_heads = v.num_kv_heads;
+  a.block_size = 16;
+  a.scale_log2 = v.scale_log2;
+  a.longest_first = PCACHE_LONGEST_FIRST && v.num_reqs > 1;
+  a.alibi_slopes = v.alibi_slopes;
+  a.query_start_loc = v.query_start_loc;
+  a.total_q = v.total_q;
+  a.causal = v.causal;
+  switch (dtype * 1000 + head_size) {
+    case 1064: return launch_multitoken_group<F16, 64>(a, stream);
+    case 1128: return launch_multitoken_group<F16, 128>(a, stream);
+    case 2064: return launch_multitoken_group<BF16, 64>(a, stream);
+    case 2128: return launch_multitoken_group<BF16, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a_in, int dtype, int head_size, bool split, hipStream_t stream) {
+  DecodeArgs a = a_in;
   a.longest_first = PCACHE_LONGEST_FIRST && !split && a.num_seqs > 1;
   switch (dtype) {
     case 1: return launch_dim<F16>(a, head_size, split, stream);

@@ -46,6 +46,12 @@ struct DecodeArgs {
   const float* k_scale;
   const float* v_scale;
   int64_t scale_stride;
+  // several query tokens per sequence (one-pass path only): sequence s owns q/out rows
+  // [query_start_loc[s], query_start_loc[s+1]) of total_q, its newest tokens; causal:
+  // token i of n attends positions <= L - n + i.  NULL: one token per sequence, row s.
+  const int32_t* query_start_loc;
+  int64_t total_q;
+  int causal;
 };
 
 struct VarlenArgs {
@@ -84,6 +90,9 @@ hipError_t launch_write_fp8(const WriteArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
 // 16-bit storage: q.k on the matrix cores (decode_mfma.hip).
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
+// the one-pass decode over several query tokens per request (at most 16 (token, head)
+// columns per request and kv head in one pass): 16-bit storage, 16-token blocks
+hipError_t launch_decode_multitoken(const VarlenArgs& a, int dtype, int head_size, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, hipStream_t stream);
 // Multi-token queries (varlen.hip); 16-bit storage only.
 hipError_t launch_varlen(const VarlenArgs& a, int dtype, int head_size, hipStream_t stream);

@@ -713,7 +713,16 @@ hipError_t launch_st(const VarlenArgs& a, int head_size, hipStream_t stream) {
 
 }  // namespace
 
+#ifndef PCACHE_VARLEN_DECODE_MT
+#define PCACHE_VARLEN_DECODE_MT 1
+#endif
+
 hipError_t launch_varlen(const VarlenArgs& a, int dtype, int head_size, hipStream_t stream) {
+  // up to 16 (query token, head) columns per request and kv head (speculative decode):
+  // the one-pass decode's persistent, longest-first unit scheme with one 16-column tile
+  if (PCACHE_VARLEN_DECODE_MT && a.num_kv_heads > 0 && a.max_query_len > 0 &&
+      (int64_t)a.max_query_len * (a.num_q_heads / a.num_kv_heads) <= 16)
+    return launch_decode_multitoken(a, dtype, head_size, stream);
   switch (dtype) {
     case 1: return launch_st<F16>(a, head_size, stream);
     case 2: return launch_st<BF16>(a, head_size, stream);

@@ -49,7 +49,9 @@ def test_varlen_parity(dt, D, G, causal):
     check(out, oracle.varlen(wl, hpool, vq), f"varlen {dt} D{D} G{G} {'causal' if causal else 'full'}")
 
 
-SHORT_QLENS = [1, 2, 4, 3, 0, 4, 1]  # at most 32 (token, head) columns: the K/V-splitting kernel
+SHORT_QLENS = [1, 2, 4, 3, 0, 4, 1]  # G <= 4: the multi-token decode; G = 8 (32 columns): K/V split over waves
+# at most 16 (token, head) columns per request and kv head: the one-pass decode's unit
+MT_QLENS = {1: [1, 16, 9, 0, 16, 5, 1], 2: [1, 8, 3, 0, 8, 2, 1], 4: [1, 4, 4, 0, 2, 4, 3], 8: [1, 2, 1, 0, 2, 2, 1]}
 
 
 @pytest.mark.parametrize("dt,D,G", CASES, ids=[f"{a}-d{b}-g{c}" for a, b, c in CASES])
@@ -58,6 +60,18 @@ def test_varlen_parity_short_queries(dt, D, G):
     vq = varlen_variant(wl, SHORT_QLENS)
     dpool = gh.filled_pool(wl)
     check(gh.varlen(dpool, vq), oracle.varlen(wl, oracle.filled_pool(wl), vq), f"varlen short {dt} D{D} G{G}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_multitoken_decode(G, causal):
+    """Up to 16 (query token, head) columns per request and kv head run on the one-pass
+    decode's unit with one 16-column score tile: column c is token c / G, head c % G."""
+    wl = custom(540 + G, "bf16", 2 * G, 2, 128, LENS)
+    vq = varlen_variant(wl, MT_QLENS[G])
+    dpool = gh.filled_pool(wl)
+    check(gh.varlen(dpool, vq, causal=causal), oracle.varlen(wl, oracle.filled_pool(wl), vq, causal=causal),
+          f"varlen multi-token G{G} {'causal' if causal else 'full'}")
 
 
 @pytest.mark.parametrize("R", [8, 128, 130])
@@ -76,6 +90,17 @@ def test_varlen_dispatch_order(R):
     vq = varlen_variant(wl, qlens.astype(np.int32))
     dpool = gh.filled_pool(wl)
     check(gh.varlen(dpool, vq), oracle.varlen(wl, oracle.filled_pool(wl), vq), f"varlen order R{R}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_alibi_multitoken(causal):
+    """The bias on the multi-token decode (origin at each query token's own position,
+    causal or not)."""
+    wl = alibi_variant(custom(512, "bf16", 16, 4, 128, LENS), np.linspace(0.25, -0.01, 16).astype(np.float32))
+    vq = varlen_variant(wl, MT_QLENS[4])
+    dpool = gh.filled_pool(wl)
+    check(gh.varlen(dpool, vq, causal=causal), oracle.varlen(wl, oracle.filled_pool(wl), vq, causal=causal),
+          f"varlen + ALiBi, multi-token {'causal' if causal else 'full'}")
 
 
 @pytest.mark.parametrize("qlens", ["long", "short"])
@@ -120,20 +145,21 @@ def test_varlen_chunked_prefill_step():
     check(gh.varlen(dpool, vq), oracle.varlen(wl, hpool, vq), "chunked prefill step")
 
 
-@pytest.mark.parametrize("mql", [8, 16])
+@pytest.mark.parametrize("mql", [2, 8, 16])
 def test_varlen_understated_max_query_len(mql):
-    """A request longer than max_query_len is still computed in full (8 x 4 columns: the
-    K/V-splitting kernel; 16 x 4: the LDS-sharing kernel, whose grid then holds one
-    32-token chunk per request for a 90-token query)."""
+    """A request longer than max_query_len is still computed in full (2 x 4 columns: the
+    multi-token decode, in passes of 4 tokens; 8 x 4: the K/V-splitting kernel; 16 x 4:
+    the LDS-sharing kernel, whose grid then holds one 32-token chunk per request)."""
     wl = custom(513, "f16", 8, 2, 64, [100, 300])
     vq = varlen_variant(wl, [90, 7])
     dpool = gh.filled_pool(wl)
     check(gh.varlen(dpool, vq, max_query_len=mql), oracle.varlen(wl, oracle.filled_pool(wl), vq), f"short grid {mql}")
 
 
-def test_varlen_bad_request_is_nan_only_there():
+@pytest.mark.parametrize("qlens", [[4, 30, 5], [2, 3, 4]], ids=["lds", "multitoken"])
+def test_varlen_bad_request_is_nan_only_there(qlens):
     wl = custom(514, "bf16", 8, 2, 128, [40, 300, 60])
-    vq = varlen_variant(wl, [4, 30, 5])
+    vq = varlen_variant(wl, qlens)
     dpool = gh.filled_pool(wl)
     ref = oracle.varlen(wl, oracle.filled_pool(wl), vq)
     qs = vq.query_start_loc
