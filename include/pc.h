@@ -74,7 +74,7 @@ typedef enum { PC_F32 = 0, PC_F16 = 1, PC_BF16 = 2 } pc_dtype;
 /* Status codes. */
 #define PC_OK 0
 #define PC_ERR_INVALID_ARG (-1) /* a null pointer, negative size, or inconsistent sizes */
-#define PC_ERR_UNSUPPORTED (-2) /* a valid request this build has no kernel for */
+#define PC_ERR_UNSUPPORTED (-2) /* a valid request the library has no kernel for */
 #define PC_ERR_LAUNCH (-3)      /* the HIP runtime refused the launch */
 
 /* Tokens per partition on the split path. */

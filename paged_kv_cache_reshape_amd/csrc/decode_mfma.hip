@@ -546,11 +546,11 @@ void decode_split_kernel(DecodeArgs a) {
   decode_unit<ST, D, G, NW, STAGES, TABLE, true, KV8, BS>(a, sm, s, kvh, part);
 }
 
-// One-pass path: persistent workgroups.  Round 0 takes units in index order (unit u =
+// One-pass path: persistent workgroups.  Turn 0 takes units in index order (unit u =
 // kv head u % Hkv of sequence u / Hkv), so no ranking stands between the launch and the
-// first loads.  While round 0 runs, the sequence lengths are fetched; after it, the
+// first loads.  While turn 0 runs, the sequence lengths are fetched; after it, the
 // remaining units are ranked longest first and dealt in snake order, and the workgroup
-// whose round-0 unit was the r-th longest receives the r-th shortest unit of round 1,
+// whose turn-0 unit was the r-th longest receives the r-th shortest unit of turn 1,
 // which evens out the sums across workgroups.  NC > G: several query tokens per
 // sequence, in passes of NC / G tokens (one pass unless max_query_len was understated).
 template <class ST, int D, int G, bool KV8, int BS, int NC = G>
@@ -560,19 +560,19 @@ void decode_onepass_kernel(DecodeArgs a) {
   constexpr int kThreads = NW * kWave;
   constexpr int STAGES = KV8 ? PCACHE_ONEPASS_STAGES_KV8 : PCACHE_ONEPASS_STAGES;
   __shared__ UnitLds<NW, D, NC, PCACHE_ONEPASS_TABLE> sm;
-  __shared__ int order_lds[kMaxRankedSeqs];  // order_lds[rank] = later-round sequence of that length rank
+  __shared__ int order_lds[kMaxRankedSeqs];  // order_lds[rank] = later-turn sequence of that length rank
   __shared__ int len_lds[kMaxRankedSeqs];
-  __shared__ int rank0_lds;                  // length rank of this workgroup's round-0 sequence
+  __shared__ int rank0_lds;                  // length rank of this workgroup's turn-0 sequence
 
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   const int64_t units = (int64_t)S * Hkv;
   const int64_t W = gridDim.x;
   const int64_t k = blockIdx.x;
-  // ranking needs whole sequences in round 0 (W a multiple of Hkv) and a later round
+  // ranking needs whole sequences in turn 0 (W a multiple of Hkv) and a later turn
   const bool ranked = a.longest_first && S <= kMaxRankedSeqs && units > W && W % Hkv == 0;
-  const int S0 = (int)(W / Hkv);  // sequences of round 0 when ranked
-  if (ranked)  // read here, used after round 0 (its barriers publish the stores)
+  const int S0 = (int)(W / Hkv);  // sequences of turn 0 when ranked
+  if (ranked)  // read here, used after turn 0 (its barriers publish the stores)
     for (int t = threadIdx.x; t < S; t += kThreads) len_lds[t] = a.seq_lens[t];
 
   auto unit = [&](int s, int kvh) __attribute__((always_inline)) {
@@ -593,7 +593,7 @@ void decode_onepass_kernel(DecodeArgs a) {
       }
       order_lds[rank] = t;
     }
-    // rank of this workgroup's round-0 sequence among sequences 0 .. S0-1
+    // rank of this workgroup's turn-0 sequence among sequences 0 .. S0-1
     if (threadIdx.x < kWave) {
       const int s0 = (int)(k / Hkv);
       const int l0 = len_lds[s0];
@@ -607,13 +607,13 @@ void decode_onepass_kernel(DecodeArgs a) {
     }
     __syncthreads();
   }
-  // unit rank of the round-0 unit: the Hkv units of one sequence are consecutive
+  // unit rank of the turn-0 unit: the Hkv units of one sequence are consecutive
   const int64_t r0 = ranked ? (int64_t)rank0_lds * Hkv + k % Hkv : k;
   const int64_t rest = units - W;
-  for (int64_t round = 1; (round - 1) * W < rest; ++round) {
-    const int64_t f = (round & 1) ? W - 1 - r0 : r0;  // snake, shortest first for the longest round-0 unit
-    const int64_t q = (round - 1) * W + f;            // position among the later units
-    if (q >= rest) continue;                          // the last round is partial
+  for (int64_t turn = 1; (turn - 1) * W < rest; ++turn) {
+    const int64_t f = (turn & 1) ? W - 1 - r0 : r0;  // snake, shortest first for the longest turn-0 unit
+    const int64_t q = (turn - 1) * W + f;            // position among the later units
+    if (q >= rest) continue;                          // the last turn is partial
     int s, kvh;
     if (ranked) {
       s = order_lds[(int)(q / Hkv)];

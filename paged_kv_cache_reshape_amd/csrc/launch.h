@@ -41,7 +41,8 @@ struct DecodeArgs {
   float* tmp_out;
   // 8-bit (OCP E4M3) pool: codes times k_scale / v_scale of the kv head
   int kv8;
-  // ALiBi: score of token t for query head h gains alibi_slopes[h] * (t - (L - 1)); NULL: none
+  // ALiBi: score of token t for query head h gains alibi_slopes[h] * (t - p), p the query
+  // token's position (L - 1 for one token per sequence); NULL: none
   const float* alibi_slopes;
   const float* k_scale;
   const float* v_scale;
@@ -86,7 +87,7 @@ struct ReduceArgs {
 hipError_t launch_write(const WriteArgs& a, int dtype, bool vec16, hipStream_t stream);
 // The write into an 8-bit (OCP E4M3) pool; `dtype` is the type of key / value.
 hipError_t launch_write_fp8(const WriteArgs& a, int dtype, hipStream_t stream);
-// Returns hipErrorInvalidValue for a (dtype, head_size, group) this build has no kernel for.
+// Returns hipErrorInvalidValue for a (dtype, head_size, group) the library has no kernel for.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
 // 16-bit storage: q.k on the matrix cores (decode_mfma.hip).
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
