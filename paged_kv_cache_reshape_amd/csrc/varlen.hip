@@ -593,8 +593,11 @@ void varlen_lds_kernel(VarlenArgs a) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
               const float* x = xs[q];
-              const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+              // NaN-propagating maximum (v_maximum3_f32): no quieting of each input, and a
+              // NaN score ends in the output through its own exponential either way
+              const float lm = __builtin_elementwise_maximum(
+                  __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), __builtin_elementwise_maximum(x[2], x[3])),
+                  __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[4], x[5]), __builtin_elementwise_maximum(x[6], x[7])));
               if (__builtin_amdgcn_ballot_w64(lm > thr[q]) != 0) {
                 float hm = fmaxf(lm, __shfl_xor(lm, 16));
                 hm = fmaxf(hm, __shfl_xor(hm, 32));
