@@ -117,7 +117,6 @@ struct UnitLds {
   float lw[NW][NC];
   int ids[TABLE];  // block ids of the unit's current chunk
   int bad;         // some id of the unit lies outside the pool
-  uint4 step_row[2][16];  // fused step write: the new token's K and V row of this kv head
 };
 
 
@@ -180,41 +179,6 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const bool bad_scale = KV8 && !(cs_raw >= 0x1p-120f && cs_raw <= 0x1p120f && vsc > 0.f && vsc <= 3.4e38f);
   bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * BS ||
              (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition) || bad_scale || (MT && L < n);
-  // The step's own K/V write, fused (16-bit pools, one token per sequence): token s is
-  // sequence s's newest token.  Its row for this kv head is written to the pool by the
-  // unit whose tokens include position L - 1, and goes, through LDS, straight into the
-  // registers of the tile holding L - 1 -- nothing in this launch reads it back from the
-  // pool, so the write needs no ordering.  A slot inside the pool that is not position
-  // L - 1 of sequence s makes the step invalid for s: its outputs become NaN and nothing
-  // is written; a slot outside the pool (padding) writes nothing, as in the plain write.
-  bool patch = false;      // this unit holds position L - 1 and writes / patches its row
-  int64_t step_dst = 0;    // element offset of the row (this kv head) in either pool
-  uint4 step_v = make_uint4(0, 0, 0, 0);  // threads < 2 * D/8: one 16-byte piece of it
-  if constexpr (!MT && !KV8) {
-    if (a.step_slots != nullptr) {
-      const int64_t slot = uniform_load(a.step_slots, s);
-      if (slot >= 0 && slot < a.num_blocks * BS) {
-        bool at_last = false;
-        if (!bad && L >= 1) {
-          const int id = uniform_load(a.block_tables + (int64_t)s * a.max_blocks_per_seq, (L - 1) / BS);
-          at_last = (int64_t)id * BS + (L - 1) % BS == slot;
-        }
-        bad = bad || !at_last;
-        patch = at_last && (!SPLIT || part == (L - 1) / kPartition);
-        const int64_t blk = slot / BS;
-        step_dst = blk * a.block_stride + (slot - blk * BS) * a.token_stride + (int64_t)kvh * a.head_stride;
-        if (patch && threadIdx.x < 2 * (D / 8)) {
-          const int tid_ = threadIdx.x;
-          const bool isv = tid_ >= D / 8;
-          const int piece = isv ? tid_ - D / 8 : tid_;
-          const uint16_t* src = static_cast<const uint16_t*>(isv ? a.step_value : a.step_key) +
-                                (int64_t)s * (isv ? a.step_value_stride : a.step_key_stride) + (int64_t)kvh * D +
-                                8 * piece;
-          step_v = *reinterpret_cast<const uint4*>(src);
-        }
-      }
-    }
-  }
   const int t_begin = SPLIT ? part * kPartition : 0;
   const int t_end = bad ? t_begin : (SPLIT ? min(L, t_begin + kPartition) : L);
   const int b_begin = t_begin / kBlockTokens;
@@ -326,25 +290,6 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   // consume the block in ring slot SL whose first token is TOK0
 #define PC_BLOCK(SL, TOK0)                                                                           \
   do {                                                                                               \
-    if constexpr (!MT && !KV8) {                                                                     \
-      /* the fused step's new row L - 1 replaces what the pool held there */                         \
-      if (patch && (TOK0) <= L - 1 && L - 1 < (TOK0) + kBlockTokens) {                               \
-        const int r_ = L - 1 - (TOK0);                                                               \
-        if (col == r_) {                                                                             \
-          _Pragma("unroll") for (int k = 0; k < KS; ++k) kb[SL][k] = sm.step_row[0][4 * k + rg];    \
-        }                                                                                            \
-        if (rg == (r_ >> 2)) {                                                                       \
-          VRow nv_;                                                                                  \
-          if constexpr (DPL == 8) {                                                                  \
-            nv_ = __builtin_bit_cast(VRow, sm.step_row[1][col]);                                     \
-          } else {                                                                                   \
-            const uint4 ch_ = sm.step_row[1][col >> 1];                                              \
-            nv_ = __builtin_bit_cast(VRow, (col & 1) ? make_uint2(ch_.z, ch_.w) : make_uint2(ch_.x, ch_.y)); \
-          }                                                                                          \
-          _Pragma("unroll") for (int e = 0; e < 4; ++e) vb[SL][e] = e == (r_ & 3) ? nv_ : vb[SL][e]; \
-        }                                                                                            \
-      }                                                                                              \
-    }                                                                                                \
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};                                                                \
     if constexpr (KV8) {                                                                             \
       /* each k-step's 8 codes widened to the query's type just before its MFMA */                   \
@@ -460,15 +405,6 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       if (i < nb) {
         sm.ids[i] = staged[r];
         if (staged[r] < 0 || (int64_t)staged[r] >= a.num_blocks) sm.bad = 1;
-      }
-    }
-    if constexpr (!MT && !KV8) {
-      if (patch && cb == b_begin && tid < 2 * (D / 8)) {
-        const bool isv = tid >= D / 8;
-        const int piece = isv ? tid - D / 8 : tid;
-        sm.step_row[isv][piece] = step_v;
-        uint16_t* dst = static_cast<uint16_t*>(const_cast<void*>(isv ? a.v_pool : a.k_pool)) + step_dst + 8 * piece;
-        *reinterpret_cast<uint4*>(dst) = step_v;
       }
     }
     lds_barrier();
