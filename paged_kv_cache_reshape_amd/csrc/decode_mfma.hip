@@ -109,6 +109,16 @@ constexpr int onepass_waves() {
 #ifndef PCACHE_SPLIT_STAGES_KV8
 #define PCACHE_SPLIT_STAGES_KV8 2
 #endif
+// Cache-policy operand of the K and V tile loads (each tile is read once per step).  The
+// V loads carry the non-temporal hint (nt, 2): measured 2% faster one-pass and 6% faster
+// split decode on the 16-bit cache, 2-4% on the 8-bit one; the same hint on the K loads
+// made both paths slower (3-7%), alone or together with V.
+#ifndef PCACHE_K_CPOL
+#define PCACHE_K_CPOL 0
+#endif
+#ifndef PCACHE_V_CPOL
+#define PCACHE_V_CPOL 2
+#endif
 
 template <int NW, int D, int NC, int TABLE>
 struct UnitLds {
@@ -148,6 +158,8 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   using VRow8 = typename VRow8Of<DPL>::type;
   constexpr int EB = KV8 ? 1 : 2;  // pool bytes per element
   constexpr int K8 = KS / 2;        // 16-byte K loads per block and lane (8-bit pool)
+  constexpr int kKCpol = PCACHE_K_CPOL;
+  constexpr int kVCpol = PCACHE_V_CPOL;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -267,21 +279,21 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                       \
       if constexpr (KV8) {                                                                           \
         _Pragma("unroll") for (int k = 0; k < K8; ++k) kq[ST][k] =                                  \
-            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 16 * k, 0, 0)); \
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 16 * k, 0, kKCpol)); \
         _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                             \
           if constexpr (DPL == 8)                                                                    \
-            vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+            vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, kVCpol)); \
           else                                                                                       \
-            vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b32(vr_, v_off, e * tok_bytes, 0)); \
+            vq[ST][e] = __builtin_bit_cast(VRow8, __builtin_amdgcn_raw_buffer_load_b32(vr_, v_off, e * tok_bytes, kVCpol)); \
         }                                                                                            \
       } else {                                                                                       \
         _Pragma("unroll") for (int k = 0; k < KS; ++k) kb[ST][k] =                                  \
-            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 64 * k, 0, 0)); \
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 64 * k, 0, kKCpol)); \
         _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                             \
           if constexpr (DPL == 8)                                                                    \
-            vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b128(vr_, v_off, e * tok_bytes, 0)); \
+            vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b128(vr_, v_off, e * tok_bytes, kVCpol)); \
           else                                                                                       \
-            vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, 0)); \
+            vb[ST][e] = __builtin_bit_cast(VRow, __builtin_amdgcn_raw_buffer_load_b64(vr_, v_off, e * tok_bytes, kVCpol)); \
         }                                                                                            \
       }                                                                                              \
     }                                                                                                \
