@@ -79,9 +79,18 @@ constexpr int kMaxRankedSeqs = 512;     // sequences ranked by length in-kernel 
 #ifndef PCACHE_ONEPASS_WAVES_D64
 #define PCACHE_ONEPASS_WAVES_D64 16
 #endif
-template <int D>
+// The 8-bit pool at head size 128 has its own wave count: 8 waves (2 per SIMD) ran the
+// one-pass decode 3% faster than 12 (measured with the non-temporal V loads below);
+// deeper rings on the 8 waves (3 or 4 stages) lost that gain again.
+#ifndef PCACHE_ONEPASS_WAVES_D128_KV8
+#define PCACHE_ONEPASS_WAVES_D128_KV8 8
+#endif
+#ifndef PCACHE_ONEPASS_OCC_KV8
+#define PCACHE_ONEPASS_OCC_KV8 2
+#endif
+template <int D, bool KV8 = false>
 constexpr int onepass_waves() {
-  return D == 64 ? PCACHE_ONEPASS_WAVES_D64 : PCACHE_ONEPASS_WAVES_D128;
+  return D == 64 ? PCACHE_ONEPASS_WAVES_D64 : KV8 ? PCACHE_ONEPASS_WAVES_D128_KV8 : PCACHE_ONEPASS_WAVES_D128;
 }
 #ifndef PCACHE_ONEPASS_STAGES
 #define PCACHE_ONEPASS_STAGES 2
@@ -566,9 +575,10 @@ void decode_split_kernel(DecodeArgs a) {
 // which evens out the sums across workgroups.  NC > G: several query tokens per
 // sequence, in passes of NC / G tokens (one pass unless max_query_len was understated).
 template <class ST, int D, int G, bool KV8, int BS, int NC = G>
-__global__ __launch_bounds__(onepass_waves<D>() * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_ONEPASS_OCC)))
+__global__ __launch_bounds__((onepass_waves<D, KV8>() * kWave))
+__attribute__((amdgpu_waves_per_eu(KV8 && D == 128 ? PCACHE_ONEPASS_OCC_KV8 : PCACHE_ONEPASS_OCC)))
 void decode_onepass_kernel(DecodeArgs a) {
-  constexpr int NW = onepass_waves<D>();
+  constexpr int NW = onepass_waves<D, KV8>();
   constexpr int kThreads = NW * kWave;
   constexpr int STAGES = KV8 ? PCACHE_ONEPASS_STAGES_KV8 : PCACHE_ONEPASS_STAGES;
   __shared__ UnitLds<NW, D, NC, PCACHE_ONEPASS_TABLE> sm;
@@ -645,7 +655,7 @@ int onepass_blocks_per_cu() {
   if (!cached) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8, BS, NC>,
-                                                     onepass_waves<D>() * kWave, 0) != hipSuccess ||
+                                                     onepass_waves<D, KV8>() * kWave, 0) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
       n = 1;
@@ -672,7 +682,7 @@ hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
   const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G, KV8, BS>();
 #endif
   const int64_t grid = units < slots ? units : slots;
-  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, KV8, BS>), dim3((unsigned)grid), dim3(onepass_waves<D>() * kWave), 0,
+  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, KV8, BS>), dim3((unsigned)grid), dim3(onepass_waves<D, KV8>() * kWave), 0,
                      stream, a);
   return hipGetLastError();
 }
