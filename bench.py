@@ -1,8 +1,10 @@
 """Benchmark: one decode step of the paged KV-cache hot path on one MI355X.
 
 A step is the whole path over one batch: the write of each sequence's new token
-into the paged pool (pc_reshape_and_cache), the planner, and the decode (one pass,
-or the 512-token split plus its log-sum-exp reduce).  The default workload is
+into the paged pool, the planner, and the decode (one pass, or the 512-token split
+plus its log-sum-exp reduce): pc_reshape_and_cache, then pc_paged_attention_decode;
+``--step fused`` runs the write and the decode as one launch
+(pc_reshape_and_cache_decode, 16-bit pools).  The default workload is
 64 sequences of 512..2048 tokens, 32 query / 8 KV heads, head size 128, bf16, one
 pass (the GQA decode the throughput target is quoted on).  ``--kv fp8`` runs the
 same step over an 8-bit (OCP E4M3) cache with per-kv-head scales: the write
@@ -18,8 +20,9 @@ Prints ONE JSON line.  ``value`` is effective GB/s over the whole step: K/V byte
 of exactly seq_len tokens per sequence plus q and out, divided by the step time
 (wall clock over the timed steps, bracketed by device synchronisations, with
 nothing else enqueued).
-``roofline`` is the decode kernel alone: the same algorithmic bytes per launch over
-its average launch time.  That time is measured with HIP events on the launch
+``roofline`` is the decode launch alone (with the fused write when the step fuses
+it, whose rows' bytes it then adds): its algorithmic bytes per launch over its
+average launch time.  That time is measured with HIP events on the launch
 stream over a run of back-to-back decode launches (rotating over the pool copies,
 one event pair around the run, so the events' own dispatch cost is spread over the
 run); the per-launch event pairs inside the timed steps are reported beside it
@@ -54,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--path", choices=["plan", "single", "split"], default="plan")
+    ap.add_argument("--step", choices=["separate", "fused"], default="separate",
+                    help="the step's write and decode as two launches, or as one (pc_reshape_and_cache_decode)")
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="cache element type: the query's type, or OCP E4M3 codes with per-kv-head scales")
     ap.add_argument("--alibi", action="store_true", help="add the ALiBi bias (geometric slopes, one per query head)")
@@ -213,13 +218,31 @@ def main():
                                       num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), alibi_slopes=inp.alibi,
                                       **pool.layout_kwargs(), **split_kw)
 
+    # the fused step: 16-bit pools, one new token per sequence (token s = sequence s's
+    # newest), and not 8-token blocks with 8 query heads per kv head at head size 128
+    can_fuse = (not fp8 and wl.dtype in ("bf16", "f16") and len(wl.slot_mapping) == S and
+                not (wl.block_size == 8 and Hq == 8 * wl.num_kv_heads and D == 128))
+    fused = args.step == "fused"
+    if fused and not can_fuse:
+        raise SystemExit("--step fused: 16-bit pools and one new token per sequence only")
+
+    def fused_step(pool):
+        o = None if ps else out
+        pc.reshape_and_cache_decode(o, inp.q, key, value, pool.k, pool.v, slots, inp.block_tables, inp.seq_lens, msl,
+                                    num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), alibi_slopes=inp.alibi,
+                                    **pool.layout_kwargs(), **split_kw)
+
     def step(i, ev=None):
         pool = pools[i % copies]
-        write(pool)
+        if not fused:
+            write(pool)
         pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, gh.TORCH_DT[wl.dtype])
         if ev is not None:
             ev[0].record(stream)
-        decode(pool)
+        if fused:
+            fused_step(pool)
+        else:
+            decode(pool)
         if ev is not None:
             ev[1].record(stream)
         if ps:
@@ -248,7 +271,8 @@ def main():
         return dec, red
 
     def decode_only(i):
-        decode(pools[i % copies])
+        """The step's decode launch alone (with the step's write when that is fused)."""
+        (fused_step if fused else decode)(pools[i % copies])
 
     def batched(fn, n):
         """Average launch time of n back-to-back launches, one event pair on the stream."""
@@ -271,14 +295,18 @@ def main():
         step(0)
     wel = timed(args.steps, rotate=False)
     wdec_b = batched(lambda i: decode_only(0), args.steps)
+    # for reference: the decode launch without the fused write, back to back
+    plain_b = batched(lambda i: decode(pools[i % copies]), args.steps) if fused else None
 
     eff = wl.effective_bytes()
+    # the fused launch also reads and writes the step's K/V rows
+    launch_bytes = eff + (4 * S * wl.num_kv_heads * D * wl.esize if fused else 0)
     ms = el / args.steps * 1e3
     dec_ms = sum(dec) / len(dec)
     red_ms = sum(red) / len(red)
-    achieved = eff / (dec_b * 1e-3) / 1e9
+    achieved = launch_bytes / (dec_b * 1e-3) / 1e9
     q = lambda xs, f: round(float(sorted(xs)[min(len(xs) - 1, int(f * len(xs)))]) * 1e3, 2)
-    traffic = stored_traffic(wl.name)
+    traffic = stored_traffic(wl.name + (" (fused step)" if fused else ""))
     res = {
         "metric": METRIC,
         "value": round(eff / (ms * 1e-3) / 1e9, 2),
@@ -294,6 +322,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads,
                    "head_size": D, "block_size": wl.block_size, "layout": wl.layout, "path": path,
+                   "step": "fused" if fused else "separate",
                    "kv_cache": "fp8_e4m3 (per-kv-head scales)" if fp8 else wl.dtype,
                    "alibi": bool(args.alibi),
                    "max_seq_len": msl, "kv_bytes_per_step": wl.kv_bytes(), "effective_bytes_per_step": eff,
@@ -305,10 +334,12 @@ def main():
         "decode_kernel_us_p10_p50_p90": [q(dec, 0.1), q(dec, 0.5), q(dec, 0.9)],
         "decode_kernel_us_batched": round(dec_b * 1e3, 2),
         "reduce_kernel_us": round(red_ms * 1e3, 2) if ps else None,
+        "unfused_decode_kernel_us_batched": round(plain_b * 1e3, 2) if fused else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel" if ps else "decode_onepass_kernel",
-                     "bytes_per_launch": eff, "launch_us": round(dec_b * 1e3, 2),
+                     "kernel": ("decode_split_kernel" if ps else "decode_onepass_kernel") +
+                               (" (with the step's K/V write)" if fused else ""),
+                     "bytes_per_launch": launch_bytes, "launch_us": round(dec_b * 1e3, 2),
                      "timing": "HIP events around back-to-back launches on the launch stream"},
         "warm_cache": {"ms_per_step": round(wel / args.steps * 1e3, 5),
                        "decode_kernel_us_batched": round(wdec_b * 1e3, 2),

@@ -13,7 +13,9 @@
  *   pc_paged_attention_reduce  merge the partitions' partial results (log-sum-exp);
  *   pc_paged_attention_plan    choose between the one-pass and the split path;
  *   pc_paged_attention_varlen  several query tokens per request (chunked prefill,
- *                              speculative decode) over the same paged history.
+ *                              speculative decode) over the same paged history;
+ *   pc_reshape_and_cache_decode  a whole decode step -- the write and the decode
+ *                              -- in one launch.
  *
  * The write and the decode also exist for an 8-bit cache (suffix _fp8): the pool
  * holds OCP E4M3 codes with one dequantisation scale per kv head for K and one
@@ -226,6 +228,44 @@ int pc_paged_attention_decode_fp8(void *out, const void *q, const uint8_t *k_poo
                                   int partition_size, float *exp_sums, float *max_logits, float *tmp_out,
                                   const float *alibi_slopes, const float *k_scale, const float *v_scale,
                                   int64_t kv_scale_stride, int dtype, void *stream);
+
+/*
+ * pc_reshape_and_cache_decode -- one decode step in one launch: the write of
+ * pc_reshape_and_cache for this step's tokens, then pc_paged_attention_decode,
+ * with the result of running the two in that order on one stream.
+ *
+ * The operations are the two defined above (same passages).  Token s of the step
+ * is sequence s's newest token (num_tokens == num_seqs): its K/V row goes to
+ * slot_mapping[s], which must be the slot of position seq_lens[s] - 1 of sequence s
+ * (its block block_tables[s*max_blocks_per_seq + (seq_lens[s]-1)/block_size], offset
+ * (seq_lens[s]-1) % block_size), or outside the pool (negative: padding, nothing is
+ * written, and the decode reads whatever the pool holds there).  The workgroup that
+ * decodes the tile holding that position stores the row, waits for the stores to
+ * complete, and only then reads the tile, so the decode sees the new row.  A slot
+ * inside the pool that is not that position is an invalid step for the sequence:
+ * nothing is written for it and its outputs (or split partials) are NaN; a sequence
+ * of length 0 has no such position, writes nothing and decodes as empty.  No other
+ * sequence may read the written slots in this step (true of a decode step: every
+ * sequence appends to its own last block), since only the writer's reads are ordered
+ * after the write.
+ *
+ *   out, q, k_pool ... partition_size, exp_sums, max_logits, tmp_out, alibi_slopes:
+ *                     as for pc_paged_attention_decode (16-bit storage: fp16 or bf16;
+ *                     fp32, and block_size 8 with num_q_heads == 8 * num_kv_heads at
+ *                     head_size 128, give PC_ERR_UNSUPPORTED); the pools are written
+ *   key, value        device [num_seqs, num_kv_heads, head_size] rows at
+ *   key_row_stride,   key_row_stride / value_row_stride elements, q's type,
+ *   value_row_stride  16-byte aligned rows (else PC_ERR_UNSUPPORTED)
+ *   slot_mapping      device int64 [num_seqs]
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ */
+int pc_reshape_and_cache_decode(void *out, const void *q, const void *key, const void *value, int64_t key_row_stride,
+                                int64_t value_row_stride, const int64_t *slot_mapping, void *k_pool, void *v_pool,
+                                int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens,
+                                int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
+                                int block_size, float scale, int partition_size, float *exp_sums, float *max_logits,
+                                float *tmp_out, const float *alibi_slopes, int dtype, void *stream);
 
 /*
  * pc_paged_attention_varlen -- attention of several new query tokens per request

@@ -10,7 +10,8 @@ The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
 * ``reshape_and_cache_fp8`` / ``paged_attention_decode_fp8`` -- the same over an
   8-bit (OCP E4M3) pool with per-kv-head scales;
 * ``paged_attention_varlen``   -- several query tokens per request (chunked
-  prefill, speculative decode), causal, over the same pool.
+  prefill, speculative decode), causal, over the same pool;
+* ``reshape_and_cache_decode`` -- a decode step's write and decode in one launch.
 """
 
 from ._native import (  # noqa: F401
@@ -25,6 +26,7 @@ from ._native import (  # noqa: F401
     paged_attention_reduce,
     paged_attention_varlen,
     reshape_and_cache,
+    reshape_and_cache_decode,
     reshape_and_cache_fp8,
     status_string,
 )

@@ -55,6 +55,10 @@ def _load():
         lib.pc_paged_attention_varlen.restype = i32
         lib.pc_paged_attention_varlen.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, vp, i32, i64, i32,
                                                   i32, i32, i32, i32, f32, i32, vp, i32, vp]
+        lib.pc_reshape_and_cache_decode.restype = i32
+        lib.pc_reshape_and_cache_decode.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, i64, i64, i64, i64, vp,
+                                                    i32, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp,
+                                                    vp, i32, vp]
         lib.pc_paged_attention_reduce.restype = i32
         lib.pc_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.pc_paged_attention_plan.restype = i32
@@ -170,6 +174,48 @@ def paged_attention_decode(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
         D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(alibi_slopes),
         dt, _stream(q, stream))
     _check("pc_paged_attention_decode", st)
+
+
+def reshape_and_cache_decode(out, q: torch.Tensor, key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor,
+                             v_pool: torch.Tensor, slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                             seq_lens: torch.Tensor, max_seq_len: int, *, num_kv_heads: int, scale: float,
+                             num_blocks: int, block_stride: int, token_stride: int, head_stride: int,
+                             block_size: int = 16, v_offset: int = 0, partition_size: int = 0, exp_sums=None,
+                             max_logits=None, tmp_out=None, alibi_slopes=None, stream=None) -> None:
+    """One decode step in one launch: ``key``/``value`` [S, Hkv, D] of each sequence's newest
+    token go to ``slot_mapping`` (int64 [S], the slot of position seq_len - 1, or outside the
+    pool), then the decode of ``q`` [S, Hq, D] -- as reshape_and_cache followed by
+    paged_attention_decode (same keyword arguments).  fp16 / bf16 only."""
+    _same_device(out, q, key, value, k_pool, v_pool, slot_mapping, block_tables, seq_lens, exp_sums, max_logits,
+                 tmp_out, alibi_slopes)
+    _check_alibi(alibi_slopes, q)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [S, Hq, D]")
+    if out is not None and (out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype):
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    S, Hq, D = q.shape
+    if key.dim() != 3 or value.shape != key.shape or key.shape[0] != S or key.stride(2) != 1 or \
+            value.stride(2) != 1 or key.stride(1) != key.shape[2] or value.stride(1) != value.shape[2]:
+        raise ValueError("key/value must be [S, Hkv, D] with contiguous rows, one token per sequence")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous() or slot_mapping.numel() != S:
+        raise ValueError("slot_mapping must be a contiguous int64 [S]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous int32 [S, W]")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [S]")
+    for t in (exp_sums, max_logits, tmp_out):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("partials must be contiguous float32")
+    dt = _dtype_code(q)
+    for t in (key, value, k_pool, v_pool):
+        if _DTYPES.get(t.dtype) != dt:
+            raise TypeError("q, key, value and the pool must share one storage dtype")
+    st = _load().pc_reshape_and_cache_decode(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(slot_mapping), _ptr(k_pool),
+        _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride, head_stride, _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads, D, block_size, scale, partition_size,
+        _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(alibi_slopes), dt, _stream(q, stream))
+    _check("pc_reshape_and_cache_decode", st)
 
 
 def _check_alibi(alibi_slopes, q):

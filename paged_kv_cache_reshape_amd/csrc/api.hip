@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kBlockTokens = 16;
 
 int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
@@ -51,7 +51,9 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
                 int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
                 int num_kv_heads, int head_size, int block_size, float scale, int partition_size, float* exp_sums,
                 float* max_logits, float* tmp_out, const float* alibi_slopes, const float* k_scale,
-                const float* v_scale, int64_t kv_scale_stride, int dtype, bool kv8, void* stream) {
+                const float* v_scale, int64_t kv_scale_stride, int dtype, bool kv8, void* stream,
+                const int64_t* step_slots = nullptr, const void* step_key = nullptr,
+                const void* step_value = nullptr, int64_t step_key_stride = 0, int64_t step_value_stride = 0) {
   const int es = esize(dtype);
   if (!es || num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_size <= 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0 || (kv8 && kv_scale_stride < 0))
@@ -109,6 +111,11 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.scale_stride = kv_scale_stride;
+  a.step_slots = step_slots;
+  a.step_key = step_key;
+  a.step_value = step_value;
+  a.step_key_stride = step_key_stride;
+  a.step_value_stride = step_value_stride;
   return status_of(pcache::launch_decode(a, dtype, head_size, split, static_cast<hipStream_t>(stream)));
 }
 
@@ -220,6 +227,33 @@ int pc_paged_attention_decode_fp8(void* out, const void* q, const uint8_t* k_poo
                      max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
                      block_size, scale, partition_size, exp_sums, max_logits, tmp_out, alibi_slopes, k_scale,
                      v_scale, kv_scale_stride, dtype, true, stream);
+}
+
+int pc_reshape_and_cache_decode(void* out, const void* q, const void* key, const void* value, int64_t key_row_stride,
+                                int64_t value_row_stride, const int64_t* slot_mapping, void* k_pool, void* v_pool,
+                                int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+                                int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
+                                int block_size, float scale, int partition_size, float* exp_sums, float* max_logits,
+                                float* tmp_out, const float* alibi_slopes, int dtype, void* stream) {
+  const int es = esize(dtype);
+  if (num_seqs < 0) return PC_ERR_INVALID_ARG;
+  const int wrc = check_write(key, value, key_row_stride, value_row_stride, k_pool, v_pool, num_blocks, block_stride,
+                              token_stride, head_stride, slot_mapping, num_seqs, num_kv_heads, head_size,
+                              block_size, es);
+  if (wrc != PC_OK) return wrc;
+  if (dtype == PC_F32) return PC_ERR_UNSUPPORTED;  // the fused write lives in the matrix-core decode
+  // 8-token blocks, 8 query heads per kv head, head size 128: the fused one-pass kernel
+  // would not keep its state in registers, so the library has no fused kernel for it
+  if (block_size == 8 && num_kv_heads > 0 && num_q_heads == 8 * num_kv_heads && head_size == 128)
+    return PC_ERR_UNSUPPORTED;
+  // the row is moved in 16-byte pieces
+  if (num_seqs > 0 && (!aligned16(key) || !aligned16(value) || !strides16(es, {key_row_stride, value_row_stride})))
+    return PC_ERR_UNSUPPORTED;
+  return decode_impl(out, q, k_pool, v_pool, num_blocks, block_stride, token_stride, head_stride, block_tables,
+                     max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
+                     block_size, scale, partition_size, exp_sums, max_logits, tmp_out, alibi_slopes, nullptr,
+                     nullptr, 0, dtype, false, stream, slot_mapping, key, value, key_row_stride, value_row_stride);
 }
 
 int pc_paged_attention_varlen(void* out, const void* q, const void* k_pool, const void* v_pool, int64_t num_blocks,

@@ -146,7 +146,8 @@ struct UnitLds {
 // one token).  NC = 16 > G takes several query tokens per sequence (query_start_loc):
 // column c = token tok0 + c / G, head h0 + c % G, each with its own causal limit; the
 // call covers tokens tok0 .. tok0 + 16/G - 1 and returns whether more remain.
-template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT, bool KV8, int BS, int NC = G>
+template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT, bool KV8, int BS, int NC = G,
+          bool FUSED = false>
 __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, NC, TABLE>& sm, int s, int kvh,
                                             int part, int tok0 = 0) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
@@ -379,8 +380,55 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 
   // ---- the unit's blocks, TABLE ids at a time -----------------------------------------
   // the previous unit read sm.bad before its merge barrier, so it can be cleared here
+  // The step's own K/V write, fused (16-bit pools, one token per sequence): token s is
+  // sequence s's newest token, and the unit whose tokens include position L - 1 stores
+  // its row for this kv head.  Wave 0 does it: the row (16 bytes per lane, lanes
+  // < 2*D/8) is read, the slot checked against the table, the row stored and the stores
+  // waited for, before a workgroup barrier that precedes every read of the tile holding
+  // L - 1.  That is the chunk's staging barrier below (wave 0 writes while the other
+  // waves issue their early first-tile loads), or, when that tile is itself one of the
+  // early first tiles (a unit of fewer than NW tiles), the barrier just below.  A slot
+  // inside the pool that is not position L - 1 of sequence s makes the step invalid for
+  // s: nothing is written and sm.bad turns its outputs to NaN; a slot outside the pool
+  // (padding) writes nothing, as in the plain write.
+  static_assert(!FUSED || (!MT && !KV8), "the fused write: one token per sequence, 16-bit pools");
+  const bool fused = FUSED && !bad && L >= 1;
+  const bool fused_early = fused && (L - 1) / kBlockTokens - b_begin < NW;
+  auto fused_write = [&]() __attribute__((always_inline)) {
+    const bool owner = !SPLIT || part == (L - 1) / kPartition;
+    const bool isv = lane >= D / 8;
+    const int piece = isv ? lane - D / 8 : lane;
+    uint4 row = make_uint4(0, 0, 0, 0);
+    if (owner && lane < 2 * (D / 8))
+      row = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(isv ? a.step_value : a.step_key) +
+                                            (int64_t)s * (isv ? a.step_value_stride : a.step_key_stride) +
+                                            (int64_t)kvh * D + 8 * piece);
+    const int64_t slot = uniform_load(a.step_slots, s);
+    if (slot >= 0 && slot < a.num_blocks * BS) {
+      const int id = uniform_load(table, (L - 1) / BS);
+      if ((int64_t)id * BS + (L - 1) % BS != slot) {
+        if (lane == 0) sm.bad = 1;
+      } else if (owner) {
+        if (lane < 2 * (D / 8)) {
+          const int64_t blk = slot / BS;
+          const int64_t dst = blk * a.block_stride + (slot - blk * BS) * a.token_stride +
+                              (int64_t)kvh * a.head_stride + 8 * piece;
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(const_cast<void*>(isv ? a.v_pool : a.k_pool)) + dst) = row;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores are complete
+      }
+    }
+  };
+
+  // the previous unit read sm.bad before its merge barrier, so it can be cleared here
   if (tid == 0) sm.bad = 0;
+  if constexpr (FUSED) {
+    if (fused_early && w == 0) fused_write();
+  }
   lds_barrier();  // the previous unit's readers of sm are done
+  if constexpr (FUSED) {
+    if (fused && !fused_early && w == 0) fused_write();
+  }
   for (int cb = b_begin; cb < b_end; cb += CT) {
     const int cn = min(CT, b_end - cb);  // tiles in this chunk
     if (cb != b_begin) __syncthreads();  // every wave has read the previous chunk's ids
@@ -409,17 +457,19 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     // pool is replaced by block 0 here; the staged check below then discards the unit.
     // (issued by every wave, so that the wait for the staged ids below is exact; a wave
     // with no tile in the chunk fetches the chunk's last one and never reads it)
-    {
-      const int jt = cb + min(w, cn - 1);
-      auto valid = [&](int id) { return (id >= 0 && (int64_t)id < a.num_blocks) ? id : 0; };
-      if constexpr (BS == 16) {
-        PC_LOAD(0, valid(uniform_load(table, jt)), 0);
-      } else if constexpr (BS == 32) {
-        PC_LOAD(0, valid(uniform_load(table, jt >> 1)), jt & 1);
-      } else {
-        PC_LOAD(0, valid(uniform_load(table, 2 * jt)), valid(uniform_load(table, min(2 * jt + 1, nblk - 1))));
-      }
-    }
+    const int jt0 = cb + min(w, cn - 1);
+    auto valid = [&](int id) { return (id >= 0 && (int64_t)id < a.num_blocks) ? id : 0; };
+#define PC_FIRST_LOAD()                                                                              \
+  do {                                                                                               \
+    if constexpr (BS == 16) {                                                                        \
+      PC_LOAD(0, valid(uniform_load(table, jt0)), 0);                                                \
+    } else if constexpr (BS == 32) {                                                                 \
+      PC_LOAD(0, valid(uniform_load(table, jt0 >> 1)), jt0 & 1);                                     \
+    } else {                                                                                         \
+      PC_LOAD(0, valid(uniform_load(table, 2 * jt0)), valid(uniform_load(table, min(2 * jt0 + 1, nblk - 1)))); \
+    }                                                                                                \
+  } while (0)
+    PC_FIRST_LOAD();
 #pragma unroll
     for (int r = 0; r < kStage; ++r) {
       const int i = tid + r * kThreads;
@@ -429,6 +479,7 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       }
     }
     lds_barrier();
+#undef PC_FIRST_LOAD
     if (__builtin_amdgcn_readfirstlane(sm.bad)) {
       bad = true;  // a block id outside the pool: nothing more is read, the outputs become NaN
       break;
@@ -548,7 +599,8 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 }
 
 // Split path: workgroup = (kv head, sequence, partition), fastest-varying first.
-template <class ST, int D, int G, bool KV8, int BS>
+// FUSED: the decode step's own K/V write in the same launch (a.step_slots).
+template <class ST, int D, int G, bool KV8, int BS, bool FUSED = false>
 __global__ __launch_bounds__(PCACHE_SPLIT_WAVES* kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int NW = PCACHE_SPLIT_WAVES;
@@ -564,7 +616,7 @@ void decode_split_kernel(DecodeArgs a) {
                    (int64_t)L > (int64_t)a.max_partitions * kPartition;
   if (!bad && part * kPartition >= L) return;  // a partition past the sequence writes nothing
   constexpr int STAGES = KV8 ? PCACHE_SPLIT_STAGES_KV8 : PCACHE_SPLIT_STAGES;
-  decode_unit<ST, D, G, NW, STAGES, TABLE, true, KV8, BS>(a, sm, s, kvh, part);
+  decode_unit<ST, D, G, NW, STAGES, TABLE, true, KV8, BS, G, FUSED>(a, sm, s, kvh, part);
 }
 
 // One-pass path: persistent workgroups.  Turn 0 takes units in index order (unit u =
@@ -574,7 +626,8 @@ void decode_split_kernel(DecodeArgs a) {
 // whose turn-0 unit was the r-th longest receives the r-th shortest unit of turn 1,
 // which evens out the sums across workgroups.  NC > G: several query tokens per
 // sequence, in passes of NC / G tokens (one pass unless max_query_len was understated).
-template <class ST, int D, int G, bool KV8, int BS, int NC = G>
+// FUSED: the decode step's own K/V write in the same launch (a.step_slots).
+template <class ST, int D, int G, bool KV8, int BS, int NC = G, bool FUSED = false>
 __global__ __launch_bounds__((onepass_waves<D, KV8>() * kWave))
 __attribute__((amdgpu_waves_per_eu(KV8 && D == 128 ? PCACHE_ONEPASS_OCC_KV8 : PCACHE_ONEPASS_OCC)))
 void decode_onepass_kernel(DecodeArgs a) {
@@ -599,7 +652,7 @@ void decode_onepass_kernel(DecodeArgs a) {
 
   auto unit = [&](int s, int kvh) __attribute__((always_inline)) {
     int tok0 = 0;
-    while (decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8, BS, NC>(a, sm, s, kvh, 0, tok0))
+    while (decode_unit<ST, D, G, NW, STAGES, PCACHE_ONEPASS_TABLE, false, KV8, BS, NC, FUSED>(a, sm, s, kvh, 0, tok0))
       tok0 += NC / G;
   };
   if (k < units) unit((int)(k / Hkv), (int)(k % Hkv));
@@ -649,12 +702,12 @@ void decode_onepass_kernel(DecodeArgs a) {
 }
 
 // Resident workgroups per CU for the one-pass kernel, queried once per instance.
-template <class ST, int D, int G, bool KV8, int BS, int NC = G>
+template <class ST, int D, int G, bool KV8, int BS, int NC = G, bool FUSED = false>
 int onepass_blocks_per_cu() {
   static int cached = 0;
   if (!cached) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8, BS, NC>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8, BS, NC, FUSED>,
                                                      onepass_waves<D, KV8>() * kWave, 0) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
@@ -665,13 +718,13 @@ int onepass_blocks_per_cu() {
   return cached;
 }
 
-template <class ST, int D, int G, bool KV8, int BS>
-hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
+template <class ST, int D, int G, bool KV8, int BS, bool FUSED>
+hipError_t launch_typed_as(const DecodeArgs& a, bool split, hipStream_t stream) {
   if (split) {
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_split_kernel<ST, D, G, KV8, BS>), dim3((unsigned)units), dim3(PCACHE_SPLIT_WAVES * kWave), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<ST, D, G, KV8, BS, FUSED>), dim3((unsigned)units),
+                       dim3(PCACHE_SPLIT_WAVES * kWave), 0, stream, a);
     return hipGetLastError();
   }
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
@@ -679,12 +732,21 @@ hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
 #ifdef PCACHE_ONEPASS_BLOCKS_PER_CU
   const int64_t slots = (int64_t)device_compute_units() * PCACHE_ONEPASS_BLOCKS_PER_CU;
 #else
-  const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G, KV8, BS>();
+  const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G, KV8, BS, G, FUSED>();
 #endif
   const int64_t grid = units < slots ? units : slots;
-  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, KV8, BS>), dim3((unsigned)grid), dim3(onepass_waves<D, KV8>() * kWave), 0,
-                     stream, a);
+  hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, KV8, BS, G, FUSED>), dim3((unsigned)grid),
+                     dim3(onepass_waves<D, KV8>() * kWave), 0, stream, a);
   return hipGetLastError();
+}
+
+template <class ST, int D, int G, bool KV8, int BS>
+hipError_t launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
+  if (a.step_slots == nullptr) return launch_typed_as<ST, D, G, KV8, BS, false>(a, split, stream);
+  // the fused write moves 16-bit rows; with 8-token blocks and 8 heads per kv head at
+  // head size 128 the fused one-pass kernel would spill registers (not built)
+  if constexpr (KV8 || (BS == 8 && G == 8 && D == 128)) return hipErrorInvalidValue;
+  else return launch_typed_as<ST, D, G, KV8, BS, true>(a, split, stream);
 }
 
 template <class ST, int D, bool KV8, int BS>

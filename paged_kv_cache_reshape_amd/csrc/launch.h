@@ -53,6 +53,13 @@ struct DecodeArgs {
   const int32_t* query_start_loc;
   int64_t total_q;
   int causal;
+  // the decode step's own K/V write, fused (16-bit pools, one token per sequence):
+  // token s = sequence s's newest token, row s of step_key / step_value (elements;
+  // [num_seqs, num_kv_heads, head_size] rows), destination step_slots[s].  NULL: none.
+  const int64_t* step_slots;
+  const void* step_key;
+  const void* step_value;
+  int64_t step_key_stride, step_value_stride;
 };
 
 struct VarlenArgs {

@@ -36,13 +36,13 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
     assert {"pc_reshape_and_cache", "pc_paged_attention_decode", "pc_paged_attention_reduce",
             "pc_paged_attention_plan", "pc_reshape_and_cache_fp8", "pc_paged_attention_decode_fp8",
-            "pc_paged_attention_varlen"} <= set(names)
+            "pc_paged_attention_varlen", "pc_reshape_and_cache_decode"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert pc.abi_version() == 4
+    assert pc.abi_version() == 5
     assert pc.status_string(0) == "ok"
     assert "invalid" in pc.status_string(-1)
     assert "unsupported" in pc.status_string(-2)
@@ -178,6 +178,34 @@ def test_varlen_validation(lib, kw, status):
 def test_varlen_empty_is_a_noop(lib):
     assert _varlen(lib, R=0) == 0
     assert _varlen(lib, T=0, q=None, out=None) == 0
+
+
+def _step(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, krs=1024, vrs=1024, sm=FAKE, k=FAKE, v=FAKE, nb=100,
+             bs=8 * 16 * 128, ts=128, hs=16 * 128, bt=FAKE, W=128, sl=FAKE, S=4, msl=2048, Hq=32, Hkv=8, D=128, B=16,
+             scale=0.088, ps=0, es=None, ml=None, tmp=None, alibi=None, dt=2)
+    a.update(kw)
+    return lib.pc_reshape_and_cache_decode(a["out"], a["q"], a["key"], a["value"], a["krs"], a["vrs"], a["sm"],
+                                           a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"], a["bt"], a["W"],
+                                           a["sl"], a["S"], a["msl"], a["Hq"], a["Hkv"], a["D"], a["B"], a["scale"],
+                                           a["ps"], a["es"], a["ml"], a["tmp"], a["alibi"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), -1), (dict(S=-1), -1), (dict(key=None), -1), (dict(sm=None), -1), (dict(krs=100), -1),
+    (dict(out=None), -1), (dict(ps=512), -1), (dict(nb=0), -1),
+    (dict(dt=0), -2),                                  # fp32: the fused write lives in the matrix-core decode
+    (dict(key=ctypes.c_void_p(0x10008)), -2),          # rows moved in 16-byte pieces
+    (dict(vrs=1028), -2),
+    (dict(D=96, bs=8 * 16 * 96, hs=16 * 96, ts=96, krs=768, vrs=768), -2),
+    (dict(B=8, Hq=64, bs=8 * 8 * 128, hs=8 * 128, W=256), -2),  # no fused kernel: 8-token blocks, G=8, D=128
+])
+def test_step_validation(lib, kw, status):
+    assert _step(lib, **kw) == status
+
+
+def test_step_empty_batch_is_a_noop(lib):
+    assert _step(lib, S=0) == 0
 
 
 def test_reduce_validation(lib):
