@@ -101,6 +101,15 @@ constexpr int onepass_waves() {
 #ifndef PCACHE_SPLIT_WAVES
 #define PCACHE_SPLIT_WAVES 4
 #endif
+// the 8-bit pool's split workgroups: 2 waves ran workload 3 2% faster than 4 (3 and 8
+// waves: 8-11% slower), measured with the non-temporal V loads
+#ifndef PCACHE_SPLIT_WAVES_KV8
+#define PCACHE_SPLIT_WAVES_KV8 2
+#endif
+template <bool KV8>
+constexpr int split_waves() {
+  return KV8 ? PCACHE_SPLIT_WAVES_KV8 : PCACHE_SPLIT_WAVES;
+}
 // waves per SIMD the register allocation must allow (the kernels fit 3 without spills)
 #ifndef PCACHE_SPLIT_OCC
 #define PCACHE_SPLIT_OCC 3
@@ -601,9 +610,9 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 // Split path: workgroup = (kv head, sequence, partition), fastest-varying first.
 // FUSED: the decode step's own K/V write in the same launch (a.step_slots).
 template <class ST, int D, int G, bool KV8, int BS, bool FUSED = false>
-__global__ __launch_bounds__(PCACHE_SPLIT_WAVES* kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
+__global__ __launch_bounds__(split_waves<KV8>() * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
 void decode_split_kernel(DecodeArgs a) {
-  constexpr int NW = PCACHE_SPLIT_WAVES;
+  constexpr int NW = split_waves<KV8>();
   constexpr int TABLE = BS >= 16 ? kPartition / kBlockTokens : kPartition / BS;  // a partition's block ids
   __shared__ UnitLds<NW, D, G, TABLE> sm;
   int64_t id = blockIdx.x;
@@ -724,7 +733,7 @@ hipError_t launch_typed_as(const DecodeArgs& a, bool split, hipStream_t stream) 
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
     if (units == 0) return hipSuccess;
     hipLaunchKernelGGL((decode_split_kernel<ST, D, G, KV8, BS, FUSED>), dim3((unsigned)units),
-                       dim3(PCACHE_SPLIT_WAVES * kWave), 0, stream, a);
+                       dim3(split_waves<KV8>() * kWave), 0, stream, a);
     return hipGetLastError();
   }
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
