@@ -88,9 +88,19 @@ constexpr int kMaxRankedSeqs = 512;     // sequences ranked by length in-kernel 
 #ifndef PCACHE_ONEPASS_OCC_KV8
 #define PCACHE_ONEPASS_OCC_KV8 2
 #endif
-template <int D, bool KV8 = false>
+// several query tokens per sequence (16 score columns) at head size 128: 8 waves ran
+// the speculative-decode workload 5% faster than 12 (the merge of 16 columns per wave
+// through LDS shrinks with the wave count; 4 waves: no gain)
+#ifndef PCACHE_ONEPASS_WAVES_D128_MT
+#define PCACHE_ONEPASS_WAVES_D128_MT 8
+#endif
+#ifndef PCACHE_ONEPASS_OCC_MT
+#define PCACHE_ONEPASS_OCC_MT PCACHE_ONEPASS_OCC
+#endif
+template <int D, bool KV8 = false, bool MT = false>
 constexpr int onepass_waves() {
-  return D == 64 ? PCACHE_ONEPASS_WAVES_D64 : KV8 ? PCACHE_ONEPASS_WAVES_D128_KV8 : PCACHE_ONEPASS_WAVES_D128;
+  return D == 64 ? PCACHE_ONEPASS_WAVES_D64
+                 : KV8 ? PCACHE_ONEPASS_WAVES_D128_KV8 : MT ? PCACHE_ONEPASS_WAVES_D128_MT : PCACHE_ONEPASS_WAVES_D128;
 }
 #ifndef PCACHE_ONEPASS_STAGES
 #define PCACHE_ONEPASS_STAGES 2
@@ -637,10 +647,11 @@ void decode_split_kernel(DecodeArgs a) {
 // sequence, in passes of NC / G tokens (one pass unless max_query_len was understated).
 // FUSED: the decode step's own K/V write in the same launch (a.step_slots).
 template <class ST, int D, int G, bool KV8, int BS, int NC = G, bool FUSED = false>
-__global__ __launch_bounds__((onepass_waves<D, KV8>() * kWave))
-__attribute__((amdgpu_waves_per_eu(KV8 && D == 128 ? PCACHE_ONEPASS_OCC_KV8 : PCACHE_ONEPASS_OCC)))
+__global__ __launch_bounds__((onepass_waves<D, KV8, (NC != G)>() * kWave))
+__attribute__((amdgpu_waves_per_eu(KV8 && D == 128 ? PCACHE_ONEPASS_OCC_KV8
+                                   : (NC != G && D == 128) ? PCACHE_ONEPASS_OCC_MT : PCACHE_ONEPASS_OCC)))
 void decode_onepass_kernel(DecodeArgs a) {
-  constexpr int NW = onepass_waves<D, KV8>();
+  constexpr int NW = onepass_waves<D, KV8, (NC != G)>();
   constexpr int kThreads = NW * kWave;
   constexpr int STAGES = KV8 ? PCACHE_ONEPASS_STAGES_KV8 : PCACHE_ONEPASS_STAGES;
   __shared__ UnitLds<NW, D, NC, PCACHE_ONEPASS_TABLE> sm;
@@ -717,7 +728,7 @@ int onepass_blocks_per_cu() {
   if (!cached) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_onepass_kernel<ST, D, G, KV8, BS, NC, FUSED>,
-                                                     onepass_waves<D, KV8>() * kWave, 0) != hipSuccess ||
+                                                     onepass_waves<D, KV8, (NC != G)>() * kWave, 0) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
       n = 1;
@@ -787,7 +798,7 @@ hipError_t launch_multitoken_typed(const DecodeArgs& a, hipStream_t stream) {
   const int64_t slots = (int64_t)device_compute_units() * onepass_blocks_per_cu<ST, D, G, false, 16, 16>();
   const int64_t grid = units < slots ? units : slots;
   hipLaunchKernelGGL((decode_onepass_kernel<ST, D, G, false, 16, 16>), dim3((unsigned)grid),
-                     dim3(onepass_waves<D>() * kWave), 0, stream, a);
+                     dim3(onepass_waves<D, false, true>() * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
