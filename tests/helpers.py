@@ -97,3 +97,17 @@ def pool_view(wl, pool_arr: np.ndarray, which: str = "k") -> np.ndarray:
     return as_strided(base, shape=(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size),
                       strides=(wl.block_stride * es, wl.token_stride * es, wl.head_stride * es, es),
                       writeable=False)
+
+
+def with_abs_values(wl):
+    """The same workload with every V element replaced by its magnitude (sign bit of
+    the value rows cleared, history and step rows alike).  Dense attention over it
+    gives sum_t p_t |v_t| / sum_t p_t per output element -- the scale of the error
+    that rounding the probabilities p_t before P.V can cause."""
+    import dataclasses
+    sign = np.uint32(0x80000000) if wl.dtype == "f32" else np.uint16(0x8000)
+    return dataclasses.replace(wl, pre_value=wl.pre_value & ~sign, value=wl.value & ~sign)
+
+
+# unit roundoff of the 16-bit types a probability may be rounded to before P.V
+PROB_ROUNDOFF = {"bf16": 2.0 ** -9, "f16": 2.0 ** -11, "f32": 0.0}

@@ -18,7 +18,7 @@ import torch
 import gpu_harness as gh
 import oracle
 import paged_kv_cache_reshape_amd as pc
-from helpers import bits_to_f64
+from helpers import PROB_ROUNDOFF, bits_to_f64, with_abs_values
 from workloads import custom, make_config, nan_bits
 
 pytestmark = pytest.mark.gpu
@@ -206,10 +206,16 @@ def test_split_partials_against_oracle():
     assert np.array_equal(written, ~np.isnan(gm)), "partitions written differ"
     assert np.abs(gm[written] - rm[written]).max() < 1e-5
     assert (np.abs(ge[written] - re[written]) / re[written]).max() < 1e-5
-    # 16-bit storage: the probabilities enter P.V rounded to the storage type (relative
-    # error <= 2^-9), so a partial output may move by up to 2^-9 * max|V|
-    vmax = max(np.abs(bits_to_f64(wl.logical_v(s), wl.dtype)).max() for s in range(S) if wl.seq_lens[s] > 0)
-    assert np.abs(gt[written] - rt[written]).max() < 2.0 ** -8 * vmax
+    # The kernel rounds each probability to the storage type before P.V (relative error
+    # <= u) and sums the normaliser from the unrounded values, so element d of a partial
+    # moves by at most u * sum_t p_t |v_t[d]| / sum_t p_t: the oracle's partials of the
+    # same workload with |V|.  Slack for the fp32 scores, exponentials and sums on top.
+    A, _, _ = oracle.partials(with_abs_values(wl), oracle.filled_pool(with_abs_values(wl)), 512, P)
+    err = np.abs(gt[written] - rt[written])
+    bound = (PROB_ROUNDOFF[wl.dtype] + 2.0 ** -14) * A[written] + 1e-6
+    say(f"split partials bf16: max err {err.max():.3e}, worst err/bound {(err / bound).max():.3f}")
+    assert (err <= bound).all()
+    assert err.max() <= 1e-2
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
