@@ -121,6 +121,57 @@ def _same_device(*ts):
             raise ValueError("tensors on different devices")
 
 
+def _pool_extent(num_blocks: int, block_stride: int, token_stride: int, head_stride: int, block_size: int,
+                 num_kv_heads: int, head_size: int) -> int:
+    """Elements a pool buffer must hold past its base: one past the largest element index
+    the strides can reach (block num_blocks-1, row block_size-1, head num_kv_heads-1)."""
+    return ((num_blocks - 1) * block_stride + (block_size - 1) * token_stride + (num_kv_heads - 1) * head_stride +
+            head_size)
+
+
+def _check_pool(k_pool, v_pool, v_offset: int, num_blocks: int, block_stride: int, token_stride: int,
+                head_stride: int, block_size: int, num_kv_heads: int, head_size: int):
+    """The pool buffers cover every element the layout can address, so no slot or block id
+    the kernels accept can reach past them."""
+    if num_blocks <= 0 or block_stride <= 0 or token_stride <= 0 or head_stride <= 0 or block_size <= 0:
+        raise ValueError("num_blocks, the strides and block_size must be positive")
+    if v_offset < 0:
+        raise ValueError("v_offset must be non-negative")
+    need = _pool_extent(num_blocks, block_stride, token_stride, head_stride, block_size, num_kv_heads, head_size)
+    for t, off, nm in ((k_pool, 0, "k_pool"), (v_pool, v_offset, "v_pool")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+        if t.numel() - off < need:
+            raise ValueError(f"{nm} holds {t.numel() - off} elements past its base but the layout addresses {need}")
+
+
+def _check_seq_inputs(S: int, block_tables, seq_lens):
+    # (max_seq_len against the table width is the library's own check)
+    if block_tables.shape[0] != S:
+        raise ValueError(f"block_tables has {block_tables.shape[0]} rows for {S} sequences")
+    if seq_lens.numel() != S:
+        raise ValueError(f"seq_lens has {seq_lens.numel()} entries for {S} sequences")
+
+
+def _check_partials(S: int, Hq: int, D: int, max_seq_len: int, partition_size: int, exp_sums, max_logits,
+                    tmp_out):
+    if partition_size == 0:
+        if exp_sums is not None or max_logits is not None or tmp_out is not None:
+            raise ValueError("the one-pass path takes no partials")
+        return
+    if exp_sums is None or max_logits is None or tmp_out is None:
+        raise ValueError("the split path needs exp_sums, max_logits and tmp_out")
+    # the decode lays partials out with P = ceil(max_seq_len / partition_size) per row and the
+    # reduce reads them with tmp_out's P, so the two must agree (with max_seq_len 0 nothing
+    # is written or read)
+    P = -(-max_seq_len // partition_size) if partition_size > 0 else 0
+    P = tmp_out.shape[2] if P == 0 and tmp_out.dim() == 4 else P
+    if tuple(exp_sums.shape) != (S, Hq, P) or tuple(max_logits.shape) != (S, Hq, P) or \
+            tuple(tmp_out.shape) != (S, Hq, P, D):
+        raise ValueError(f"partials must be [S, Hq, P] and [S, Hq, P, D] with P = ceil(max_seq_len / "
+                         f"partition_size) = {P}")
+
+
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                       slot_mapping: torch.Tensor, *, num_blocks: int, block_stride: int, token_stride: int,
                       head_stride: int, block_size: int = 16, v_offset: int = 0, stream=None) -> None:
@@ -137,6 +188,7 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tens
         if _DTYPES.get(t.dtype) != dt:
             raise TypeError("key, value and the pool must share one storage dtype")
     T, Hkv, D = key.shape
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size, Hkv, D)
     st = _load().pc_reshape_and_cache(_ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(k_pool),
                                       _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride, head_stride,
                                       _ptr(slot_mapping), T, Hkv, D, block_size, dt, _stream(key, stream))
@@ -168,6 +220,10 @@ def paged_attention_decode(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
     if _DTYPES.get(k_pool.dtype) != dt or _DTYPES.get(v_pool.dtype) != dt:
         raise TypeError("q and the pool must share one storage dtype")
     S, Hq, D = q.shape
+    _check_seq_inputs(S, block_tables, seq_lens)
+    _check_partials(S, Hq, D, max_seq_len, partition_size, exp_sums, max_logits, tmp_out)
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size,
+                num_kv_heads, D)
     st = _load().pc_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
         head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads,
@@ -210,6 +266,12 @@ def reshape_and_cache_decode(out, q: torch.Tensor, key: torch.Tensor, value: tor
     for t in (key, value, k_pool, v_pool):
         if _DTYPES.get(t.dtype) != dt:
             raise TypeError("q, key, value and the pool must share one storage dtype")
+    if key.shape[1] != num_kv_heads or key.shape[2] != D:
+        raise ValueError("key/value rows must hold num_kv_heads x head_size elements")
+    _check_seq_inputs(S, block_tables, seq_lens)
+    _check_partials(S, Hq, D, max_seq_len, partition_size, exp_sums, max_logits, tmp_out)
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size,
+                num_kv_heads, D)
     st = _load().pc_reshape_and_cache_decode(
         _ptr(out), _ptr(q), _ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(slot_mapping), _ptr(k_pool),
         _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride, head_stride, _ptr(block_tables),
@@ -251,6 +313,7 @@ def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_pool: torch.
         raise TypeError("key and value must share one dtype")
     T, Hkv, D = key.shape
     _check_kv_scales(k_scale, v_scale, Hkv, kv_scale_stride)
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size, Hkv, D)
     st = _load().pc_reshape_and_cache_fp8(_ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(k_pool),
                                           _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
                                           head_stride, _ptr(slot_mapping), T, Hkv, D, block_size, _ptr(k_scale),
@@ -286,6 +349,10 @@ def paged_attention_decode_fp8(out, q: torch.Tensor, k_pool: torch.Tensor, v_poo
     _check_kv_scales(k_scale, v_scale, num_kv_heads, kv_scale_stride)
     dt = _dtype_code(q)
     S, Hq, D = q.shape
+    _check_seq_inputs(S, block_tables, seq_lens)
+    _check_partials(S, Hq, D, max_seq_len, partition_size, exp_sums, max_logits, tmp_out)
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size,
+                num_kv_heads, D)
     st = _load().pc_paged_attention_decode_fp8(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
         head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads,
@@ -314,6 +381,10 @@ def paged_attention_varlen(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     R = seq_lens.numel()
     if query_start_loc.numel() != R + 1:
         raise ValueError("query_start_loc must hold num_reqs + 1 entries")
+    if block_tables.shape[0] != R:
+        raise ValueError(f"block_tables has {block_tables.shape[0]} rows for {R} requests")
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size,
+                num_kv_heads, q.shape[2])
     _check_alibi(alibi_slopes, q)
     dt = _dtype_code(q)
     if _DTYPES.get(k_pool.dtype) != dt or _DTYPES.get(v_pool.dtype) != dt:
@@ -336,6 +407,15 @@ def paged_attention_reduce(out: torch.Tensor, exp_sums: torch.Tensor, max_logits
                                   and max_logits.is_contiguous()):
         raise ValueError("contiguous out [S,Hq,D] and partials [S,Hq,P(,D)] expected")
     S, Hq, P, D = tmp_out.shape
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [S, Hq, D] matching tmp_out [S, Hq, P, D]")
+    if tuple(exp_sums.shape) != (S, Hq, P) or tuple(max_logits.shape) != (S, Hq, P):
+        raise ValueError("exp_sums and max_logits must be [S, Hq, P] matching tmp_out")
+    for t in (exp_sums, max_logits, tmp_out):
+        if t.dtype != torch.float32:
+            raise ValueError("partials must be float32")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous() or seq_lens.numel() != S:
+        raise ValueError("seq_lens must be a contiguous int32 [S]")
     st = _load().pc_paged_attention_reduce(_ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out),
                                            _ptr(seq_lens), S, Hq, D, P, partition_size, _dtype_code(out),
                                            _stream(out, stream))
