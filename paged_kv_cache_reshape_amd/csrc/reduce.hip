@@ -5,13 +5,19 @@
 // (s, h) over the n = ceil(seq_len / partition) partitions that hold tokens:
 // M = max m_p, w_p = l_p * exp(m_p - M), out = sum w_p o_p / sum w_p.
 //
-// The work is tiny (4 MiB of partials for 4 sequences of 32768 tokens) and latency
-// bound, so the kernel is built around one round trip to memory: a 256-thread
-// workgroup per (sequence, query head, 32-dim slice of the output); once the
-// sequence's length is known (one scalar load) each thread issues, at once, every
-// load it needs -- m_p, l_p and one 16-byte piece of o_p for each of its partitions
-// p = g, g + 32, ... -- then a block-wide max, the weights, the weighted sums and one
-// LDS reduction over the 32 partition groups.
+// The work is small and latency bound, so both kernels are built around one round
+// trip to memory: once a row's sequence length is known, every load the row needs --
+// m_p, l_p and 16-byte pieces of o_p for each partition p < n -- is issued at once.
+// * Many partitions per row (long sequences, few rows): reduce_kernel, a 256-thread
+//   workgroup per (sequence, query head, 32-dim slice of the output); its threads
+//   take partitions g, g + 32, ... side by side, then a block-wide max, the weights,
+//   the weighted sums and one LDS reduction over the 32 partition groups.
+// * Few partitions per row (at most kRowsMaxParts, i.e. sequences up to 8192 tokens,
+//   typically many rows): reduce_rows_kernel, one wave per (sequence, query head).
+//   The wave's lanes form 64 / (D/4) partition groups of D/4 lanes (a float4 of the
+//   row each); the max and the sums fold across the groups with lane shuffles, so no
+//   barrier and no LDS are involved.  (The slice kernel would leave most of its 32
+//   groups idle there and pay two barriers per workgroup.)
 #include <cmath>
 
 #include "device_common.h"
@@ -123,12 +129,106 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
   }
 }
 
+// ---- few partitions per row: one wave per (sequence, query head) --------------------
+constexpr int kRowsMaxParts = 16;  // partitions a row may have on this kernel
+constexpr int kRowsPerBlock = 4;   // waves (rows) per workgroup
+
+template <class ST, int D>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void reduce_rows_kernel(ReduceArgs a) {
+  constexpr int kLanes = D / 4;               // lanes covering one partition's row (a float4 each)
+  constexpr int kGroupsW = kWave / kLanes;    // partition groups in the wave
+  constexpr int kPer = kRowsMaxParts / kGroupsW;  // partitions per lane, all loads in flight
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t sh = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;  // s * num_q_heads + h
+  if (sh >= (int64_t)a.num_seqs * a.num_q_heads) return;
+  const int s = (int)(sh / a.num_q_heads);
+  const int c = lane % kLanes;
+  const int grp = lane / kLanes;
+  const int L = a.seq_lens[s];  // wave-uniform
+  const int64_t n64 = L <= 0 ? 0 : ((int64_t)L + a.partition_size - 1) / a.partition_size;
+  const bool bad = L < 0 || n64 > a.max_partitions;
+  const int n = bad ? 0 : (int)n64;  // <= max_partitions <= kRowsMaxParts
+  const float* ml = a.max_logits + sh * a.max_partitions;
+  const float* es = a.exp_sums + sh * a.max_partitions;
+  const float4* rows = reinterpret_cast<const float4*>(a.tmp_out + sh * a.max_partitions * D) + c;
+
+  float m[kPer], l[kPer];
+  float4 t[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int p = grp + i * kGroupsW;
+    const bool in = p < n;
+    m[i] = in ? ml[p] : -INFINITY;
+    l[i] = in ? es[p] : 0.f;
+    t[i] = in ? rows[(int64_t)p * (D / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) M = fmaxf(M, m[i]);
+#pragma unroll
+  for (int off = kLanes; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float w = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const float wp = m[i] == -INFINITY ? 0.f : l[i] * __builtin_amdgcn_exp2f((m[i] - M) * kLog2e);
+    w += wp;
+    o.x = fmaf(wp, t[i].x, o.x);
+    o.y = fmaf(wp, t[i].y, o.y);
+    o.z = fmaf(wp, t[i].z, o.z);
+    o.w = fmaf(wp, t[i].w, o.w);
+  }
+#pragma unroll
+  for (int off = kLanes; off < kWave; off <<= 1) {
+    w += __shfl_xor(w, off);
+    o.x += __shfl_xor(o.x, off);
+    o.y += __shfl_xor(o.y, off);
+    o.z += __shfl_xor(o.z, off);
+    o.w += __shfl_xor(o.w, off);
+  }
+  if (grp != 0) return;
+  const float inv = 1.f / w;
+  float r[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = bad ? NAN : (n == 0 ? 0.f : r[e]);
+  const int64_t base = sh * D + 4 * c;
+  if constexpr (ST::kBytes == 4) {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + base) = make_float4(r[0], r[1], r[2], r[3]);
+  } else {
+    const uint32_t lo = to_storage<ST>(r[0]) | (to_storage<ST>(r[1]) << 16);
+    const uint32_t hi = to_storage<ST>(r[2]) | (to_storage<ST>(r[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + base) = make_uint2(lo, hi);
+  }
+}
+
 }  // namespace
+
+template <class ST>
+hipError_t launch_rows(const ReduceArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  if (a.head_size == 128)
+    hipLaunchKernelGGL((reduce_rows_kernel<ST, 128>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((reduce_rows_kernel<ST, 64>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, hipStream_t stream) {
   const int64_t n = (int64_t)a.num_seqs * a.num_q_heads * (a.head_size / kSlice);
   if (n == 0) return hipSuccess;
   if (!reduce_supported(a.head_size)) return hipErrorInvalidValue;
+  // the rows kernel stores 4 output elements at once: out must be aligned to that
+  const uintptr_t out_align = (dtype == 0 ? 16u : 8u) - 1u;
+  if (a.max_partitions <= kRowsMaxParts && (a.head_size == 64 || a.head_size == 128) &&
+      (reinterpret_cast<uintptr_t>(a.out) & out_align) == 0) {
+    switch (dtype) {
+      case 0: return launch_rows<F32>(a, stream);
+      case 1: return launch_rows<F16>(a, stream);
+      case 2: return launch_rows<BF16>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const dim3 grid((unsigned)n), block(kReduceThreads);
   switch (dtype) {
     case 0: hipLaunchKernelGGL((reduce_kernel<F32>), grid, block, 0, stream, a); break;
