@@ -70,14 +70,23 @@ constexpr int kPartition = 512;
 constexpr float kLazy = 8.f;            // log2-domain slack before the exponent reference moves
 constexpr int kMaxRankedSeqs = 512;     // sequences ranked by length in-kernel (beyond: index order)
 
-// One-pass workgroup: one per CU, as many waves as the register allocation lets a
-// CU hold (3 per SIMD at head_size 128, 4 at 64), so the persistent grid fills the
-// chip with one workgroup per CU and the units dealt to it share its waves.
+// One-pass workgroup at head size 128: one per CU, as many waves as the register
+// allocation lets a CU hold (3 per SIMD), so the persistent grid fills the chip with one
+// workgroup per CU and the units dealt to it share its waves.  At head size 64 a unit
+// carries half the bytes per token, and a 16-wave workgroup spent a large share of each
+// unit in its fixed costs (id staging, first loads, merge) with every wave of the CU
+// waiting at them together; two 8-wave workgroups per CU (4 waves per SIMD) overlap one
+// unit's fixed costs with the other's stream: the combined-block workload (128
+// sequences of 1..2048 tokens) ran 12% faster than with 16 waves (4 waves, four
+// workgroups per CU: 8% slower than 16).
 #ifndef PCACHE_ONEPASS_WAVES_D128
 #define PCACHE_ONEPASS_WAVES_D128 12
 #endif
 #ifndef PCACHE_ONEPASS_WAVES_D64
-#define PCACHE_ONEPASS_WAVES_D64 16
+#define PCACHE_ONEPASS_WAVES_D64 8
+#endif
+#ifndef PCACHE_ONEPASS_OCC_D64
+#define PCACHE_ONEPASS_OCC_D64 4
 #endif
 // The 8-bit pool at head size 128 has its own wave count: 8 waves (2 per SIMD) ran the
 // one-pass decode 3% faster than 12 (measured with the non-temporal V loads below);
@@ -648,8 +657,9 @@ void decode_split_kernel(DecodeArgs a) {
 // FUSED: the decode step's own K/V write in the same launch (a.step_slots).
 template <class ST, int D, int G, bool KV8, int BS, int NC = G, bool FUSED = false>
 __global__ __launch_bounds__((onepass_waves<D, KV8, (NC != G)>() * kWave))
-__attribute__((amdgpu_waves_per_eu(KV8 && D == 128 ? PCACHE_ONEPASS_OCC_KV8
-                                   : (NC != G && D == 128) ? PCACHE_ONEPASS_OCC_MT : PCACHE_ONEPASS_OCC)))
+__attribute__((amdgpu_waves_per_eu(D == 64 ? PCACHE_ONEPASS_OCC_D64
+                                   : KV8 ? PCACHE_ONEPASS_OCC_KV8
+                                   : (NC != G) ? PCACHE_ONEPASS_OCC_MT : PCACHE_ONEPASS_OCC)))
 void decode_onepass_kernel(DecodeArgs a) {
   constexpr int NW = onepass_waves<D, KV8, (NC != G)>();
   constexpr int kThreads = NW * kWave;
