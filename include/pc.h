@@ -131,8 +131,8 @@ int pc_reshape_and_cache(const void *key, const void *value, int64_t key_row_str
  * section "How Each K/V Tile Contributes to the Output" (scores = q.k * scale,
  * online softmax with running max, sum and accumulator, output acc / l).  Logical
  * token t of sequence s lives in physical block block_tables[s*max_blocks_per_seq
- * + t/16] at offset t%16 ("How vLLM CUDA Kernels Write and Read the Paged KV
- * Cache", section "Reading logical blocks during attention").
+ * + t/block_size] at offset t%block_size ("How vLLM CUDA Kernels Write and Read
+ * the Paged KV Cache", section "Reading logical blocks during attention").
  *
  *   out               device [num_seqs, num_q_heads, head_size] (one-pass path only)
  *   q                 device [num_seqs, num_q_heads, head_size], contiguous

@@ -618,7 +618,9 @@ int oracle_merge(double *out, const double *tmp_out, const double *max_logits, c
     return OR_OK;
 }
 
-/* The decode and the partials over an E4M3 pool (q, out in fmt). */
+/* Multi-token queries: each packed query row of request r (rows query_start_loc[r] ..
+   query_start_loc[r+1], its newest tokens) attends the positions it may see (causal: up to
+   its own position seq_len - n + i; otherwise all of [0, seq_len)). */
 int oracle_varlen(double *out, const void *q, const void *k_pool, const void *v_pool, int64_t pool_elems,
                   int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
                   const int32_t *block_tables, int max_blocks_per_seq, const int32_t *query_start_loc,
@@ -666,6 +668,7 @@ int oracle_varlen(double *out, const void *q, const void *k_pool, const void *v_
     return run_job(&j, nthreads);
 }
 
+/* The decode and the partials over an E4M3 pool (q, out in fmt). */
 int oracle_decode_kv8(double *out, const void *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t pool_elems,
                       int64_t num_blocks, int64_t block_stride, int64_t token_stride, int64_t head_stride,
                       const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens, int num_seqs,

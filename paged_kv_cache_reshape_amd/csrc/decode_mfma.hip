@@ -452,8 +452,10 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   if (tid == 0) sm.bad = 0;
   if constexpr (FUSED) {
     if (fused_early && w == 0) fused_write();
+    global_barrier();  // the previous unit's readers of sm are done; the row store is visible
+  } else {
+    lds_barrier();  // the previous unit's readers of sm are done
   }
-  lds_barrier();  // the previous unit's readers of sm are done
   if constexpr (FUSED) {
     if (fused && !fused_early && w == 0) fused_write();
   }
@@ -506,7 +508,12 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
         if (staged[r] < 0 || (int64_t)staged[r] >= a.num_blocks) sm.bad = 1;
       }
     }
-    lds_barrier();
+    // fused step: this barrier follows the row store of a unit whose tile holding L - 1 is
+    // read only after it, so it orders global memory too
+    if constexpr (FUSED)
+      global_barrier();
+    else
+      lds_barrier();
 #undef PC_FIRST_LOAD
     if (__builtin_amdgcn_readfirstlane(sm.bad)) {
       bad = true;  // a block id outside the pool: nothing more is read, the outputs become NaN

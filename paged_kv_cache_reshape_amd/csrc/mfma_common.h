@@ -129,5 +129,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier whose workgroup-scope release/acquire covers global memory as well: a global
+// store by one wave before it is visible to every wave's global loads after it, and the
+// compiler may move no global access across it.  (It waits for the wave's outstanding
+// vector memory accesses, loads included.)
+__device__ __forceinline__ void global_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 }  // namespace
 }  // namespace pcache
