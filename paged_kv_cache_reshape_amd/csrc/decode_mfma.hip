@@ -31,8 +31,9 @@
 //   registers from the block id; the per-lane offsets are loop constants.  A ring
 //   of STAGES register sets keeps the next STAGES-1 blocks in flight while one is
 //   consumed.  The ring loop has wave-uniform control flow, issues every load
-//   unconditionally (clamped to the wave's last block) and exits only at its
-//   bottom, so the compiler waits for exactly the ring stage being consumed.
+//   unconditionally and exits only at its bottom, so the compiler waits for exactly
+//   the ring stage being consumed; the steps past the wave's last block load through
+//   a buffer resource of extent 0, which returns zeros without touching memory.
 // * A unit's block ids are staged in LDS by the whole workgroup, which checks them
 //   against the pool once; each wave reads its ids from there one block ahead.
 //
@@ -294,8 +295,11 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 
   // K/V of tile (A, B) into ring slot ST.  16-token blocks: block A.  32: rows 16*B ..
   // of block A.  8: rows 0-7 from block A, 8-15 from block B (each lane addresses its own
-  // block, so these are global loads with 64-bit lane addresses).
-#define PC_LOAD(ST, A, B)                                                                            \
+  // block, so these are global loads with 64-bit lane addresses).  EXT is the extent of the
+  // tile's buffer resources: tile_bytes, or 0 for a ring step that only keeps the load
+  // count static (past the wave's last tile): a buffer load past its extent returns zeros
+  // without a memory access, so such a step costs no HBM traffic (16- and 32-token blocks).
+#define PC_LOAD(ST, A, B, EXT)                                                                       \
   do {                                                                                               \
     if constexpr (BS == 8) {                                                                         \
       const int64_t ka_ = (int64_t)((col < 8) ? (A) : (B)) * block_bytes + k_off8;                   \
@@ -313,8 +317,8 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       }                                                                                              \
     } else {                                                                                         \
       const int64_t boff_ = (int64_t)(A) * block_bytes + (BS == 32 ? (int64_t)(B) * tile_bytes : 0); \
-      const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, tile_bytes);                       \
-      const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, tile_bytes);                       \
+      const __amdgpu_buffer_rsrc_t kr_ = tile_rsrc(kpool + boff_, (EXT));                            \
+      const __amdgpu_buffer_rsrc_t vr_ = tile_rsrc(vpool + boff_, (EXT));                            \
       if constexpr (KV8) {                                                                           \
         _Pragma("unroll") for (int k = 0; k < K8; ++k) kq[ST][k] =                                  \
             __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, k_off + 16 * k, 0, kKCpol)); \
@@ -488,15 +492,16 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     // (issued by every wave, so that the wait for the staged ids below is exact; a wave
     // with no tile in the chunk fetches the chunk's last one and never reads it)
     const int jt0 = cb + min(w, cn - 1);
+    const uint32_t ext0 = w < cn ? tile_bytes : 0u;  // a wave with no tile in the chunk reads nothing
     auto valid = [&](int id) { return (id >= 0 && (int64_t)id < a.num_blocks) ? id : 0; };
 #define PC_FIRST_LOAD()                                                                              \
   do {                                                                                               \
     if constexpr (BS == 16) {                                                                        \
-      PC_LOAD(0, valid(uniform_load(table, jt0)), 0);                                                \
+      PC_LOAD(0, valid(uniform_load(table, jt0)), 0, ext0);                                          \
     } else if constexpr (BS == 32) {                                                                 \
-      PC_LOAD(0, valid(uniform_load(table, jt0 >> 1)), jt0 & 1);                                     \
+      PC_LOAD(0, valid(uniform_load(table, jt0 >> 1)), jt0 & 1, ext0);                               \
     } else {                                                                                         \
-      PC_LOAD(0, valid(uniform_load(table, 2 * jt0)), valid(uniform_load(table, min(2 * jt0 + 1, nblk - 1)))); \
+      PC_LOAD(0, valid(uniform_load(table, 2 * jt0)), valid(uniform_load(table, min(2 * jt0 + 1, nblk - 1))), ext0); \
     }                                                                                                \
   } while (0)
     PC_FIRST_LOAD();
@@ -522,22 +527,23 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     if (nwc == 0) continue;
     if (alibi) ab = slope * kLog2e / cs;
     auto ref_of = [&](int j) -> int2 { return tile_of(w + min(j, nwc - 1) * NW); };
+    auto ext_of = [&](int j) -> uint32_t { return j < nwc ? tile_bytes : 0u; };
 #pragma unroll
     for (int st = 1; st < STAGES - 1; ++st) {
       const int2 t = ref_of(st);
-      PC_LOAD(st, __builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y));
+      PC_LOAD(st, __builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y), ext_of(st));
     }
     int2 ref_next = ref_of(STAGES - 1);
     // The ring turns a whole number of times: a step past the wave's last tile in the
-    // chunk consumes a repeat of that tile (fetched again from cache) with every token
-    // masked, which changes no state.
+    // chunk consumes the zeros of its empty-extent loads with every token masked, which
+    // changes no state.
     int it0 = 0;
     do {
 #pragma unroll
       for (int st = 0; st < STAGES; ++st) {
         const int it = it0 + st;
         PC_LOAD((st + STAGES - 1) % STAGES, __builtin_amdgcn_readfirstlane(ref_next.x),
-                __builtin_amdgcn_readfirstlane(ref_next.y));
+                __builtin_amdgcn_readfirstlane(ref_next.y), ext_of(it + STAGES - 1));
         ref_next = ref_of(it + STAGES);
         // keep the scheduler from sinking the prefetch below the wait for this tile
         __builtin_amdgcn_sched_barrier(0);
