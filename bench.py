@@ -67,6 +67,11 @@ def parse():
     ap.add_argument("--varlen", choices=["prefill", "spec"], default=None,
                     help="time multi-token queries instead: a chunked-prefill step (512-token chunks) or a "
                          "speculative-decode step (4 query tokens per request)")
+    ap.add_argument("--other-configs", default="2,3,4",
+                    help="workloads also timed on their planned path and reported under other_configs "
+                         "(comma list; '' for none)")
+    ap.add_argument("--read-peak-gib", type=int, default=4,
+                    help="GiB read by the streaming-read yardstick (0: skip it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -110,7 +115,7 @@ def cpu_baseline(wl, seconds: float):
     """The fp64 oracle on the host: the step's write plus the decode of the whole batch,
     repeated until about ``seconds`` of wall time have passed."""
     import oracle
-    threads = min(os.cpu_count() or 1, 16)
+    threads = min(host_cpus()[1], 16)
     pool = oracle.filled_pool(wl, step_write=False)
 
     def run(nthreads, budget):
@@ -126,11 +131,140 @@ def cpu_baseline(wl, seconds: float):
     reps, el = run(threads, seconds)
     reps1, el1 = run(1, seconds / 3)
     what = f"full steps (write + fp64 decode of all {wl.num_seqs} sequences) of the same workload"
+    reported, usable = host_cpus()
     return {"value": round(wl.effective_bytes() * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "host_cpus": reported, "host_cpus_usable": usable,
+            "threads_note": "threads = the CPUs this process may use, at most 16 (one GPU's share of the box)",
             "kind": "oracle", "sample": f"{reps} {what} in {el:.1f} s on {threads} host threads",
             "tokens_per_s": round(wl.num_seqs * reps / el, 3),
             "single_thread": {"value": round(wl.effective_bytes() * reps1 / el1 / 1e9, 4), "unit": "GB/s",
                               "cores": 1, "sample": f"{reps1} {what} in {el1:.1f} s on 1 host thread"}}
+
+
+def host_cpus():
+    """(CPUs the host reports, CPUs this process may run on)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return os.cpu_count() or usable, usable
+
+
+def measure_read_peak(torch, pc, gib: int, reps: int = 10):
+    """The streaming-read yardstick (pc_stream_read): every byte of a ``gib`` GiB buffer
+    read once per launch, for both cache policies the decode uses; GB/s of the faster,
+    from HIP events around ``reps`` back-to-back launches on the launch stream."""
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    wgs = 256 * 16
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for pol in (0, 2):
+        for _ in range(3):
+            pc.stream_read(buf, sink, cache_policy=pol)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            pc.stream_read(buf, sink, cache_policy=pol)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates["nt" if pol else "default"] = round(n / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+    del buf
+    return {"gbs": max(rates.values()), "by_cache_policy": rates, "bytes_per_launch": n,
+            "kernel": "stream_read_kernel (pc_stream_read)"}
+
+
+def measure_config(idx: int, steps: int, warmup: int):
+    """One workload on the path the planner picks: the whole step (write, plan, decode
+    and, on the split path, the reduce) by wall clock, and the decode, the reduce and the
+    two together by HIP events around back-to-back launches (pool copies rotating)."""
+    import torch
+    import gpu_harness as gh
+    import paged_kv_cache_reshape_amd as pc
+    from workloads import make_config
+
+    print(f"[bench] other workload {idx}: generating", file=sys.stderr, flush=True)
+    wl = make_config(idx)
+    S, Hq, D = wl.q.shape
+    per_copy = (2 if wl.layout != "combined" else 1) * wl.pool_elems * wl.kv_esize
+    copies = max(1, min(8, -(-(1 << 30) // max(1, wl.kv_bytes())) + 1))
+    copies = max(1, min(copies, int(64e9 // per_copy)))
+    pools = [gh.filled_pool(wl, step_write=False) for _ in range(copies)]
+    inp = gh.DecodeInputs(wl)
+    key, value = gh.to_dev(wl.key, wl.dtype), gh.to_dev(wl.value, wl.dtype)
+    slots = torch.from_numpy(wl.slot_mapping).cuda()
+    out = torch.empty_like(inp.q)
+    msl = inp.max_seq_len
+    dt = gh.TORCH_DT[wl.dtype]
+    ps, P, _ = pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, dt)
+    kw = {}
+    if ps:
+        kw = dict(partition_size=ps, exp_sums=torch.empty((S, Hq, P), device="cuda"),
+                  max_logits=torch.empty((S, Hq, P), device="cuda"), tmp_out=torch.empty((S, Hq, P, D), device="cuda"))
+    stream = torch.cuda.current_stream()
+
+    def decode(i):
+        pool = pools[i % copies]
+        pc.paged_attention_decode(None if ps else out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                  num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pool.layout_kwargs(), **kw)
+
+    def reduce(i):
+        pc.paged_attention_reduce(out, kw["exp_sums"], kw["max_logits"], kw["tmp_out"], inp.seq_lens)
+
+    def call(i):
+        decode(i)
+        if ps:
+            reduce(i)
+
+    def step(i):
+        pool = pools[i % copies]
+        pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **pool.layout_kwargs())
+        pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, dt)
+        call(i)
+
+    def batched(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    step_us = (time.perf_counter() - t0) / steps * 1e6
+    dec_us = batched(decode, steps)
+    red_us = batched(reduce, steps) if ps else 0.0
+    call_us = batched(call, steps)
+    eff = wl.effective_bytes()
+    rec = {"workload": wl.name, "path": "split" if ps else "single", "num_seqs": S, "num_q_heads": Hq,
+           "num_kv_heads": wl.num_kv_heads, "head_size": D, "dtype": wl.dtype, "layout": wl.layout,
+           "effective_bytes_per_step": eff, "us_per_step": round(step_us, 2),
+           "tokens_per_s": round(S / (step_us * 1e-6), 1),
+           "decode_us": round(dec_us, 2), "reduce_us": round(red_us, 2) if ps else None,
+           "call_us": round(call_us, 2),
+           "call_gbs": round(eff / (call_us * 1e-6) / 1e9, 1),
+           "call_frac": round(eff / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "decode_frac": round(eff / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "timing": "call = decode (+ reduce) back to back, HIP events on the launch stream; step = wall clock "
+                     "of write + plan + call", "pool_copies": copies}
+    if wl.prefix_blocks:
+        uniq = wl.unique_kv_bytes() + wl.qo_bytes()
+        rec.update(unique_bytes_per_step=uniq, unique_call_gbs=round(uniq / (call_us * 1e-6) / 1e9, 1),
+                   unique_call_frac=round(uniq / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    del pools
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -345,6 +479,29 @@ def main():
                        "decode_kernel_us_batched": round(wdec_b * 1e3, 2),
                        "value": round(eff / (wel / args.steps) / 1e9, 2)},
     }
+    if ps:
+        res["decode_plus_reduce_us_batched"] = round(batched(lambda i: (decode(pools[i % copies]), pc.paged_attention_reduce(
+            out, es, ml, tmp, inp.seq_lens)), args.steps) * 1e3, 2)
+        res["reduce_kernel_us_batched"] = round(batched(lambda i: pc.paged_attention_reduce(
+            out, es, ml, tmp, inp.seq_lens), args.steps) * 1e3, 2)
+    if wl.prefix_blocks:
+        uniq = wl.unique_kv_bytes() + wl.qo_bytes()
+        res["config"]["unique_bytes_per_step"] = uniq
+        res["unique_bytes"] = {"gbs_step": round(uniq / (ms * 1e-3) / 1e9, 2),
+                               "gbs_decode_launch": round(uniq / (dec_b * 1e-3) / 1e9, 2),
+                               "frac_decode_launch": round(uniq / (dec_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "note": "distinct physical K/V rows read (the shared prefix once) plus q and out"}
+    del pools
+    torch.cuda.empty_cache()
+    if args.read_peak_gib > 0:
+        print("[bench] streaming-read yardstick", file=sys.stderr, flush=True)
+        rp = measure_read_peak(torch, pc, args.read_peak_gib)
+        res["roofline"]["measured_read_peak"] = rp["gbs"]
+        res["roofline"]["frac_of_measured_read_peak"] = round(achieved / rp["gbs"], 4)
+        res["read_peak"] = rp
+    others = [int(x) for x in args.other_configs.split(",") if x.strip() != ""]
+    if others:
+        res["other_configs"] = {str(i): measure_config(i, args.steps, args.warmup) for i in others if i != args.config}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
@@ -448,7 +605,7 @@ def bench_varlen(args):
     if not args.no_cpu_baseline:
         import oracle
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        threads = min(os.cpu_count() or 1, 16)
+        threads = min(host_cpus()[1], 16)
         pool = oracle.filled_pool(wl)
         # a bounded sample: the first requests' query rows (the others get empty ranges)
         k = 1 if args.varlen == "prefill" else wl.num_seqs

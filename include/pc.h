@@ -343,6 +343,25 @@ int pc_paged_attention_reduce(void *out, const float *exp_sums, const float *max
 int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_size, int max_seq_len,
                             int dtype, int *partition_size, int *max_num_partitions, size_t *workspace_bytes);
 
+/*
+ * pc_stream_read -- measurement aid: read `bytes` of device memory once.
+ *
+ * Not a step of the path.  The decode is bound by one read of every K/V byte from HBM
+ * ("vLLM 源码完全拆解（七）", section 性能模型), and this plain streaming read -- each
+ * workgroup a contiguous chunk, 16-byte loads, eight in flight per lane -- measures how
+ * fast one GPU can do that, so a decode's rate can be quoted against it beside the
+ * rated peak.  The words read are folded with XOR into sink[w] (w < num_workgroups)
+ * so the loads are not dead; sink's contents mean nothing.
+ *
+ *   src             device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink            device uint32 [num_workgroups]
+ *   cache_policy    0 (default) or 2 (non-temporal hint, as the decode's V loads)
+ * A chunk of more than 2^31 - 32768 bytes per workgroup gives PC_ERR_UNSUPPORTED.
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ */
+int pc_stream_read(const void *src, int64_t bytes, uint32_t *sink, int num_workgroups, int cache_policy,
+                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,9 @@ The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
   8-bit (OCP E4M3) pool with per-kv-head scales;
 * ``paged_attention_varlen``   -- several query tokens per request (chunked
   prefill, speculative decode), causal, over the same pool;
-* ``reshape_and_cache_decode`` -- a decode step's write and decode in one launch.
+* ``reshape_and_cache_decode`` -- a decode step's write and decode in one launch;
+* ``stream_read``              -- measurement aid: one plain read of a buffer (the
+  yardstick the benchmark quotes the decode's HBM rate against).
 """
 
 from ._native import (  # noqa: F401
@@ -29,4 +31,5 @@ from ._native import (  # noqa: F401
     reshape_and_cache_decode,
     reshape_and_cache_fp8,
     status_string,
+    stream_read,
 )

@@ -64,6 +64,8 @@ def _load():
         lib.pc_paged_attention_plan.restype = i32
         lib.pc_paged_attention_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                                 ctypes.POINTER(i32), ctypes.POINTER(sz)]
+        lib.pc_stream_read.restype = i32
+        lib.pc_stream_read.argtypes = [vp, i64, vp, i32, i32, vp]
         _lib = lib
     return _lib
 
@@ -430,3 +432,14 @@ def paged_attention_plan(num_seqs: int, num_q_heads: int, num_kv_heads: int, hea
                                          _DTYPES[dtype], ctypes.byref(ps), ctypes.byref(mp), ctypes.byref(ws))
     _check("pc_paged_attention_plan", st)
     return ps.value, mp.value, ws.value
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, *, cache_policy: int = 0, stream=None) -> None:
+    """Measurement aid: read every byte of ``src`` once (pc_stream_read); ``sink`` is a uint32
+    (int32) tensor with one entry per workgroup of the launch."""
+    _same_device(src, sink)
+    if not src.is_contiguous() or sink.dtype not in (torch.int32, torch.uint32) or not sink.is_contiguous():
+        raise ValueError("src must be contiguous and sink a contiguous 32-bit integer tensor")
+    st = _load().pc_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), sink.numel(),
+                                cache_policy, _stream(src, stream))
+    _check("pc_stream_read", st)

@@ -216,6 +216,16 @@ def test_reduce_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 4, 512, 9, None) == -1
 
 
+def test_stream_read_validation(lib):
+    f = lib.pc_stream_read
+    assert f(None, 1 << 20, FAKE, 64, 0, None) == -1  # no source
+    assert f(FAKE, 0, FAKE, 64, 0, None) == -1  # nothing to read
+    assert f(FAKE, 1 << 20, FAKE, 0, 0, None) == -1  # no workgroups
+    assert f(FAKE, 1 << 20, FAKE, 64, 1, None) == -1  # cache policy is 0 or 2
+    assert f(FAKE, (1 << 20) + 8, FAKE, 64, 0, None) == -2  # not whole 16-byte vectors
+    assert f(FAKE, 1 << 40, FAKE, 1, 0, None) == -2  # a chunk past 32-bit offsets
+
+
 def test_plan_choices():
     bf16 = torch.bfloat16
     # 64 sequences x 8 kv heads = 512 units: enough work units for a single pass
