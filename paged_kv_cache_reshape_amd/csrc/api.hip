@@ -116,7 +116,20 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   a.step_value = step_value;
   a.step_key_stride = step_key_stride;
   a.step_value_stride = step_value_stride;
-  return status_of(pcache::launch_decode(a, dtype, head_size, split, static_cast<hipStream_t>(stream)));
+  // Head size 64 with a token's kv heads next to each other (NHD, or K then V per block):
+  // one kv head's token rows are 128-byte pieces a whole token row apart.  Kv heads 2p
+  // and 2p+1 are then read together as 256-byte pieces and computed as one head of 128
+  // with twice the query heads (16-bit pools, at most 8 query columns).
+  const int group = num_q_heads / num_kv_heads;
+  const bool pair = !kv8 && dtype != PC_F32 && head_size == 64 && head_stride == head_size && num_kv_heads % 2 == 0 &&
+                    group <= 4 && step_slots == nullptr && pcache::decode_supported(dtype, 128, 2 * group);
+  if (pair) {
+    a.pair = 1;
+    a.num_kv_heads = num_kv_heads / 2;
+    a.head_stride = 2 * head_stride;
+  }
+  return status_of(pcache::launch_decode(a, dtype, pair ? 2 * head_size : head_size, split,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace

@@ -199,6 +199,8 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   constexpr int K8 = KS / 2;        // 16-byte K loads per block and lane (8-bit pool)
   constexpr int kKCpol = PCACHE_K_CPOL;
   constexpr int kVCpol = PCACHE_V_CPOL;
+  // kv head pairs (a.pair): 16-bit pools, one query token, head size 128 = two heads of 64
+  constexpr bool PAIRABLE = !KV8 && !MT && !FUSED && D == 128 && G >= 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -241,7 +243,18 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   // B operand: column `col` (zero for col >= C), dims 32*k + 8*rg .. +8 (16-bit
   // pool) or rg*(D/4) + 8*k .. +8 (8-bit pool, the order its K rows are read in)
   uint4 qb[KS];
-  {
+  if (PAIRABLE && a.pair) {
+    // kv head pair: column c belongs to kv head 2p + (c >= G/2), whose 64 dims are dims
+    // 64*(c >= G/2) .. +64 of the pair's 128-element row; its q fills its own half of the
+    // contraction and zeros the other, so one tile scores both heads
+    const int qc = col < C ? col : C - 1;
+    const int hi = qc >= G / 2;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.num_q_heads + h0 + qc) * (D / 2) + 8 * rg;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      qb[k] = (col < C && (k >= KS / 2) == (bool)hi) ? *reinterpret_cast<const uint4*>(qrow + 32 * (k % (KS / 2)))
+                                                      : make_uint4(0, 0, 0, 0);
+  } else {
     // keep the address inside q for the zero columns
     const int qc = col < C ? col : C - 1;
     const int64_t qr = MT ? (int64_t)(q0 + tok0 + qc / G) : (int64_t)s;
@@ -600,9 +613,13 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     }
     __syncthreads();
   }
-  for (int o = tid; o < C * D; o += kThreads) {
-    const int g = o / D;  // score column
-    const int d = o - g * D;
+  // pairs: column g writes the 64 dims of its own head, dims 64*(g >= G/2) .. of the row
+  const bool pr = PAIRABLE && a.pair;
+  const int Dout = pr ? D / 2 : D;
+  for (int o = tid; o < C * Dout; o += kThreads) {
+    const int g = pr ? o / (D / 2) : o / D;  // score column
+    const int dd = pr ? o - g * (D / 2) : o - g * D;
+    const int d = pr ? dd + (g >= G / 2 ? D / 2 : 0) : dd;
     float M = -INFINITY, ls = 0.f, os = 0.f;
     if constexpr (MT) {
       M = sm.lw[1][g];
@@ -627,13 +644,13 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
                           : (int64_t)s * a.num_q_heads + h0 + g;
     if constexpr (SPLIT) {
       const int64_t sp = sh * a.max_partitions + part;
-      a.tmp_out[sp * D + d] = res;
-      if (d == 0) {
+      a.tmp_out[sp * Dout + dd] = res;
+      if (dd == 0) {
         a.max_logits[sp] = any_bad ? NAN : M * (cs * kLn2);  // back to the natural-log domain
         a.exp_sums[sp] = any_bad ? NAN : ls;
       }
     } else {
-      static_cast<uint16_t*>(a.out)[sh * D + d] = (uint16_t)to_storage<ST>(res);
+      static_cast<uint16_t*>(a.out)[sh * Dout + dd] = (uint16_t)to_storage<ST>(res);
     }
   }
   return MT && tok0 + TPC < n;
@@ -679,7 +696,7 @@ void decode_onepass_kernel(DecodeArgs a) {
   constexpr int STAGES = KV8 ? PCACHE_ONEPASS_STAGES_KV8 : PCACHE_ONEPASS_STAGES;
   __shared__ UnitLds<NW, D, NC, PCACHE_ONEPASS_TABLE> sm;
   __shared__ int order_lds[kMaxRankedSeqs];  // order_lds[rank] = later-turn sequence of that length rank
-  __shared__ int len_lds[kMaxRankedSeqs];
+  __shared__ __align__(16) int len_lds[kMaxRankedSeqs];
   __shared__ int rank0_lds;                  // length rank of this workgroup's turn-0 sequence
 
   const int S = a.num_seqs;
@@ -702,13 +719,18 @@ void decode_onepass_kernel(DecodeArgs a) {
   if (units <= W) return;
   if (ranked) {
     // sequences S0 .. S-1 by length, longest first (ties by index)
+    const int4* l4 = reinterpret_cast<const int4*>(len_lds);
     for (int t = S0 + (int)threadIdx.x; t < S; t += kThreads) {
       const int lt = len_lds[t];
+      auto before = [&](int lu, int u) { return (int)((lu > lt) || (lu == lt && u < t)); };
       int rank = 0;
-      for (int u = S0; u < S; ++u) {
-        const int lu = len_lds[u];
-        rank += (lu > lt) || (lu == lt && u < t);
+      int u = S0;
+      for (; u < S && (u & 3) != 0; ++u) rank += before(len_lds[u], u);
+      for (; u + 4 <= S; u += 4) {
+        const int4 v = l4[u >> 2];
+        rank += before(v.x, u) + before(v.y, u + 1) + before(v.z, u + 2) + before(v.w, u + 3);
       }
+      for (; u < S; ++u) rank += before(len_lds[u], u);
       order_lds[rank] = t;
     }
     // rank of this workgroup's turn-0 sequence among sequences 0 .. S0-1

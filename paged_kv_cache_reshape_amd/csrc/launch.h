@@ -60,6 +60,11 @@ struct DecodeArgs {
   const void* step_key;
   const void* step_value;
   int64_t step_key_stride, step_value_stride;
+  // head size 64 with the kv heads of a token next to each other (head_stride == 64): kv
+  // heads 2p and 2p+1 are read as one head of 128 elements and computed together, G query
+  // heads each; num_kv_heads and head_stride then count pairs, q / out / partials keep
+  // head size 64 (decode_mfma.hip).  0: off.
+  int pair;
 };
 
 struct VarlenArgs {
