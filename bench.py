@@ -72,6 +72,12 @@ def parse():
                          "(comma list; '' for none)")
     ap.add_argument("--read-peak-gib", type=int, default=4,
                     help="GiB read by the streaming-read yardstick (0: skip it)")
+    ap.add_argument("--plan-grid", action="store_true",
+                    help="time the one-pass path against split + reduce over a grid of batch shapes and length "
+                         "mixes (the data the planner is fitted on); one JSON line per shape, then exit")
+    ap.add_argument("--grid-max-gib", type=float, default=6.0, help="--plan-grid: skip shapes above this K/V size")
+    ap.add_argument("--grid-heads", default="32/8,32/32",
+                    help="--plan-grid: num_q_heads/num_kv_heads pairs (comma list)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -288,6 +294,8 @@ def main():
 
     if args.varlen:
         return bench_varlen(args)
+    if args.plan_grid:
+        return bench_plan_grid(args)
 
     import gpu_harness as gh
     import paged_kv_cache_reshape_amd as pc
@@ -624,6 +632,114 @@ def bench_varlen(args):
                                "sample": f"{reps} x fp64 attention of the query rows of the first {k} request(s) "
                                          f"({rows} rows each) in {el_c:.1f} s on {threads} host threads"}
     print(json.dumps(res), flush=True)
+
+
+# --plan-grid: units (= num_seqs * num_kv_heads), longest lengths and length mixes of the grid
+GRID_UNITS = (32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
+GRID_MAX_LEN = (512, 2048, 8192, 32768)
+GRID_MIXES = ("fixed", "uniform", "loguniform")
+
+
+def grid_lengths(rng, S: int, max_len: int, mix: str):
+    """Sequence lengths of one grid shape: all max_len; uniform on [1, max_len]; or
+    floor(exp(U[ln 16, ln(max_len + 1)))) -- each mix with its longest at max_len."""
+    import numpy as np
+    if mix == "fixed":
+        L = np.full(S, max_len)
+    elif mix == "uniform":
+        L = rng.integers(1, max_len + 1, S)
+    else:
+        L = np.floor(np.exp(rng.uniform(np.log(16), np.log(max_len + 1), S))).astype(np.int64)
+    L[0] = max_len
+    return np.clip(L, 1, max_len).astype(np.int32)
+
+
+def bench_plan_grid(args):
+    """Both decode paths on synthetic batches: the pool is random bf16, each sequence's blocks
+    a random draw from it; several table sets over disjoint blocks rotate so that no launch
+    finds the previous one's K/V in cache.  Times are HIP events around back-to-back
+    launches: the one-pass decode, and the split decode with its reduce."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_reshape_amd as pc
+
+    torch.cuda.set_device(0)
+    D, B, dt = 128, 16, torch.bfloat16
+    rng = np.random.Generator(np.random.PCG64(2024))
+    stream = torch.cuda.current_stream()
+
+    def batched(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    heads = [tuple(int(x) for x in hh.split("/")) for hh in args.grid_heads.split(",") if hh]
+    for Hq, Hkv in heads:
+        for units in GRID_UNITS:
+            S = units // Hkv
+            if S < 1:
+                continue
+            for max_len in GRID_MAX_LEN:
+                for mix in GRID_MIXES:
+                    L = grid_lengths(rng, S, max_len, mix)
+                    nb = -(-L // B)
+                    kv = int(L.astype(np.int64).sum()) * Hkv * D * 2 * 2
+                    if kv > args.grid_max_gib * (1 << 30):
+                        continue
+                    sets = max(1, min(8, -(-(2 << 30) // kv)))
+                    need = int(nb.sum())
+                    blocks = need * sets
+                    elems = blocks * Hkv * B * D
+                    k_pool = torch.randn(elems, dtype=dt, device="cuda")
+                    v_pool = torch.randn(elems, dtype=dt, device="cuda")
+                    perm = torch.randperm(blocks, dtype=torch.int32)
+                    W = int(nb.max())
+                    tables = []
+                    for c in range(sets):
+                        t = torch.full((S, W), -1, dtype=torch.int32)
+                        off = c * need
+                        for si in range(S):
+                            t[si, :nb[si]] = perm[off:off + nb[si]]
+                            off += int(nb[si])
+                        tables.append(t.cuda())
+                    sl = torch.from_numpy(L).cuda()
+                    q = torch.randn(S, Hq, D, dtype=dt, device="cuda")
+                    out = torch.empty_like(q)
+                    P = -(-max_len // pc.PARTITION_SIZE)
+                    es = torch.empty((S, Hq, P), device="cuda")
+                    ml = torch.empty_like(es)
+                    tmp = torch.empty((S, Hq, P, D), device="cuda")
+                    lay = dict(num_kv_heads=Hkv, scale=D ** -0.5, num_blocks=blocks, block_stride=Hkv * B * D,
+                               token_stride=D, head_stride=B * D, block_size=B)
+
+                    def single(i):
+                        pc.paged_attention_decode(out, q, k_pool, v_pool, tables[i % sets], sl, max_len, **lay)
+
+                    def split(i):
+                        pc.paged_attention_decode(None, q, k_pool, v_pool, tables[i % sets], sl, max_len,
+                                                  partition_size=pc.PARTITION_SIZE, exp_sums=es, max_logits=ml,
+                                                  tmp_out=tmp, **lay)
+                        pc.paged_attention_reduce(out, es, ml, tmp, sl)
+
+                    n = max(3, min(30, int(5000 // max(1, kv >> 20))))  # about 5 GB read per path
+                    for fn in (single, split):
+                        fn(0)
+                    t1 = batched(single, n)
+                    t2 = batched(split, n)
+                    ps, _, _ = pc.paged_attention_plan(S, Hq, Hkv, D, max_len, dt)
+                    print(json.dumps({"num_q_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "num_seqs": S,
+                                      "units": units, "max_len": max_len, "mix": mix,
+                                      "mean_len": round(float(L.mean()), 1), "kv_bytes": kv,
+                                      "single_us": round(t1, 2), "split_us": round(t2, 2),
+                                      "faster": "single" if t1 <= t2 else "split",
+                                      "plan": "split" if ps else "single", "launches": n}), flush=True)
+                    del k_pool, v_pool, tables, es, ml, tmp
+                    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":
