@@ -330,9 +330,12 @@ int pc_paged_attention_reduce(void *out, const float *exp_sums, const float *max
  *
  * The pages' rule of thumb trades the one-pass path's idle compute units when
  * sequences are few and long against the split path's extra launch and partial
- * traffic ("vLLM 源码完全拆解（七）", section V1与V2).  This planner counts work
- * units of one (sequence, kv head) -- every query head of a group is computed
- * from one read of its K/V -- against the GPU's compute units.
+ * traffic ("vLLM 源码完全拆解（七）", section V1与V2).  This planner estimates both
+ * paths' times from a model of the library's kernels fitted to measurements on
+ * MI355X (see pc_paged_attention_plan_lens), taking every sequence to be max_seq_len
+ * long; work units are (sequence, kv head) -- every query head of a group is computed
+ * from one read of its K/V.  A caller that knows the lengths should use
+ * pc_paged_attention_plan_lens: a skewed batch can favour the other path.
  *
  *   partition_size      out: 0 (one pass) or PC_PARTITION_SIZE (split)
  *   max_num_partitions  out: P for the split path (1 for one pass)
@@ -342,6 +345,36 @@ int pc_paged_attention_reduce(void *out, const float *exp_sums, const float *max
  */
 int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_size, int max_seq_len,
                             int dtype, int *partition_size, int *max_num_partitions, size_t *workspace_bytes);
+
+/*
+ * pc_paged_attention_plan_lens -- pc_paged_attention_plan for a batch whose sequence
+ * lengths the host knows (a serving scheduler does: it builds slot_mapping from them).
+ *
+ * The same choice as pc_paged_attention_plan ("vLLM 源码完全拆解（七）", section
+ * V1与V2: idle compute units with few long sequences against the split path's second
+ * launch and partial traffic), made from the lengths themselves rather than from their
+ * maximum: how the lengths are spread decides how evenly the one-pass workgroups are
+ * loaded, and with it which path is faster.  The library estimates both paths' launch
+ * times from a model of its kernels fitted to measurements on MI355X and returns the
+ * faster.  With partition_size 0 the decode itself picks its one-pass kernel from the
+ * unit count (num_seqs * num_kv_heads) and max_seq_len: one workgroup per unit when
+ * max_seq_len <= 512, or for at least 32 units per compute unit with max_seq_len <=
+ * 2048 (16-bit pools); persistent, longest-first workgroups otherwise.  pc_paged_attention_plan applies the same model with every sequence taken
+ * to be max_seq_len long.
+ *
+ *   seq_lens            HOST int32 [num_seqs], each >= 0 (the decode's seq_lens)
+ *   head_stride         the pool's head_stride in elements (the decode computes pairs of
+ *                       kv heads together when head_size is 64 and the heads of a token
+ *                       are adjacent; the plan accounts for it)
+ *   kv_fp8              1 for an 8-bit pool (pc_paged_attention_decode_fp8), else 0
+ *   partition_size ...  out, as for pc_paged_attention_plan (max_seq_len = the largest
+ *                       seq_lens entry)
+ * Host only: no device work, no allocation visible to the caller.  Returns PC_OK or
+ * PC_ERR_INVALID_ARG (a negative length, a NULL seq_lens with num_seqs > 0, bad sizes).
+ */
+int pc_paged_attention_plan_lens(const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                                 int head_size, int64_t head_stride, int kv_fp8, int dtype, int *partition_size,
+                                 int *max_num_partitions, size_t *workspace_bytes);
 
 /*
  * pc_stream_read -- measurement aid: read `bytes` of device memory once.

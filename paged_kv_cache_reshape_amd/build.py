@@ -34,7 +34,13 @@ def common_flags() -> list[str]:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(REPO, "include"), "-I", CSRC,
         "-Wall", "-Wno-unused-command-line-argument",
-    ]
+    ] + tuning_flags()
+
+
+def tuning_flags() -> list[str]:
+    """Extra -D flags for a tuning build (PCACHE_HIPCC_DEFINES, space separated, e.g.
+    "PCACHE_ONEPASS_KERNEL=1"): the kernels' PCACHE_* macros.  Empty for the library."""
+    return ["-D" + d for d in os.environ.get("PCACHE_HIPCC_DEFINES", "").split() if d]
 
 
 def sources() -> list[str]:

@@ -3,17 +3,20 @@
 // the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <numeric>
+#include <vector>
 
 #include "launch.h"
 #include "pc.h"
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kBlockTokens = 16;
 
 int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
@@ -103,6 +106,7 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   a.block_size = block_size;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.max_partitions = parts;
+  a.max_seq_len = max_seq_len;
   a.exp_sums = exp_sums;
   a.max_logits = max_logits;
   a.tmp_out = tmp_out;
@@ -158,6 +162,135 @@ int device_compute_units() {
   return cached[dev];
 }
 
+// The one-pass path has two kernels.  The persistent one (one workgroup of 12 waves per
+// CU, units dealt longest first) keeps long units streaming but pays each unit's start
+// and merge in series; the grid one (a 4-wave workgroup per unit, three per CU, dealt by
+// the hardware) overlaps those costs across workgroups but leaves the longest units to
+// whichever workgroup draws them.  Of the rules of this form tried against measurements
+// of both kernels and the split path on MI355X (194 batch shapes: 1/8 to 32 units per
+// CU, longest sequences of 512 to 32768 tokens, fixed, uniform and log-uniform mixes),
+// this one left the planner's choice within 5% of the fastest of the three on the most
+// shapes: the grid kernel when the longest sequence fits one 512-token partition, or for
+// at least 32 units per CU with sequences up to 2048 tokens.
+bool onepass_grid(int64_t units, int max_seq_len, int compute_units) {
+  return max_seq_len <= 512 || (units >= 32LL * compute_units && max_seq_len <= 2048);
+}
+
+namespace {
+
+// Estimated launch time (us) of each decode path for a batch, from a model fitted to
+// measurements of the three kernels on MI355X: 194 batch shapes, GQA 32/8 and MHA
+// 32/32, head size 128, bf16, 16-token blocks.
+//   * persistent one pass: each workgroup's units under the kernel's own deal (turn 0
+//     in index order, then sequences ranked longest first and dealt in snake order),
+//     each unit costing its bytes plus a fixed equivalent; the workgroups stream
+//     concurrently, each at 1 / (1/R0 + n/B) with n of them still busy (a shared memory
+//     system: a lone CU streams near R0, a full chip near B in total);
+//   * grid one pass and split: one workgroup per unit (per 512-token partition), three
+//     per CU; the larger of the whole batch at a chip rate, the workgroup slots' total
+//     occupancy, and the longest unit alone at a per-workgroup rate that falls with the
+//     number of busy workgroups; the split path adds its reduce.
+struct Batch {
+  const int32_t* lens;
+  int S, Hq, units_per_seq;  // units_per_seq: kv heads (or kv head pairs)
+  double tok_bytes;          // K and V bytes per token of one unit
+  int cus, wgs_per_cu;       // persistent workgroups: cus * wgs_per_cu
+};
+
+double est_persistent(const Batch& b) {
+  constexpr double R0 = 54.58e3, Bw = 12812e3, o1 = 71.2e3, c1 = 3.21;  // bytes/us, bytes, us
+  const int H = b.units_per_seq, S = b.S;
+  const int64_t U = (int64_t)S * H, W = (int64_t)b.cus * b.wgs_per_cu;
+  std::vector<double> load((size_t)W, 0.0);
+  std::vector<int> cnt((size_t)W, 0);
+  for (int64_t k = 0; k < std::min(U, W); ++k) {
+    load[k] += b.lens[k / H] * b.tok_bytes;
+    ++cnt[k];
+  }
+  if (U > W) {
+    const bool ranked = S <= 512 && W % H == 0;  // as the kernel decides (longest first on)
+    const int S0 = (int)(W / H);
+    std::vector<int> order, rank0;
+    if (ranked) {
+      auto longer = [&](int x, int y) { return b.lens[x] > b.lens[y] || (b.lens[x] == b.lens[y] && x < y); };
+      order.resize(S - S0);
+      std::iota(order.begin(), order.end(), S0);
+      std::sort(order.begin(), order.end(), longer);
+      std::vector<int> first(S0);
+      std::iota(first.begin(), first.end(), 0);
+      std::sort(first.begin(), first.end(), longer);
+      rank0.resize(S0);
+      for (int i = 0; i < S0; ++i) rank0[first[i]] = i;
+    }
+    const int64_t rest = U - W;
+    for (int64_t k = 0; k < W; ++k) {
+      const int64_t r0 = ranked ? (int64_t)rank0[k / H] * H + k % H : k;
+      for (int64_t t = 1; (t - 1) * W < rest; ++t) {
+        const int64_t q = (t - 1) * W + ((t & 1) ? W - 1 - r0 : r0);
+        if (q >= rest) continue;
+        const int s = ranked ? order[q / H] : (int)((W + q) / H);
+        load[k] += b.lens[s] * b.tok_bytes;
+        ++cnt[k];
+      }
+    }
+  }
+  for (int64_t k = 0; k < W; ++k) load[k] += cnt[k] * o1;
+  std::sort(load.begin(), load.end());
+  double t = 0.0, prev = 0.0;
+  int64_t busy = 0;
+  for (double x : load) busy += x > 0.0;
+  for (double x : load) {
+    if (x <= 0.0) continue;
+    t += (x - prev) * (1.0 / R0 + busy / Bw);
+    prev = x;
+    --busy;
+  }
+  return t + c1;
+}
+
+// grid one pass (split = false) or split (split = true)
+double est_per_unit_workgroups(const Batch& b, bool split) {
+  const double BW = split ? 6345e3 : 5840e3, R = split ? 1304e3 : 831e3, t0 = split ? 1.82 : 0.0,
+               c = split ? 9.40 : 3.99, R1 = split ? 44.65e3 : 50.84e3, B1 = split ? 1e12 : 42445e3;
+  double total = 0.0;
+  int64_t n = 0;
+  int lmax = 0;
+  for (int s = 0; s < b.S; ++s) {
+    const int L = std::max(b.lens[s], 0);
+    total += (double)L * b.tok_bytes * b.units_per_seq;
+    n += (int64_t)(split ? (L + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE : 1) * b.units_per_seq;
+    lmax = std::max(lmax, L);
+  }
+  const double slots = 3.0 * b.cus;
+  const double bmax = (split ? std::min(lmax, PC_PARTITION_SIZE) : lmax) * b.tok_bytes;
+  const double r1 = 1.0 / (1.0 / R1 + std::min((double)n, slots) / B1);
+  double t = std::max({total / BW, (n * t0 + total / R) / slots, bmax / r1 + t0}) + c;
+  if (split) t += 0.63e-3 * b.S * b.Hq * ((lmax + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE);
+  return t;
+}
+
+// 1: split, 0: one pass
+int plan_choice(const int32_t* lens, int S, int Hq, int Hkv, int D, bool paired, bool kv8, int dtype) {
+  int lmax = 0;
+  for (int s = 0; s < S; ++s) lmax = std::max(lmax, lens[s]);
+  if (lmax <= PC_PARTITION_SIZE) return 0;  // one partition: the split path only adds its reduce
+  const int cus = device_compute_units();
+  Batch b{};
+  b.lens = lens;
+  b.S = S;
+  b.Hq = Hq;
+  b.units_per_seq = paired ? Hkv / 2 : Hkv;
+  const int Deff = paired ? 2 * D : D;
+  b.tok_bytes = 2.0 * Deff * (kv8 ? 1 : esize(dtype));
+  b.cus = cus;
+  b.wgs_per_cu = (Deff == 64 && !kv8) ? 2 : 1;  // the persistent kernel's workgroups per CU
+  const int64_t units = (int64_t)S * b.units_per_seq;
+  const bool grid = dtype == PC_F32 || (!kv8 && onepass_grid(units, lmax, cus));
+  const double one = grid ? est_per_unit_workgroups(b, false) : est_persistent(b);
+  return est_per_unit_workgroups(b, true) < one ? 1 : 0;
+}
+
+}  // namespace
 }  // namespace pcache
 
 extern "C" {
@@ -334,25 +467,50 @@ int pc_paged_attention_reduce(void* out, const float* exp_sums, const float* max
   return status_of(pcache::launch_reduce(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+int plan_common(const int32_t* lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_size, int max_seq_len,
+                bool paired, bool kv8, int dtype, int* partition_size, int* max_num_partitions,
+                size_t* workspace_bytes) {
+  const int parts = (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE;
+  const bool split = num_seqs > 0 && parts > 1 &&
+                     pcache::plan_choice(lens, num_seqs, num_q_heads, num_kv_heads, head_size, paired, kv8, dtype);
+  const int mp = split ? parts : 1;
+  if (partition_size) *partition_size = split ? PC_PARTITION_SIZE : 0;
+  if (max_num_partitions) *max_num_partitions = mp;
+  if (workspace_bytes)
+    *workspace_bytes = split ? (size_t)num_seqs * num_q_heads * mp * ((size_t)head_size + 2) * sizeof(float) : 0;
+  return PC_OK;
+}
+}  // namespace
+
 int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_size, int max_seq_len,
                             int dtype, int* partition_size, int* max_num_partitions, size_t* workspace_bytes) {
   if (!esize(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || max_seq_len < 0 ||
       num_q_heads % num_kv_heads != 0)
     return PC_ERR_INVALID_ARG;
-  const int parts = (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE;
-  // One (sequence, kv head) unit per workgroup on the one-pass path.  With fewer
-  // units than compute units the one-pass path leaves CUs idle while the long
-  // units stream their history; the split path multiplies the units by the
-  // partition count at the cost of a second launch and the partials' traffic.
-  const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  const bool split = parts > 1 && units < pcache::device_compute_units();
-  const int ps = split ? PC_PARTITION_SIZE : 0;
-  const int mp = split ? parts : 1;
-  if (partition_size) *partition_size = ps;
-  if (max_num_partitions) *max_num_partitions = mp;
-  if (workspace_bytes)
-    *workspace_bytes = split ? (size_t)num_seqs * num_q_heads * mp * ((size_t)head_size + 2) * sizeof(float) : 0;
-  return PC_OK;
+  // lengths unknown: every sequence is taken to be max_seq_len long
+  std::vector<int32_t> lens((size_t)num_seqs, max_seq_len);
+  return plan_common(lens.data(), num_seqs, num_q_heads, num_kv_heads, head_size, max_seq_len, false, false, dtype,
+                     partition_size, max_num_partitions, workspace_bytes);
+}
+
+int pc_paged_attention_plan_lens(const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                                 int head_size, int64_t head_stride, int kv_fp8, int dtype, int* partition_size,
+                                 int* max_num_partitions, size_t* workspace_bytes) {
+  if (!esize(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      num_q_heads % num_kv_heads != 0 || (kv_fp8 != 0 && kv_fp8 != 1) || (num_seqs > 0 && !seq_lens))
+    return PC_ERR_INVALID_ARG;
+  int max_seq_len = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    if (seq_lens[s] < 0) return PC_ERR_INVALID_ARG;
+    max_seq_len = std::max(max_seq_len, seq_lens[s]);
+  }
+  // the decode's own pairing rule (16-bit pools, head size 64, heads side by side)
+  const int group = num_q_heads / num_kv_heads;
+  const bool paired = !kv_fp8 && dtype != PC_F32 && head_size == 64 && head_stride == head_size &&
+                      num_kv_heads % 2 == 0 && group <= 4;
+  return plan_common(seq_lens, num_seqs, num_q_heads, num_kv_heads, head_size, max_seq_len, paired, kv_fp8 != 0,
+                     dtype, partition_size, max_num_partitions, workspace_bytes);
 }
 
 }  // extern "C"

@@ -677,6 +677,26 @@ void decode_split_kernel(DecodeArgs a) {
   decode_unit<ST, D, G, NW, STAGES, TABLE, true, KV8, BS, G, FUSED>(a, sm, s, kvh, part);
 }
 
+// One-pass path for many short units: one workgroup of PCACHE_GRID_WAVES waves per
+// (sequence, kv head), dealt by the hardware as earlier workgroups finish (several per
+// CU, so one unit's start and merge overlap another's stream).
+#ifndef PCACHE_GRID_WAVES
+#define PCACHE_GRID_WAVES 4
+#endif
+#ifndef PCACHE_GRID_TABLE
+#define PCACHE_GRID_TABLE 128  // block ids staged at once (2048 tokens of 16-token blocks)
+#endif
+template <class ST, int D, int G, bool KV8, int BS>
+__global__ __launch_bounds__(PCACHE_GRID_WAVES * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
+void decode_grid_kernel(DecodeArgs a) {
+  constexpr int NW = PCACHE_GRID_WAVES;
+  __shared__ UnitLds<NW, D, G, PCACHE_GRID_TABLE> sm;
+  const int kvh = (int)(blockIdx.x % a.num_kv_heads);
+  const int s = (int)(blockIdx.x / a.num_kv_heads);
+  constexpr int STAGES = KV8 ? PCACHE_SPLIT_STAGES_KV8 : PCACHE_SPLIT_STAGES;
+  decode_unit<ST, D, G, NW, STAGES, PCACHE_GRID_TABLE, false, KV8, BS>(a, sm, s, kvh, 0);
+}
+
 // One-pass path: persistent workgroups.  Turn 0 takes units in index order (unit u =
 // kv head u % Hkv of sequence u / Hkv), so no ranking stands between the launch and the
 // first loads.  While turn 0 runs, the sequence lengths are fetched; after it, the
@@ -794,6 +814,18 @@ hipError_t launch_typed_as(const DecodeArgs& a, bool split, hipStream_t stream) 
   }
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
   if (units == 0) return hipSuccess;
+  // PCACHE_ONEPASS_KERNEL (tuning builds): 1 always persistent, 2 always one workgroup
+  // per unit; 0 (the library) the rule of onepass_grid
+#ifndef PCACHE_ONEPASS_KERNEL
+#define PCACHE_ONEPASS_KERNEL 0
+#endif
+  if constexpr (!FUSED && !KV8 && PCACHE_ONEPASS_KERNEL != 1) {
+    if (PCACHE_ONEPASS_KERNEL == 2 || onepass_grid(units, a.max_seq_len, device_compute_units())) {
+      hipLaunchKernelGGL((decode_grid_kernel<ST, D, G, KV8, BS>), dim3((unsigned)units),
+                         dim3(PCACHE_GRID_WAVES * kWave), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
 #ifdef PCACHE_ONEPASS_BLOCKS_PER_CU
   const int64_t slots = (int64_t)device_compute_units() * PCACHE_ONEPASS_BLOCKS_PER_CU;
 #else

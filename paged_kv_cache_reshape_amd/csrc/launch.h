@@ -35,6 +35,7 @@ struct DecodeArgs {
   int block_size;      // tokens per pool block: 8, 16 or 32
   float scale_log2;    // scale * log2(e): scores are kept in the base-2 domain
   int max_partitions;  // split path only
+  int max_seq_len;     // host-known bound of seq_lens (the one-pass path picks its kernel from it)
   int longest_first;   // one-pass path: workgroup i takes the i-th longest sequence's units
   float* exp_sums;
   float* max_logits;
@@ -114,5 +115,9 @@ bool reduce_supported(int head_size);
 // Compute units of the current device (cached per device; 256, MI355X's count, when
 // no device can be queried).
 int device_compute_units();
+// The one-pass path's kernel for a batch of `units` (sequence, kv head) units whose
+// longest holds max_seq_len tokens: true for one workgroup per unit (dealt by the
+// hardware), false for the persistent, longest-first workgroups (api.hip).
+bool onepass_grid(int64_t units, int max_seq_len, int compute_units);
 
 }  // namespace pcache
