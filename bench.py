@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--grid-max-gib", type=float, default=6.0, help="--plan-grid: skip shapes above this K/V size")
     ap.add_argument("--grid-heads", default="32/8,32/32",
                     help="--plan-grid: num_q_heads/num_kv_heads pairs (comma list)")
+    ap.add_argument("--grid-units", default="", help="--plan-grid: unit counts (comma list; default the grid's)")
+    ap.add_argument("--grid-max-len", default="", help="--plan-grid: longest lengths (comma list)")
+    ap.add_argument("--grid-mixes", default="", help="--plan-grid: length mixes (comma list)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -205,7 +208,7 @@ def measure_config(idx: int, steps: int, warmup: int):
     out = torch.empty_like(inp.q)
     msl = inp.max_seq_len
     dt = gh.TORCH_DT[wl.dtype]
-    ps, P, _ = pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, dt)
+    ps, P, _ = pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, dt)
     kw = {}
     if ps:
         kw = dict(partition_size=ps, exp_sums=torch.empty((S, Hq, P), device="cuda"),
@@ -228,7 +231,7 @@ def measure_config(idx: int, steps: int, warmup: int):
     def step(i):
         pool = pools[i % copies]
         pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **pool.layout_kwargs())
-        pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, dt)
+        pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, dt)
         call(i)
 
     def batched(fn, n):
@@ -326,7 +329,8 @@ def main():
     out = torch.empty_like(inp.q)
     msl = inp.max_seq_len
     if args.path == "plan":
-        ps, P, _ = pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, gh.TORCH_DT[wl.dtype])
+        ps, P, _ = pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride,
+                                                gh.TORCH_DT[wl.dtype], kv_fp8=wl.fp8)
     elif args.path == "split":
         ps, P = pc.PARTITION_SIZE, -(-msl // pc.PARTITION_SIZE)
     else:
@@ -378,7 +382,8 @@ def main():
         pool = pools[i % copies]
         if not fused:
             write(pool)
-        pc.paged_attention_plan(S, Hq, wl.num_kv_heads, D, msl, gh.TORCH_DT[wl.dtype])
+        pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, gh.TORCH_DT[wl.dtype],
+                                     kv_fp8=wl.fp8)
         if ev is not None:
             ev[0].record(stream)
         if fused:
@@ -640,10 +645,13 @@ GRID_MAX_LEN = (512, 2048, 8192, 32768)
 GRID_MIXES = ("fixed", "uniform", "loguniform")
 
 
-def grid_lengths(rng, S: int, max_len: int, mix: str):
+def grid_lengths(S: int, max_len: int, mix: str, num_kv_heads: int = 0):
     """Sequence lengths of one grid shape: all max_len; uniform on [1, max_len]; or
-    floor(exp(U[ln 16, ln(max_len + 1)))) -- each mix with its longest at max_len."""
+    floor(exp(U[ln 16, ln(max_len + 1)))) -- each mix with its longest at max_len.  Each
+    shape draws from its own seed, so a shape's lengths do not depend on the others."""
     import numpy as np
+    key = f"{S}/{num_kv_heads}/{max_len}/{mix}".encode()
+    rng = np.random.Generator(np.random.PCG64(int.from_bytes(key, "little") % (1 << 63)))
     if mix == "fixed":
         L = np.full(S, max_len)
     elif mix == "uniform":
@@ -665,8 +673,10 @@ def bench_plan_grid(args):
 
     torch.cuda.set_device(0)
     D, B, dt = 128, 16, torch.bfloat16
-    rng = np.random.Generator(np.random.PCG64(2024))
     stream = torch.cuda.current_stream()
+    units_list = [int(x) for x in args.grid_units.split(",")] if args.grid_units else GRID_UNITS
+    len_list = [int(x) for x in args.grid_max_len.split(",")] if args.grid_max_len else GRID_MAX_LEN
+    mix_list = args.grid_mixes.split(",") if args.grid_mixes else GRID_MIXES
 
     def batched(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -680,13 +690,13 @@ def bench_plan_grid(args):
 
     heads = [tuple(int(x) for x in hh.split("/")) for hh in args.grid_heads.split(",") if hh]
     for Hq, Hkv in heads:
-        for units in GRID_UNITS:
+        for units in units_list:
             S = units // Hkv
             if S < 1:
                 continue
-            for max_len in GRID_MAX_LEN:
-                for mix in GRID_MIXES:
-                    L = grid_lengths(rng, S, max_len, mix)
+            for max_len in len_list:
+                for mix in mix_list:
+                    L = grid_lengths(S, max_len, mix, Hkv)
                     nb = -(-L // B)
                     kv = int(L.astype(np.int64).sum()) * Hkv * D * 2 * 2
                     if kv > args.grid_max_gib * (1 << 30):
@@ -731,7 +741,7 @@ def bench_plan_grid(args):
                         fn(0)
                     t1 = batched(single, n)
                     t2 = batched(split, n)
-                    ps, _, _ = pc.paged_attention_plan(S, Hq, Hkv, D, max_len, dt)
+                    ps, _, _ = pc.paged_attention_plan_lens(L, Hq, Hkv, D, B * D, dt)
                     print(json.dumps({"num_q_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "num_seqs": S,
                                       "units": units, "max_len": max_len, "mix": mix,
                                       "mean_len": round(float(L.mean()), 1), "kv_bytes": kv,

@@ -7,6 +7,7 @@ The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
 * ``paged_attention_decode``   -- one-pass decode, or the 512-token split partials;
 * ``paged_attention_reduce``   -- log-sum-exp merge of the partials;
 * ``paged_attention_plan``     -- the planner's choice between the two paths;
+* ``paged_attention_plan_lens`` -- the same choice from the host's sequence lengths;
 * ``reshape_and_cache_fp8`` / ``paged_attention_decode_fp8`` -- the same over an
   8-bit (OCP E4M3) pool with per-kv-head scales;
 * ``paged_attention_varlen``   -- several query tokens per request (chunked
@@ -25,6 +26,7 @@ from ._native import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_fp8,
     paged_attention_plan,
+    paged_attention_plan_lens,
     paged_attention_reduce,
     paged_attention_varlen,
     reshape_and_cache,
