@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--grid-units", default="", help="--plan-grid: unit counts (comma list; default the grid's)")
     ap.add_argument("--grid-max-len", default="", help="--plan-grid: longest lengths (comma list)")
     ap.add_argument("--grid-mixes", default="", help="--plan-grid: length mixes (comma list)")
+    ap.add_argument("--grid-prefix", type=int, default=0,
+                    help="--plan-grid: a shared prefix of this many tokens (a multiple of 16): every sequence's "
+                         "first blocks, all but its last, point to the same physical blocks")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -208,7 +211,8 @@ def measure_config(idx: int, steps: int, warmup: int):
     out = torch.empty_like(inp.q)
     msl = inp.max_seq_len
     dt = gh.TORCH_DT[wl.dtype]
-    ps, P, _ = pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, dt)
+    ps, P, _ = pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, dt,
+                                    shared_lens=wl.shared_lens())
     kw = {}
     if ps:
         kw = dict(partition_size=ps, exp_sums=torch.empty((S, Hq, P), device="cuda"),
@@ -231,7 +235,8 @@ def measure_config(idx: int, steps: int, warmup: int):
     def step(i):
         pool = pools[i % copies]
         pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **pool.layout_kwargs())
-        pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, dt)
+        pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, dt,
+                                    shared_lens=wl.shared_lens())
         call(i)
 
     def batched(fn, n):
@@ -330,7 +335,7 @@ def main():
     msl = inp.max_seq_len
     if args.path == "plan":
         ps, P, _ = pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride,
-                                                gh.TORCH_DT[wl.dtype], kv_fp8=wl.fp8)
+                                                gh.TORCH_DT[wl.dtype], kv_fp8=wl.fp8, shared_lens=wl.shared_lens())
     elif args.path == "split":
         ps, P = pc.PARTITION_SIZE, -(-msl // pc.PARTITION_SIZE)
     else:
@@ -383,7 +388,7 @@ def main():
         if not fused:
             write(pool)
         pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, gh.TORCH_DT[wl.dtype],
-                                     kv_fp8=wl.fp8)
+                                     kv_fp8=wl.fp8, shared_lens=wl.shared_lens())
         if ev is not None:
             ev[0].record(stream)
         if fused:
@@ -662,6 +667,14 @@ def grid_lengths(S: int, max_len: int, mix: str, num_kv_heads: int = 0):
     return np.clip(L, 1, max_len).astype(np.int32)
 
 
+def grid_shared_lens(lens, prefix_tokens, block_size=16):
+    """Per sequence of a --plan-grid batch: the leading tokens read from the shared prefix's
+    blocks (every sequence's last block is its own)."""
+    import numpy as np
+    nb = -(-np.asarray(lens, np.int64) // block_size)
+    return (np.minimum(prefix_tokens // block_size, np.maximum(nb - 1, 0)) * block_size).astype(np.int32)
+
+
 def bench_plan_grid(args):
     """Both decode paths on synthetic batches: the pool is random bf16, each sequence's blocks
     a random draw from it; several table sets over disjoint blocks rotate so that no launch
@@ -710,11 +723,15 @@ def bench_plan_grid(args):
                     perm = torch.randperm(blocks, dtype=torch.int32)
                     W = int(nb.max())
                     tables = []
+                    shb = grid_shared_lens(L, args.grid_prefix, B) // B  # shared prefix blocks per sequence
                     for c in range(sets):
                         t = torch.full((S, W), -1, dtype=torch.int32)
                         off = c * need
                         for si in range(S):
                             t[si, :nb[si]] = perm[off:off + nb[si]]
+                            sh = int(shb[si])
+                            if sh > 0:  # the blocks of set c's first sequence serve as the prefix
+                                t[si, :sh] = perm[c * need:c * need + sh]
                             off += int(nb[si])
                         tables.append(t.cuda())
                     sl = torch.from_numpy(L).cuda()
@@ -741,10 +758,12 @@ def bench_plan_grid(args):
                         fn(0)
                     t1 = batched(single, n)
                     t2 = batched(split, n)
-                    ps, _, _ = pc.paged_attention_plan_lens(L, Hq, Hkv, D, B * D, dt)
+                    ps, _, _ = pc.paged_attention_plan_lens(L, Hq, Hkv, D, B * D, dt,
+                                                            shared_lens=grid_shared_lens(L, args.grid_prefix, B))
                     print(json.dumps({"num_q_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "num_seqs": S,
                                       "units": units, "max_len": max_len, "mix": mix,
                                       "mean_len": round(float(L.mean()), 1), "kv_bytes": kv,
+                                      "prefix": args.grid_prefix,
                                       "single_us": round(t1, 2), "split_us": round(t2, 2),
                                       "faster": "single" if t1 <= t2 else "split",
                                       "plan": "split" if ps else "single", "launches": n}), flush=True)

@@ -363,6 +363,14 @@ int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int
  * to be max_seq_len long.
  *
  *   seq_lens            HOST int32 [num_seqs], each >= 0 (the decode's seq_lens)
+ *   shared_lens         NULL, or HOST int32 [num_seqs]: how many leading tokens of each
+ *                       sequence sit in blocks that other sequences of the batch also read
+ *                       (a shared prefix, "PagedAttention kernel: paged KV cache & block
+ *                       tables", section Interviewer follow-ups: sequences sharing a
+ *                       prefix point at the same physical blocks); 0 <= shared_lens[s] <=
+ *                       seq_lens[s].  Shared tokens come partly from cache, the more so on
+ *                       the split path, which reads every sequence's first partitions side
+ *                       by side.
  *   head_stride         the pool's head_stride in elements (the decode computes pairs of
  *                       kv heads together when head_size is 64 and the heads of a token
  *                       are adjacent; the plan accounts for it)
@@ -370,11 +378,12 @@ int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int
  *   partition_size ...  out, as for pc_paged_attention_plan (max_seq_len = the largest
  *                       seq_lens entry)
  * Host only: no device work, no allocation visible to the caller.  Returns PC_OK or
- * PC_ERR_INVALID_ARG (a negative length, a NULL seq_lens with num_seqs > 0, bad sizes).
+ * PC_ERR_INVALID_ARG (a negative length, a shared count outside [0, seq_len], a NULL
+ * seq_lens with num_seqs > 0, bad sizes).
  */
-int pc_paged_attention_plan_lens(const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
-                                 int head_size, int64_t head_stride, int kv_fp8, int dtype, int *partition_size,
-                                 int *max_num_partitions, size_t *workspace_bytes);
+int pc_paged_attention_plan_lens(const int32_t *seq_lens, const int32_t *shared_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_size, int64_t head_stride, int kv_fp8, int dtype,
+                                 int *partition_size, int *max_num_partitions, size_t *workspace_bytes);
 
 /*
  * pc_stream_read -- measurement aid: read `bytes` of device memory once.

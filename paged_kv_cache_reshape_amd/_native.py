@@ -65,7 +65,7 @@ def _load():
         lib.pc_paged_attention_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                                 ctypes.POINTER(i32), ctypes.POINTER(sz)]
         lib.pc_paged_attention_plan_lens.restype = i32
-        lib.pc_paged_attention_plan_lens.argtypes = [vp, i32, i32, i32, i32, i64, i32, i32, ctypes.POINTER(i32),
+        lib.pc_paged_attention_plan_lens.argtypes = [vp, vp, i32, i32, i32, i32, i64, i32, i32, ctypes.POINTER(i32),
                                                      ctypes.POINTER(i32), ctypes.POINTER(sz)]
         lib.pc_stream_read.restype = i32
         lib.pc_stream_read.argtypes = [vp, i64, vp, i32, i32, vp]
@@ -428,16 +428,25 @@ def paged_attention_reduce(out: torch.Tensor, exp_sums: torch.Tensor, max_logits
 
 
 def paged_attention_plan_lens(seq_lens, num_q_heads: int, num_kv_heads: int, head_size: int, head_stride: int,
-                              dtype: torch.dtype, kv_fp8: bool = False):
+                              dtype: torch.dtype, kv_fp8: bool = False, shared_lens=None):
     """(partition_size, max_num_partitions, workspace_bytes) for a batch whose lengths the
-    host knows: ``seq_lens`` is a host sequence of ints (list, numpy array or CPU tensor)."""
+    host knows: ``seq_lens`` (and optional ``shared_lens``, the leading tokens of each
+    sequence in blocks other sequences also read) are host sequences of ints (list, numpy
+    array or CPU tensor)."""
     import numpy as np
-    lens = np.ascontiguousarray(np.asarray(seq_lens.cpu() if isinstance(seq_lens, torch.Tensor) else seq_lens,
-                                           dtype=np.int32))
+
+    def host(x):
+        return np.ascontiguousarray(np.asarray(x.cpu() if isinstance(x, torch.Tensor) else x, dtype=np.int32))
+    lens = host(seq_lens)
+    shared = None if shared_lens is None else host(shared_lens)
+    if shared is not None and shared.shape != lens.shape:
+        raise ValueError("shared_lens must have one entry per sequence")
     ps, mp, ws = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_size_t(0)
-    st = _load().pc_paged_attention_plan_lens(lens.ctypes.data if lens.size else None, int(lens.size), num_q_heads,
-                                              num_kv_heads, head_size, head_stride, int(bool(kv_fp8)),
-                                              _DTYPES[dtype], ctypes.byref(ps), ctypes.byref(mp), ctypes.byref(ws))
+    st = _load().pc_paged_attention_plan_lens(lens.ctypes.data if lens.size else None,
+                                              shared.ctypes.data if shared is not None and shared.size else None,
+                                              int(lens.size), num_q_heads, num_kv_heads, head_size, head_stride,
+                                              int(bool(kv_fp8)), _DTYPES[dtype], ctypes.byref(ps), ctypes.byref(mp),
+                                              ctypes.byref(ws))
     _check("pc_paged_attention_plan_lens", st)
     return ps.value, mp.value, ws.value
 

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int kBlockTokens = 16;
 
 int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
@@ -190,12 +190,23 @@ namespace {
 //     per CU; the larger of the whole batch at a chip rate, the workgroup slots' total
 //     occupancy, and the longest unit alone at a per-workgroup rate that falls with the
 //     number of busy workgroups; the split path adds its reduce.
+// Tokens in blocks that several sequences of the batch read (a shared prefix) come
+// partly from cache: each counts as a fraction of a token read from HBM, fitted per
+// kernel on batches with a shared 1024-token prefix (24 more measured shapes; the grid
+// kernel's on those the one-pass rule gives it): 0.60 persistent, 0.52 grid, 0.46 split
+// (which runs every sequence's first partitions side by side).
 struct Batch {
   const int32_t* lens;
+  const int32_t* shared;     // per sequence: leading tokens in blocks other sequences also read (or NULL)
   int S, Hq, units_per_seq;  // units_per_seq: kv heads (or kv head pairs)
   double tok_bytes;          // K and V bytes per token of one unit
   int cus, wgs_per_cu;       // persistent workgroups: cus * wgs_per_cu
 };
+
+double unit_bytes(const Batch& b, int s, int t0, int t1, double lam) {  // tokens [t0, t1) of sequence s
+  const int sh = b.shared ? std::max(0, std::min(b.shared[s], t1) - t0) : 0;
+  return ((t1 - t0) - sh + lam * sh) * b.tok_bytes;
+}
 
 double est_persistent(const Batch& b) {
   constexpr double R0 = 54.58e3, Bw = 12812e3, o1 = 71.2e3, c1 = 3.21;  // bytes/us, bytes, us
@@ -203,8 +214,9 @@ double est_persistent(const Batch& b) {
   const int64_t U = (int64_t)S * H, W = (int64_t)b.cus * b.wgs_per_cu;
   std::vector<double> load((size_t)W, 0.0);
   std::vector<int> cnt((size_t)W, 0);
+  constexpr double lam = 0.60;
   for (int64_t k = 0; k < std::min(U, W); ++k) {
-    load[k] += b.lens[k / H] * b.tok_bytes;
+    load[k] += unit_bytes(b, (int)(k / H), 0, b.lens[k / H], lam);
     ++cnt[k];
   }
   if (U > W) {
@@ -229,7 +241,7 @@ double est_persistent(const Batch& b) {
         const int64_t q = (t - 1) * W + ((t & 1) ? W - 1 - r0 : r0);
         if (q >= rest) continue;
         const int s = ranked ? order[q / H] : (int)((W + q) / H);
-        load[k] += b.lens[s] * b.tok_bytes;
+        load[k] += unit_bytes(b, s, 0, b.lens[s], lam);
         ++cnt[k];
       }
     }
@@ -252,17 +264,23 @@ double est_persistent(const Batch& b) {
 double est_per_unit_workgroups(const Batch& b, bool split) {
   const double BW = split ? 6345e3 : 5840e3, R = split ? 1304e3 : 831e3, t0 = split ? 1.82 : 0.0,
                c = split ? 9.40 : 3.99, R1 = split ? 44.65e3 : 50.84e3, B1 = split ? 1e12 : 42445e3;
-  double total = 0.0;
+  const double lam = split ? 0.46 : 0.52;
+  double total = 0.0, bmax = 0.0;
   int64_t n = 0;
   int lmax = 0;
   for (int s = 0; s < b.S; ++s) {
     const int L = std::max(b.lens[s], 0);
-    total += (double)L * b.tok_bytes * b.units_per_seq;
-    n += (int64_t)(split ? (L + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE : 1) * b.units_per_seq;
+    const int step = split ? PC_PARTITION_SIZE : std::max(L, 1);
+    for (int t0 = 0; t0 < L; t0 += step) {  // the sequence's units (its partitions on the split path)
+      const double x = unit_bytes(b, s, t0, std::min(L, t0 + step), lam);
+      total += x * b.units_per_seq;
+      bmax = std::max(bmax, x);
+      n += b.units_per_seq;
+    }
+    if (!split && L == 0) n += b.units_per_seq;
     lmax = std::max(lmax, L);
   }
   const double slots = 3.0 * b.cus;
-  const double bmax = (split ? std::min(lmax, PC_PARTITION_SIZE) : lmax) * b.tok_bytes;
   const double r1 = 1.0 / (1.0 / R1 + std::min((double)n, slots) / B1);
   double t = std::max({total / BW, (n * t0 + total / R) / slots, bmax / r1 + t0}) + c;
   if (split) t += 0.63e-3 * b.S * b.Hq * ((lmax + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE);
@@ -270,13 +288,15 @@ double est_per_unit_workgroups(const Batch& b, bool split) {
 }
 
 // 1: split, 0: one pass
-int plan_choice(const int32_t* lens, int S, int Hq, int Hkv, int D, bool paired, bool kv8, int dtype) {
+int plan_choice(const int32_t* lens, const int32_t* shared, int S, int Hq, int Hkv, int D, bool paired, bool kv8,
+                int dtype) {
   int lmax = 0;
   for (int s = 0; s < S; ++s) lmax = std::max(lmax, lens[s]);
   if (lmax <= PC_PARTITION_SIZE) return 0;  // one partition: the split path only adds its reduce
   const int cus = device_compute_units();
   Batch b{};
   b.lens = lens;
+  b.shared = shared;
   b.S = S;
   b.Hq = Hq;
   b.units_per_seq = paired ? Hkv / 2 : Hkv;
@@ -468,12 +488,13 @@ int pc_paged_attention_reduce(void* out, const float* exp_sums, const float* max
 }
 
 namespace {
-int plan_common(const int32_t* lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_size, int max_seq_len,
-                bool paired, bool kv8, int dtype, int* partition_size, int* max_num_partitions,
-                size_t* workspace_bytes) {
+int plan_common(const int32_t* lens, const int32_t* shared, int num_seqs, int num_q_heads, int num_kv_heads,
+                int head_size, int max_seq_len, bool paired, bool kv8, int dtype, int* partition_size,
+                int* max_num_partitions, size_t* workspace_bytes) {
   const int parts = (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE;
   const bool split = num_seqs > 0 && parts > 1 &&
-                     pcache::plan_choice(lens, num_seqs, num_q_heads, num_kv_heads, head_size, paired, kv8, dtype);
+                     pcache::plan_choice(lens, shared, num_seqs, num_q_heads, num_kv_heads, head_size, paired, kv8,
+                                         dtype);
   const int mp = split ? parts : 1;
   if (partition_size) *partition_size = split ? PC_PARTITION_SIZE : 0;
   if (max_num_partitions) *max_num_partitions = mp;
@@ -490,27 +511,28 @@ int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int
     return PC_ERR_INVALID_ARG;
   // lengths unknown: every sequence is taken to be max_seq_len long
   std::vector<int32_t> lens((size_t)num_seqs, max_seq_len);
-  return plan_common(lens.data(), num_seqs, num_q_heads, num_kv_heads, head_size, max_seq_len, false, false, dtype,
-                     partition_size, max_num_partitions, workspace_bytes);
+  return plan_common(lens.data(), nullptr, num_seqs, num_q_heads, num_kv_heads, head_size, max_seq_len, false, false,
+                     dtype, partition_size, max_num_partitions, workspace_bytes);
 }
 
-int pc_paged_attention_plan_lens(const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
-                                 int head_size, int64_t head_stride, int kv_fp8, int dtype, int* partition_size,
-                                 int* max_num_partitions, size_t* workspace_bytes) {
+int pc_paged_attention_plan_lens(const int32_t* seq_lens, const int32_t* shared_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_size, int64_t head_stride, int kv_fp8, int dtype,
+                                 int* partition_size, int* max_num_partitions, size_t* workspace_bytes) {
   if (!esize(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
       num_q_heads % num_kv_heads != 0 || (kv_fp8 != 0 && kv_fp8 != 1) || (num_seqs > 0 && !seq_lens))
     return PC_ERR_INVALID_ARG;
   int max_seq_len = 0;
   for (int s = 0; s < num_seqs; ++s) {
-    if (seq_lens[s] < 0) return PC_ERR_INVALID_ARG;
+    if (seq_lens[s] < 0 || (shared_lens && (shared_lens[s] < 0 || shared_lens[s] > seq_lens[s])))
+      return PC_ERR_INVALID_ARG;
     max_seq_len = std::max(max_seq_len, seq_lens[s]);
   }
   // the decode's own pairing rule (16-bit pools, head size 64, heads side by side)
   const int group = num_q_heads / num_kv_heads;
   const bool paired = !kv_fp8 && dtype != PC_F32 && head_size == 64 && head_stride == head_size &&
                       num_kv_heads % 2 == 0 && group <= 4;
-  return plan_common(seq_lens, num_seqs, num_q_heads, num_kv_heads, head_size, max_seq_len, paired, kv_fp8 != 0,
-                     dtype, partition_size, max_num_partitions, workspace_bytes);
+  return plan_common(seq_lens, shared_lens, num_seqs, num_q_heads, num_kv_heads, head_size, max_seq_len, paired,
+                     kv_fp8 != 0, dtype, partition_size, max_num_partitions, workspace_bytes);
 }
 
 }  // extern "C"

@@ -118,8 +118,9 @@ def decode(pool: DevicePool, inp: DecodeInputs, path: str = "plan", max_seq_len:
     S, Hq, D = inp.q.shape
     msl = inp.max_seq_len if max_seq_len is None else max_seq_len
     if path == "plan":
+        shared = wl.shared_lens() if max_seq_len is None and np.array_equal(inp.seq_lens_host, wl.seq_lens) else None
         ps, _, _ = pc.paged_attention_plan_lens(inp.seq_lens_host, Hq, wl.num_kv_heads, D, wl.head_stride,
-                                                TORCH_DT[wl.dtype], kv_fp8=pool.fp8)
+                                                TORCH_DT[wl.dtype], kv_fp8=pool.fp8, shared_lens=shared)
         path = "split" if ps else "single"
     out = torch.empty_like(inp.q)
     if path == "single":

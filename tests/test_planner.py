@@ -24,28 +24,32 @@ def onepass_grid(units, max_len):
 def rows():
     out = []
     for line in open(TABLE):
-        m = re.match(r"\| (\d+) \| (\d+) \| (\d+) \| (\d+) \| (\w+) \| [\d.]+ \| ([\d.]+) \| ([\d.]+) \| ([\d.]+) \|", line)
+        m = re.match(r"\| (\d+) \| (\d+) \| (\d+) \| (\d+) \| (\w+) \| (\d+) \| [\d.]+ \| ([\d.]+) \| ([\d.]+) "
+                     r"\| ([\d.]+) \|", line)
         if m:
             Hq, Hkv, U, ml = (int(m.group(i)) for i in range(1, 5))
-            out.append((Hq, Hkv, U, ml, m.group(5), float(m.group(6)), float(m.group(7)), float(m.group(8))))
+            out.append((Hq, Hkv, U, ml, m.group(5), int(m.group(6)), float(m.group(7)), float(m.group(8)),
+                        float(m.group(9))))
     return out
 
 
 def test_table_is_complete():
     r = rows()
-    assert len(r) >= 190
+    assert len(r) >= 210
     assert {x[1] for x in r} == {8, 32}
+    assert sum(1 for x in r if x[5]) >= 24  # batches with a shared prefix
 
 
 def test_planner_picks_the_faster_path():
     losses = []
-    for Hq, Hkv, U, ml, mix, t_pers, t_grid, t_split in rows():
+    for Hq, Hkv, U, ml, mix, prefix, t_pers, t_grid, t_split in rows():
         lens = bench.grid_lengths(U // Hkv, ml, mix, Hkv)
-        ps, P, ws = pc.paged_attention_plan_lens(lens, Hq, Hkv, 128, 16 * 128, torch.bfloat16)
+        ps, P, ws = pc.paged_attention_plan_lens(lens, Hq, Hkv, 128, 16 * 128, torch.bfloat16,
+                                                 shared_lens=bench.grid_shared_lens(lens, prefix))
         assert ps in (0, pc.PARTITION_SIZE) and P == (-(-ml // 512) if ps else 1)
         t_one = t_grid if onepass_grid(U, ml) else t_pers
         chosen = t_split if ps else t_one
-        losses.append((chosen / min(t_one, t_split), chosen / min(t_pers, t_grid, t_split), (Hq, Hkv, U, ml, mix)))
+        losses.append((chosen / min(t_one, t_split), chosen / min(t_pers, t_grid, t_split), (Hq, Hkv, U, ml, mix, prefix)))
     within = sum(1 for l2, _, _ in losses if l2 <= 1.05)
     worst = max(losses)
     print(f"planner: {within}/{len(losses)} within 5% of the faster path, worst {worst[0]:.3f} at {worst[2]}; "

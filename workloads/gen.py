@@ -208,6 +208,15 @@ class Workload:
                 used[b] = max(used.get(b, 0), tok)
         return sum(used.values()) * self.num_kv_heads * self.head_size * 2 * self.kv_esize
 
+    def shared_lens(self) -> np.ndarray:
+        """Per sequence: leading tokens in blocks that other sequences also read (the shared
+        prefix's blocks; a sequence's last block is always its own).  All zero without one."""
+        if not self.prefix_blocks:
+            return np.zeros(self.num_seqs, np.int32)
+        nb = -(-self.seq_lens.astype(np.int64) // self.block_size)
+        sh = np.minimum(self.prefix_blocks, np.maximum(nb - 1, 0)) * self.block_size
+        return np.minimum(sh, self.seq_lens).astype(np.int32)
+
     # ----- memory images ---------------------------------------------------------
     def nan_pool(self) -> np.ndarray:
         """One pool buffer (element bits) filled with the quiet-NaN pattern (0x7F for E4M3)."""
