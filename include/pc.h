@@ -27,8 +27,9 @@
  *   except the out-parameters of pc_paged_attention_plan, which are host pointers.
  *   The caller owns every buffer, allocates the split workspace (sizes from
  *   pc_paged_attention_plan) and keeps it alive until the stream has executed the
- *   call.  The library allocates no memory and keeps no state beyond a cached
- *   device-property query.
+ *   call.  The library allocates no memory and keeps no state beyond cached
+ *   device-property and symbol-address queries; the one device buffer it holds is
+ *   a static array of its code object (see pc_paged_attention_split_noalloc).
  * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).  All
  *   device work is enqueued on it and nothing waits for it; a write followed by a
  *   decode on the same stream sees the written tokens.
@@ -78,6 +79,7 @@ typedef enum { PC_F32 = 0, PC_F16 = 1, PC_BF16 = 2 } pc_dtype;
 #define PC_ERR_INVALID_ARG (-1) /* a null pointer, negative size, or inconsistent sizes */
 #define PC_ERR_UNSUPPORTED (-2) /* a valid request the library has no kernel for */
 #define PC_ERR_LAUNCH (-3)      /* the HIP runtime refused the launch */
+#define PC_ERR_TOO_LARGE (-4)   /* the request needs more than the library's fixed buffer holds */
 
 /* Tokens per partition on the split path. */
 #define PC_PARTITION_SIZE 512
@@ -403,6 +405,41 @@ int pc_paged_attention_plan_lens(const int32_t *seq_lens, const int32_t *shared_
  */
 int pc_stream_read(const void *src, int64_t bytes, uint32_t *sink, int num_workgroups, int cache_policy,
                    void *stream);
+
+/* Bytes of the device buffer behind pc_paged_attention_split_noalloc, per GPU. */
+#define PC_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * pc_paged_attention_split_noalloc -- the split decode and its reduce in one call
+ * that allocates nothing, for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid hipMalloc).
+ *
+ * Computes what pc_paged_attention_decode with partition_size = PC_PARTITION_SIZE
+ * followed by pc_paged_attention_reduce computes -- the same kernels, so the same
+ * bits in out -- but keeps exp_sums, max_logits and tmp_out in a device buffer of
+ * PC_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on (from the
+ * first call on that GPU until the process ends).  Arguments as for
+ * pc_paged_attention_decode, without the partition size and the partials; out is
+ * [num_seqs, num_q_heads, head_size] in the storage dtype.
+ *
+ * Limit: with P = ceil(max_seq_len / PC_PARTITION_SIZE) and R = num_seqs *
+ * num_q_heads * P, the partials take 4 * (R * head_size + 2 * R) bytes (each piece
+ * rounded up to 256); more than PC_NOALLOC_SCRATCH_BYTES gives PC_ERR_TOO_LARGE
+ * before anything is enqueued (use pc_paged_attention_decode with a workspace then).
+ * The call makes no hipMalloc, hipFree or other allocating call; on its first call on
+ * a GPU it looks up the buffer's device address (hipGetSymbolAddress).
+ * Concurrency: every call on one GPU uses that GPU's one buffer, which keeps the last
+ * call's contents.  Calls on one GPU whose executions overlap (different streams, or
+ * other threads' streams) race on it; calls in one stream are ordered.
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED, PC_ERR_TOO_LARGE or
+ * PC_ERR_LAUNCH.
+ */
+int pc_paged_attention_split_noalloc(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                     int64_t num_blocks, int64_t block_stride, int64_t token_stride,
+                                     int64_t head_stride, const int32_t *block_tables, int max_blocks_per_seq,
+                                     const int32_t *seq_lens, int num_seqs, int max_seq_len, int num_q_heads,
+                                     int num_kv_heads, int head_size, int block_size, float scale,
+                                     const float *alibi_slopes, int dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -13,12 +13,15 @@ The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
 * ``paged_attention_varlen``   -- several query tokens per request (chunked
   prefill, speculative decode), causal, over the same pool;
 * ``reshape_and_cache_decode`` -- a decode step's write and decode in one launch;
+* ``paged_attention_split_noalloc`` -- the split decode and its reduce with the
+  partials in the library's own device buffer, for callers that cannot allocate;
 * ``stream_read``              -- measurement aid: one plain read of a buffer (the
   yardstick the benchmark quotes the decode's HBM rate against).
 """
 
 from ._native import (  # noqa: F401
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     PARTITION_SIZE,
     PagedCacheError,
     abi_version,
@@ -28,6 +31,7 @@ from ._native import (  # noqa: F401
     paged_attention_plan,
     paged_attention_plan_lens,
     paged_attention_reduce,
+    paged_attention_split_noalloc,
     paged_attention_varlen,
     reshape_and_cache,
     reshape_and_cache_decode,

@@ -15,7 +15,8 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpcache.so")
 
-PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED, PC_ERR_LAUNCH = 0, -1, -2, -3
+PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED, PC_ERR_LAUNCH, PC_ERR_TOO_LARGE = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 128 << 20  # PC_NOALLOC_SCRATCH_BYTES
 PARTITION_SIZE = 512
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _lib = None
@@ -67,6 +68,9 @@ def _load():
         lib.pc_paged_attention_plan_lens.restype = i32
         lib.pc_paged_attention_plan_lens.argtypes = [vp, vp, i32, i32, i32, i32, i64, i32, i32, ctypes.POINTER(i32),
                                                      ctypes.POINTER(i32), ctypes.POINTER(sz)]
+        lib.pc_paged_attention_split_noalloc.restype = i32
+        lib.pc_paged_attention_split_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32,
+                                                         i32, i32, i32, i32, f32, vp, i32, vp]
         lib.pc_stream_read.restype = i32
         lib.pc_stream_read.argtypes = [vp, i64, vp, i32, i32, vp]
         _lib = lib
@@ -235,6 +239,38 @@ def paged_attention_decode(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
         D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(alibi_slopes),
         dt, _stream(q, stream))
     _check("pc_paged_attention_decode", st)
+
+
+def paged_attention_split_noalloc(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                  block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, *,
+                                  num_kv_heads: int, scale: float, num_blocks: int, block_stride: int,
+                                  token_stride: int, head_stride: int, block_size: int = 16, v_offset: int = 0,
+                                  alibi_slopes=None, stream=None) -> None:
+    """The split decode and its reduce into ``out`` [S, Hq, D] with the partials in the
+    library's own device buffer (pc_paged_attention_split_noalloc): allocates nothing.
+    Keyword arguments as for paged_attention_decode."""
+    _same_device(out, q, k_pool, v_pool, block_tables, seq_lens, alibi_slopes)
+    _check_alibi(alibi_slopes, q)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [S, Hq, D]")
+    if out is None or out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous int32 [S, W]")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [S]")
+    dt = _dtype_code(q)
+    if _DTYPES.get(k_pool.dtype) != dt or _DTYPES.get(v_pool.dtype) != dt:
+        raise TypeError("q and the pool must share one storage dtype")
+    S, Hq, D = q.shape
+    _check_seq_inputs(S, block_tables, seq_lens)
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size,
+                num_kv_heads, D)
+    st = _load().pc_paged_attention_split_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
+        head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads,
+        D, block_size, scale, _ptr(alibi_slopes), dt, _stream(q, stream))
+    _check("pc_paged_attention_split_noalloc", st)
 
 
 def reshape_and_cache_decode(out, q: torch.Tensor, key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor,

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 constexpr int kBlockTokens = 16;
 
 int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
@@ -323,6 +323,7 @@ const char* pc_status_string(int status) {
     case PC_ERR_INVALID_ARG: return "invalid argument";
     case PC_ERR_UNSUPPORTED: return "unsupported configuration";
     case PC_ERR_LAUNCH: return "kernel launch failed";
+    case PC_ERR_TOO_LARGE: return "request exceeds the library's fixed device buffer";
     default: return "unknown status";
   }
 }

@@ -42,11 +42,12 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert pc.abi_version() == 7
+    assert pc.abi_version() == 8
     assert pc.status_string(0) == "ok"
     assert "invalid" in pc.status_string(-1)
     assert "unsupported" in pc.status_string(-2)
     assert "launch" in pc.status_string(-3)
+    assert "buffer" in pc.status_string(-4)
 
 
 def _decode(lib, **kw):
