@@ -66,3 +66,28 @@ def test_planner_without_lengths_on_the_workloads():
     assert pc.paged_attention_plan(4, 32, 8, 128, 32768, bf16)[0] == 512  # 32 units x 32768: split
     assert pc.paged_attention_plan(16, 32, 8, 128, 8192, bf16)[0] == 512  # 128 units x 8192: split
     assert pc.paged_attention_plan(512, 32, 8, 128, 8192, bf16)[0] == 0  # 4096 units x 8192: one pass
+
+
+def workload_rows():
+    out = []
+    for line in open(TABLE):
+        m = re.match(r"\| (\d) \| `(\w+)` \| ([\d.]+) \| ([\d.]+) \|", line)
+        if m:
+            out.append((int(m.group(1)), m.group(2), float(m.group(3)), float(m.group(4))))
+    return out
+
+
+def test_planner_on_the_five_workloads():
+    """Each workload, timed on both paths (the table's last section): the planner, given
+    its lengths and its shared prefix tokens, picks the faster."""
+    from workloads import make_config
+    rows = workload_rows()
+    assert [r[0] for r in rows] == [0, 1, 2, 3, 4]
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    for idx, name, t_one, t_split in rows:
+        wl = make_config(idx, contents=False)
+        assert wl.name == name
+        ps, _, _ = pc.paged_attention_plan_lens(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_size,
+                                                 wl.head_stride, dt[wl.dtype], shared_lens=wl.shared_lens())
+        faster_split = t_split < t_one
+        assert bool(ps) == faster_split, (name, ps, t_one, t_split)
