@@ -126,9 +126,14 @@ constexpr int onepass_waves() {
 #ifndef PCACHE_SPLIT_WAVES_KV8
 #define PCACHE_SPLIT_WAVES_KV8 2
 #endif
-template <bool KV8>
+// one query head per kv head (MHA), 16-bit pools: 2 waves ran the mixed-serving workload
+// (256 sequences of 16-8192 tokens, most partitions short) 2-3% faster than 4
+#ifndef PCACHE_SPLIT_WAVES_MHA
+#define PCACHE_SPLIT_WAVES_MHA 2
+#endif
+template <bool KV8, int G>
 constexpr int split_waves() {
-  return KV8 ? PCACHE_SPLIT_WAVES_KV8 : PCACHE_SPLIT_WAVES;
+  return KV8 ? PCACHE_SPLIT_WAVES_KV8 : (G == 1 ? PCACHE_SPLIT_WAVES_MHA : PCACHE_SPLIT_WAVES);
 }
 // waves per SIMD the register allocation must allow (the kernels fit 3 without spills)
 #ifndef PCACHE_SPLIT_OCC
@@ -656,19 +661,24 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   return MT && tok0 + TPC < n;
 }
 
-// Split path: workgroup = (kv head, sequence, partition), fastest-varying first.
+// Split path: workgroup = (kv head, sequence, partition), fastest-varying first, the
+// partitions in descending order.  Every sequence's partition p runs beside the others'
+// partition p (a shared prefix's blocks are then read from L2 by all of them at once;
+// partition fastest ran the mixed-serving workload at half speed), and the last
+// partitions, which only the long sequences have, start first: the grid ends on the
+// dense low partitions instead of a sparse tail of long sequences' last partitions.
 // FUSED: the decode step's own K/V write in the same launch (a.step_slots).
 template <class ST, int D, int G, bool KV8, int BS, bool FUSED = false>
-__global__ __launch_bounds__(split_waves<KV8>() * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
+__global__ __launch_bounds__((split_waves<KV8, G>() * kWave)) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
 void decode_split_kernel(DecodeArgs a) {
-  constexpr int NW = split_waves<KV8>();
+  constexpr int NW = split_waves<KV8, G>();
   constexpr int TABLE = BS >= 16 ? kPartition / kBlockTokens : kPartition / BS;  // a partition's block ids
   __shared__ UnitLds<NW, D, G, TABLE> sm;
   int64_t id = blockIdx.x;
   const int kvh = (int)(id % a.num_kv_heads);
   id /= a.num_kv_heads;
   const int s = (int)(id % a.num_seqs);
-  const int part = (int)(id / a.num_seqs);
+  const int part = a.max_partitions - 1 - (int)(id / a.num_seqs);
   const int L = uniform_load(a.seq_lens, s);
   const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * BS ||
                    (int64_t)L > (int64_t)a.max_partitions * kPartition;
@@ -809,7 +819,7 @@ hipError_t launch_typed_as(const DecodeArgs& a, bool split, hipStream_t stream) 
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
     if (units == 0) return hipSuccess;
     hipLaunchKernelGGL((decode_split_kernel<ST, D, G, KV8, BS, FUSED>), dim3((unsigned)units),
-                       dim3(split_waves<KV8>() * kWave), 0, stream, a);
+                       dim3(split_waves<KV8, G>() * kWave), 0, stream, a);
     return hipGetLastError();
   }
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
