@@ -84,6 +84,9 @@ def parse():
     ap.add_argument("--grid-prefix", type=int, default=0,
                     help="--plan-grid: a shared prefix of this many tokens (a multiple of 16): every sequence's "
                          "first blocks, all but its last, point to the same physical blocks")
+    ap.add_argument("--no-prefix-path", action="store_true",
+                    help="a workload with a shared prefix on the split path: the plain split decode instead of "
+                         "pc_paged_attention_decode_prefix")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -189,7 +192,7 @@ def measure_read_peak(torch, pc, gib: int, reps: int = 10):
             "kernel": "stream_read_kernel (pc_stream_read)"}
 
 
-def measure_config(idx: int, steps: int, warmup: int):
+def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = False):
     """One workload on the path the planner picks: the whole step (write, plan, decode
     and, on the split path, the reduce) by wall clock, and the decode, the reduce and the
     two together by HIP events around back-to-back launches (pool copies rotating)."""
@@ -218,9 +221,19 @@ def measure_config(idx: int, steps: int, warmup: int):
         kw = dict(partition_size=ps, exp_sums=torch.empty((S, Hq, P), device="cuda"),
                   max_logits=torch.empty((S, Hq, P), device="cuda"), tmp_out=torch.empty((S, Hq, P, D), device="cuda"))
     stream = torch.cuda.current_stream()
+    use_prefix = bool(ps and wl.prefix_blocks and not no_prefix_path)
+    if use_prefix:
+        pkw = dict(exp_sums=kw["exp_sums"], max_logits=kw["max_logits"], tmp_out=kw["tmp_out"],
+                   prefix_table=torch.from_numpy(wl.prefix_table()).cuda(),
+                   shared_lens=torch.from_numpy(wl.shared_lens()).cuda())
 
     def decode(i):
         pool = pools[i % copies]
+        if use_prefix:
+            pc.paged_attention_decode_prefix(inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                             num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pkw,
+                                             **pool.layout_kwargs())
+            return
         pc.paged_attention_decode(None if ps else out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
                                   num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pool.layout_kwargs(), **kw)
 
@@ -262,7 +275,8 @@ def measure_config(idx: int, steps: int, warmup: int):
     # the reduce's share of the call (reduces alone back to back would wait on the host)
     red_us = call_us - dec_us
     eff = wl.effective_bytes()
-    rec = {"workload": wl.name, "path": "split" if ps else "single", "num_seqs": S, "num_q_heads": Hq,
+    rec = {"workload": wl.name, "path": ("split (shared prefix)" if use_prefix else "split") if ps else "single",
+           "num_seqs": S, "num_q_heads": Hq,
            "num_kv_heads": wl.num_kv_heads, "head_size": D, "dtype": wl.dtype, "layout": wl.layout,
            "effective_bytes_per_step": eff, "us_per_step": round(step_us, 2),
            "tokens_per_s": round(S / (step_us * 1e-6), 1),
@@ -350,6 +364,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
     fp8 = wl.fp8
     split_kw = dict(partition_size=ps, exp_sums=es, max_logits=ml, tmp_out=tmp) if ps else {}
+    # sequences sharing a prefix, on the split path: each shared tile read once for many
+    use_prefix = bool(ps and wl.prefix_blocks and not fp8 and args.step == "separate" and not args.no_prefix_path)
+    if use_prefix:
+        prefix_kw = dict(prefix_table=torch.from_numpy(wl.prefix_table()).to(dev),
+                         shared_lens=torch.from_numpy(wl.shared_lens()).to(dev))
 
     def write(pool):
         if fp8:
@@ -365,6 +384,11 @@ def main():
                                           pool.k_scale, pool.v_scale, num_kv_heads=wl.num_kv_heads,
                                           scale=float(wl.scale), alibi_slopes=inp.alibi, **pool.layout_kwargs(),
                                           **pool.scale_kwargs(), **split_kw)
+        elif use_prefix:
+            pc.paged_attention_decode_prefix(inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
+                                             num_kv_heads=wl.num_kv_heads, scale=float(wl.scale),
+                                             alibi_slopes=inp.alibi, exp_sums=es, max_logits=ml, tmp_out=tmp,
+                                             **prefix_kw, **pool.layout_kwargs())
         else:
             pc.paged_attention_decode(o, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
                                       num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), alibi_slopes=inp.alibi,
@@ -474,7 +498,8 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads,
-                   "head_size": D, "block_size": wl.block_size, "layout": wl.layout, "path": path,
+                   "head_size": D, "block_size": wl.block_size, "layout": wl.layout,
+                   "path": path + (" (shared prefix)" if use_prefix else ""),
                    "step": "fused" if fused else "separate",
                    "kv_cache": "fp8_e4m3 (per-kv-head scales)" if fp8 else wl.dtype,
                    "alibi": bool(args.alibi),
@@ -490,7 +515,8 @@ def main():
         "unfused_decode_kernel_us_batched": round(plain_b * 1e3, 2) if fused else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("decode_split_kernel" if ps else "decode_onepass_kernel") +
+                     "kernel": ("decode_split_kernel + decode_prefix_kernel" if use_prefix else
+                                "decode_split_kernel" if ps else "decode_onepass_kernel") +
                                (" (with the step's K/V write)" if fused else ""),
                      "bytes_per_launch": launch_bytes, "launch_us": round(dec_b * 1e3, 2),
                      "timing": "HIP events around back-to-back launches on the launch stream"},
@@ -521,7 +547,8 @@ def main():
         res["read_peak"] = rp
     others = [int(x) for x in args.other_configs.split(",") if x.strip() != ""]
     if others:
-        res["other_configs"] = {str(i): measure_config(i, args.steps, args.warmup) for i in others if i != args.config}
+        res["other_configs"] = {str(i): measure_config(i, args.steps, args.warmup, args.no_prefix_path)
+                                for i in others if i != args.config}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

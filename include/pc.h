@@ -11,6 +11,8 @@
  *                              softmax . V -- either in one pass, or per 512-token
  *                              partition writing partial results;
  *   pc_paged_attention_reduce  merge the partitions' partial results (log-sum-exp);
+ *   pc_paged_attention_decode_prefix  the split path for sequences sharing a prefix,
+ *                              each shared tile read once for many sequences;
  *   pc_paged_attention_plan    choose between the one-pass and the split path;
  *   pc_paged_attention_varlen  several query tokens per request (chunked prefill,
  *                              speculative decode) over the same paged history;
@@ -175,6 +177,46 @@ int pc_paged_attention_decode(void *out, const void *q, const void *k_pool, cons
                               int num_kv_heads, int head_size, int block_size, float scale, int partition_size,
                               float *exp_sums, float *max_logits, float *tmp_out, const float *alibi_slopes,
                               int dtype, void *stream);
+
+/*
+ * pc_paged_attention_decode_prefix -- the split path's decode for a batch whose
+ * sequences share a common prefix: the same partials as pc_paged_attention_decode with
+ * partition_size = PC_PARTITION_SIZE, computed with one read of each prefix tile for
+ * many sequences at once.
+ *
+ * Sequences that share a prefix point their first table entries at the same physical
+ * blocks ("PagedAttention kernel: paged KV cache & block tables", section Interviewer
+ * follow-ups).  Each such block is then read by every sharing sequence.  Here the
+ * caller names the shared blocks.  For every partition that a sequence's shared tokens
+ * cover completely, one workgroup per kv head computes that partition's partials for
+ * 16 / G sequences at once (G query heads per kv head): each K/V tile is read once and
+ * scored against all their queries.  The remaining partitions run as on the split path.
+ * Follow with pc_paged_attention_reduce as usual.  The results are the split path's, up
+ * to rounding.
+ *
+ *   all arguments but the three below: as for pc_paged_attention_decode with
+ *                       partition_size = PC_PARTITION_SIZE (exp_sums, max_logits and
+ *                       tmp_out required, [num_seqs, num_q_heads, P(, head_size)])
+ *   prefix_table        device int32 [prefix_blocks]: the shared blocks, in token order
+ *   prefix_blocks       >= 0; 0: no prefix (exactly the split decode)
+ *   shared_lens         device int32 [num_seqs]: sequence s's tokens [0, shared_lens[s])
+ *                       lie in prefix_table's blocks, i.e. its table's first
+ *                       ceil(shared_lens[s] / 16) entries equal prefix_table's; 0 for a
+ *                       sequence that shares nothing.  Must not exceed seq_lens[s] or
+ *                       prefix_blocks * 16.
+ * fp16 / bf16 pools of 16-token blocks with a prefix (else PC_ERR_UNSUPPORTED).  A
+ * sequence whose shared_lens entry exceeds its length or the prefix, or whose table
+ * differs from prefix_table over a partition its shared tokens cover, gets NaN
+ * partials there (so NaN outputs after the reduce) instead of a wrong value.
+ * Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED or PC_ERR_LAUNCH.
+ */
+int pc_paged_attention_decode_prefix(const void *q, const void *k_pool, const void *v_pool, int64_t num_blocks,
+                                     int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                     const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens,
+                                     int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
+                                     int block_size, float scale, float *exp_sums, float *max_logits, float *tmp_out,
+                                     const float *alibi_slopes, const int32_t *prefix_table, int prefix_blocks,
+                                     const int32_t *shared_lens, int dtype, void *stream);
 
 /*
  * pc_reshape_and_cache_fp8 -- write new K/V rows into an 8-bit (OCP E4M3) pool.

@@ -6,6 +6,8 @@ The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
 * ``reshape_and_cache``        -- scatter new K/V rows through ``slot_mapping``;
 * ``paged_attention_decode``   -- one-pass decode, or the 512-token split partials;
 * ``paged_attention_reduce``   -- log-sum-exp merge of the partials;
+* ``paged_attention_decode_prefix`` -- the split path's partials for sequences sharing a
+  prefix, each shared tile read once for many sequences;
 * ``paged_attention_plan``     -- the planner's choice between the two paths;
 * ``paged_attention_plan_lens`` -- the same choice from the host's sequence lengths;
 * ``reshape_and_cache_fp8`` / ``paged_attention_decode_fp8`` -- the same over an
@@ -27,6 +29,7 @@ from ._native import (  # noqa: F401
     abi_version,
     library,
     paged_attention_decode,
+    paged_attention_decode_prefix,
     paged_attention_decode_fp8,
     paged_attention_plan,
     paged_attention_plan_lens,

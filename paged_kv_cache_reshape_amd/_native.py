@@ -68,6 +68,9 @@ def _load():
         lib.pc_paged_attention_plan_lens.restype = i32
         lib.pc_paged_attention_plan_lens.argtypes = [vp, vp, i32, i32, i32, i32, i64, i32, i32, ctypes.POINTER(i32),
                                                      ctypes.POINTER(i32), ctypes.POINTER(sz)]
+        lib.pc_paged_attention_decode_prefix.restype = i32
+        lib.pc_paged_attention_decode_prefix.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32,
+                                                         i32, i32, i32, f32, vp, vp, vp, vp, vp, i32, vp, i32, vp]
         lib.pc_paged_attention_split_noalloc.restype = i32
         lib.pc_paged_attention_split_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32,
                                                          i32, i32, i32, i32, f32, vp, i32, vp]
@@ -239,6 +242,47 @@ def paged_attention_decode(out, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
         D, block_size, scale, partition_size, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(alibi_slopes),
         dt, _stream(q, stream))
     _check("pc_paged_attention_decode", st)
+
+
+def paged_attention_decode_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                  block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, *,
+                                  num_kv_heads: int, scale: float, num_blocks: int, block_stride: int,
+                                  token_stride: int, head_stride: int, exp_sums, max_logits, tmp_out,
+                                  prefix_table, shared_lens, block_size: int = 16, v_offset: int = 0,
+                                  alibi_slopes=None, stream=None) -> None:
+    """The split path's partials for sequences sharing a prefix (pc_paged_attention_decode_prefix):
+    ``prefix_table`` int32 [prefix_blocks] the shared blocks, ``shared_lens`` int32 [S] each
+    sequence's tokens in them.  Follow with paged_attention_reduce."""
+    _same_device(q, k_pool, v_pool, block_tables, seq_lens, exp_sums, max_logits, tmp_out, alibi_slopes,
+                 prefix_table, shared_lens)
+    _check_alibi(alibi_slopes, q)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [S, Hq, D]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous int32 [S, W]")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [S]")
+    for t in (exp_sums, max_logits, tmp_out):
+        if t is None or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("partials must be contiguous float32")
+    dt = _dtype_code(q)
+    if _DTYPES.get(k_pool.dtype) != dt or _DTYPES.get(v_pool.dtype) != dt:
+        raise TypeError("q and the pool must share one storage dtype")
+    S, Hq, D = q.shape
+    if prefix_table.dtype != torch.int32 or prefix_table.dim() != 1 or not prefix_table.is_contiguous():
+        raise ValueError("prefix_table must be a contiguous int32 [prefix_blocks]")
+    if shared_lens.dtype != torch.int32 or not shared_lens.is_contiguous() or shared_lens.numel() != S:
+        raise ValueError("shared_lens must be a contiguous int32 [S]")
+    _check_seq_inputs(S, block_tables, seq_lens)
+    _check_partials(S, Hq, D, max_seq_len, PARTITION_SIZE, exp_sums, max_logits, tmp_out)
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size,
+                num_kv_heads, D)
+    st = _load().pc_paged_attention_decode_prefix(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride, head_stride,
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, num_kv_heads, D, block_size,
+        scale, _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(alibi_slopes), _ptr(prefix_table),
+        prefix_table.numel(), _ptr(shared_lens), dt, _stream(q, stream))
+    _check("pc_paged_attention_decode_prefix", st)
 
 
 def paged_attention_split_noalloc(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 constexpr int kBlockTokens = 16;
 
 int esize(int dtype) { return dtype == PC_F32 ? 4 : (dtype == PC_F16 || dtype == PC_BF16) ? 2 : 0; }
@@ -56,7 +56,8 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
                 float* max_logits, float* tmp_out, const float* alibi_slopes, const float* k_scale,
                 const float* v_scale, int64_t kv_scale_stride, int dtype, bool kv8, void* stream,
                 const int64_t* step_slots = nullptr, const void* step_key = nullptr,
-                const void* step_value = nullptr, int64_t step_key_stride = 0, int64_t step_value_stride = 0) {
+                const void* step_value = nullptr, int64_t step_key_stride = 0, int64_t step_value_stride = 0,
+                const int32_t* prefix_table = nullptr, int prefix_blocks = 0, const int32_t* shared_lens = nullptr) {
   const int es = esize(dtype);
   if (!es || num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_size <= 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0 || (kv8 && kv_scale_stride < 0))
@@ -88,6 +89,8 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   const int parts = split ? (max_seq_len + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE : 1;
   if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX) return PC_ERR_UNSUPPORTED;
   if (split && parts == 0) return PC_OK;  // every sequence is empty: no partials exist
+  // a common prefix (split path): fp16 / bf16 pools of 16-token blocks
+  if (shared_lens && (dtype == PC_F32 || kv8 || block_size != kBlockTokens)) return PC_ERR_UNSUPPORTED;
   pcache::DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -120,20 +123,26 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   a.step_value = step_value;
   a.step_key_stride = step_key_stride;
   a.step_value_stride = step_value_stride;
+  a.prefix_table = prefix_table;
+  a.prefix_blocks = prefix_blocks;
+  a.shared_lens = shared_lens;
   // Head size 64 with a token's kv heads next to each other (NHD, or K then V per block):
   // one kv head's token rows are 128-byte pieces a whole token row apart.  Kv heads 2p
   // and 2p+1 are then read together as 256-byte pieces and computed as one head of 128
   // with twice the query heads (16-bit pools, at most 8 query columns).
   const int group = num_q_heads / num_kv_heads;
   const bool pair = !kv8 && dtype != PC_F32 && head_size == 64 && head_stride == head_size && num_kv_heads % 2 == 0 &&
-                    group <= 4 && step_slots == nullptr && pcache::decode_supported(dtype, 128, 2 * group);
+                    group <= 4 && step_slots == nullptr && shared_lens == nullptr &&
+                    pcache::decode_supported(dtype, 128, 2 * group);
   if (pair) {
     a.pair = 1;
     a.num_kv_heads = num_kv_heads / 2;
     a.head_stride = 2 * head_stride;
   }
-  return status_of(pcache::launch_decode(a, dtype, pair ? 2 * head_size : head_size, split,
-                                         static_cast<hipStream_t>(stream)));
+  hipError_t e = pcache::launch_decode(a, dtype, pair ? 2 * head_size : head_size, split,
+                                       static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && shared_lens) e = pcache::launch_decode_prefix(a, dtype, head_size, static_cast<hipStream_t>(stream));
+  return status_of(e);
 }
 
 }  // namespace
@@ -380,6 +389,22 @@ int pc_paged_attention_decode(void* out, const void* q, const void* k_pool, cons
                      max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
                      block_size, scale, partition_size, exp_sums, max_logits, tmp_out, alibi_slopes, nullptr,
                      nullptr, 0, dtype, false, stream);
+}
+
+int pc_paged_attention_decode_prefix(const void* q, const void* k_pool, const void* v_pool, int64_t num_blocks,
+                                     int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+                                     int num_seqs, int max_seq_len, int num_q_heads, int num_kv_heads, int head_size,
+                                     int block_size, float scale, float* exp_sums, float* max_logits, float* tmp_out,
+                                     const float* alibi_slopes, const int32_t* prefix_table, int prefix_blocks,
+                                     const int32_t* shared_lens, int dtype, void* stream) {
+  if (prefix_blocks < 0 || (prefix_blocks > 0 && (!prefix_table || !shared_lens))) return PC_ERR_INVALID_ARG;
+  const bool pfx = prefix_blocks > 0;
+  return decode_impl(nullptr, q, k_pool, v_pool, num_blocks, block_stride, token_stride, head_stride, block_tables,
+                     max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_size,
+                     block_size, scale, PC_PARTITION_SIZE, exp_sums, max_logits, tmp_out, alibi_slopes, nullptr,
+                     nullptr, 0, dtype, false, stream, nullptr, nullptr, nullptr, 0, 0, pfx ? prefix_table : nullptr,
+                     pfx ? prefix_blocks : 0, pfx ? shared_lens : nullptr);
 }
 
 int pc_paged_attention_decode_fp8(void* out, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,

@@ -180,8 +180,13 @@ struct UnitLds {
 // one token).  NC = 16 > G takes several query tokens per sequence (query_start_loc):
 // column c = token tok0 + c / G, head h0 + c % G, each with its own causal limit; the
 // call covers tokens tok0 .. tok0 + 16/G - 1 and returns whether more remain.
+// PFX: a common-prefix unit (split path, NC = 16): column c is query head h0 + c % G of
+// sequence s * (16 / G) + c / G (`s` numbers the unit's group of sequences), and the
+// unit reads partition `part` of the prefix blocks a.prefix_table once for all of them.
+// A column is written when its sequence's shared tokens cover the partition completely;
+// NaN when its table does not hold the prefix blocks there (or its length is invalid).
 template <class ST, int D, int G, int NW, int STAGES, int TABLE, bool SPLIT, bool KV8, int BS, int NC = G,
-          bool FUSED = false>
+          bool FUSED = false, bool PFX = false>
 __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, NC, TABLE>& sm, int s, int kvh,
                                             int part, int tok0 = 0) {
   static_assert(ST::kBytes == 2, "16-bit storage only");
@@ -189,8 +194,10 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group of 1, 2, 4 or 8 query heads");
   static_assert(STAGES >= 2 && STAGES <= 4, "prefetch ring of 2..4 register sets");
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size 8, 16 or 32");
-  constexpr bool MT = NC != G;  // several query tokens per sequence
-  static_assert(NC == G || (NC == 16 && !SPLIT && !KV8), "multi-token units: one pass, 16-bit pools");
+  constexpr bool MC = NC != G;       // several score columns per unit
+  constexpr bool MT = MC && !PFX;    // several query tokens per sequence
+  static_assert(NC == G || (NC == 16 && !KV8 && (PFX ? SPLIT && !FUSED && BS == 16 : !SPLIT)),
+                "multi-token units: one pass, 16-bit pools; common-prefix units: split, 16-token blocks");
   // tiles per staged chunk: the chunk's block ids must fit the TABLE entries
   constexpr int CT = BS >= 16 ? TABLE * (BS / 16) : TABLE / (16 / BS);
   static_assert(!SPLIT || CT >= kPartition / kBlockTokens, "a partition's ids fit the table");
@@ -205,7 +212,7 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   constexpr int kKCpol = PCACHE_K_CPOL;
   constexpr int kVCpol = PCACHE_V_CPOL;
   // kv head pairs (a.pair): 16-bit pools, one query token, head size 128 = two heads of 64
-  constexpr bool PAIRABLE = !KV8 && !MT && !FUSED && D == 128 && G >= 2;
+  constexpr bool PAIRABLE = !KV8 && !MC && !FUSED && D == 128 && G >= 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -213,7 +220,31 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const int rg = lane >> 4;   // row group of the score tile: tokens 4*rg .. 4*rg+3
   const int col = lane & 15;  // score column: query head of the group
 
-  const int L = uniform_load(a.seq_lens, s);
+  // a common-prefix unit covers its whole partition
+  const int L = PFX ? (part + 1) * kPartition : uniform_load(a.seq_lens, s);
+  // PFX: this lane's column: sequence pcs of length pcL; pc_out = the column's
+  // (sequence, head, partition) partial is written here, pc_on = it is computed (else NaN)
+  int pcs = 0, pcL = 0;
+  bool pc_out = false, pc_on = false;
+  if constexpr (PFX) {
+    pcs = s * (NC / G) + col / G;
+    const bool in = pcs < a.num_seqs;
+    const int sl = in ? a.shared_lens[pcs] : 0;
+    pcL = in ? a.seq_lens[pcs] : 0;
+    pc_out = in && sl >= (part + 1) * kPartition;
+    bool ok = pc_out && sl <= pcL && sl <= a.prefix_blocks * BS &&
+              (int64_t)pcL <= (int64_t)a.max_partitions * kPartition && (int64_t)pcL <= (int64_t)a.max_blocks_per_seq * BS;
+    // the column's table holds the prefix blocks over this partition: the four lanes of
+    // a column check 8 of its 32 entries each
+    const int e0 = part * (kPartition / BS) + 8 * rg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      ok = ok && a.block_tables[(int64_t)pcs * a.max_blocks_per_seq + e0 + i] == a.prefix_table[e0 + i];
+    int okv = ok ? 1 : 0;
+    okv &= __shfl_xor(okv, 16);
+    okv &= __shfl_xor(okv, 32);
+    pc_on = okv != 0;
+  }
   // the sequence's query rows: q0 .. q0 + n - 1 (the decode: row s alone)
   int q0 = s, n = 1;
   if constexpr (MT) {
@@ -224,10 +255,10 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     if (tok0 >= n) return false;
   }
   constexpr int TPC = NC / G;                      // query tokens per call
-  const int C = MT ? min(n - tok0, TPC) * G : G;   // score columns in use
+  const int C = MT ? min(n - tok0, TPC) * G : NC;  // score columns in use
   const int ci = MT ? tok0 + col / G : 0;          // this lane's query token
   // the column's own position (the ALiBi origin) and last visible position
-  const int qpos = MT ? L - n + ci : L - 1;
+  const int qpos = MT ? L - n + ci : (PFX ? pcL - 1 : L - 1);
   const int lim = (MT && !a.causal) ? L - 1 : qpos;
   const int min_lim = (MT && a.causal) ? L - n + tok0 : L - 1;  // smallest over the call's columns
   // 8-bit pool: the kv head's dequantisation scales (k_scale folded into the score scale)
@@ -235,15 +266,15 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   const float vsc = KV8 ? uniform_load(a.v_scale, (int64_t)kvh * a.scale_stride) : 1.f;
   const float cs_raw = a.scale_log2 * ksc;
   const bool bad_scale = KV8 && !(cs_raw >= 0x1p-120f && cs_raw <= 0x1p120f && vsc > 0.f && vsc <= 3.4e38f);
-  bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * BS ||
-             (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition) || bad_scale || (MT && L < n);
+  bool bad = !PFX && (L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * BS ||
+                      (SPLIT && (int64_t)L > (int64_t)a.max_partitions * kPartition) || bad_scale || (MT && L < n));
   const int t_begin = SPLIT ? part * kPartition : 0;
   const int t_end = bad ? t_begin : (SPLIT ? min(L, t_begin + kPartition) : L);
   const int b_begin = t_begin / kBlockTokens;
   const int b_end = (t_end + kBlockTokens - 1) / kBlockTokens;
   const int h0 = kvh * G;
   const float cs = bad_scale ? 1.f : cs_raw;  // > 0 (scale validated on the host, k_scale here)
-  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int32_t* table = PFX ? a.prefix_table : a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
   // B operand: column `col` (zero for col >= C), dims 32*k + 8*rg .. +8 (16-bit
   // pool) or rg*(D/4) + 8*k .. +8 (8-bit pool, the order its K rows are read in)
@@ -262,12 +293,13 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
   } else {
     // keep the address inside q for the zero columns
     const int qc = col < C ? col : C - 1;
-    const int64_t qr = MT ? (int64_t)(q0 + tok0 + qc / G) : (int64_t)s;
+    const int64_t qr = MT ? (int64_t)(q0 + tok0 + qc / G) : (PFX ? (int64_t)pcs : (int64_t)s);
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (qr * a.num_q_heads + h0 + (qc & (G - 1))) * D +
                            (KV8 ? rg * (D / 4) : 8 * rg);
 #pragma unroll
     for (int k = 0; k < KS; ++k)
-      qb[k] = col < C ? *reinterpret_cast<const uint4*>(qrow + (KV8 ? 8 : 32) * k) : make_uint4(0, 0, 0, 0);
+      qb[k] = (PFX ? pc_on : col < C) ? *reinterpret_cast<const uint4*>(qrow + (KV8 ? 8 : 32) * k)
+                                       : make_uint4(0, 0, 0, 0);
   }
 
   // softmax state of head `col` (meaningful for col < G): the four row-group lanes
@@ -597,7 +629,13 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
 
   // ---- merge the waves and write ------------------------------------------------------
   const bool any_bad = bad;  // block-uniform (the table check is a block-wide vote)
-  if constexpr (MT) {
+  // PFX: columns written and columns computed, bit c (lanes 0..15 hold columns 0..15)
+  uint32_t pfx_out = 0, pfx_on = 0;
+  if constexpr (PFX) {
+    pfx_out = (uint32_t)__builtin_amdgcn_ballot_w64(pc_out) & 0xFFFFu;
+    pfx_on = (uint32_t)__builtin_amdgcn_ballot_w64(pc_on) & 0xFFFFu;
+  }
+  if constexpr (MC) {
     // 16 columns: per column, once (one thread each), the max M over the waves, each
     // wave's weight exp2((m_w - M) cs) in place of m_w, the merged sum in place of
     // wave 0's and M in place of wave 1's (both read just before)
@@ -625,8 +663,10 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     const int g = pr ? o / (D / 2) : o / D;  // score column
     const int dd = pr ? o - g * (D / 2) : o - g * D;
     const int d = pr ? dd + (g >= G / 2 ? D / 2 : 0) : dd;
+    if (PFX && !((pfx_out >> g) & 1u)) continue;  // not this unit's partial
+    const bool colbad = PFX && !((pfx_on >> g) & 1u);
     float M = -INFINITY, ls = 0.f, os = 0.f;
-    if constexpr (MT) {
+    if constexpr (MC) {
       M = sm.lw[1][g];
       ls = sm.lw[0][g];
 #pragma unroll
@@ -644,15 +684,16 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
       }
     }
     float res = M == -INFINITY ? 0.f : os / ls * vsc;
-    if (any_bad) res = NAN;
-    const int64_t sh = MT ? (int64_t)(q0 + tok0 + g / G) * a.num_q_heads + h0 + (g & (G - 1))
-                          : (int64_t)s * a.num_q_heads + h0 + g;
+    if (any_bad || colbad) res = NAN;
+    const int64_t sh = MT    ? (int64_t)(q0 + tok0 + g / G) * a.num_q_heads + h0 + (g & (G - 1))
+                       : PFX ? (int64_t)(s * (NC / G) + g / G) * a.num_q_heads + h0 + (g & (G - 1))
+                             : (int64_t)s * a.num_q_heads + h0 + g;
     if constexpr (SPLIT) {
       const int64_t sp = sh * a.max_partitions + part;
       a.tmp_out[sp * Dout + dd] = res;
       if (dd == 0) {
-        a.max_logits[sp] = any_bad ? NAN : M * (cs * kLn2);  // back to the natural-log domain
-        a.exp_sums[sp] = any_bad ? NAN : ls;
+        a.max_logits[sp] = (any_bad || colbad) ? NAN : M * (cs * kLn2);  // back to the natural-log domain
+        a.exp_sums[sp] = (any_bad || colbad) ? NAN : ls;
       }
     } else {
       static_cast<uint16_t*>(a.out)[sh * Dout + dd] = (uint16_t)to_storage<ST>(res);
@@ -683,8 +724,31 @@ void decode_split_kernel(DecodeArgs a) {
   const bool bad = L < 0 || (int64_t)L > (int64_t)a.max_blocks_per_seq * BS ||
                    (int64_t)L > (int64_t)a.max_partitions * kPartition;
   if (!bad && part * kPartition >= L) return;  // a partition past the sequence writes nothing
+  // a partition the sequence's shared prefix tokens cover completely: the prefix kernel's
+  if (a.shared_lens != nullptr && (part + 1) * kPartition <= a.prefix_blocks * BS &&
+      uniform_load(a.shared_lens, s) >= (part + 1) * kPartition)
+    return;
   constexpr int STAGES = KV8 ? PCACHE_SPLIT_STAGES_KV8 : PCACHE_SPLIT_STAGES;
   decode_unit<ST, D, G, NW, STAGES, TABLE, true, KV8, BS, G, FUSED>(a, sm, s, kvh, part);
+}
+
+// Common-prefix units of the split path: workgroup = (kv head, group of 16 / G sequences,
+// partition of the prefix), kv head fastest.  Each tile of the partition is read once for
+// the group's 16 score columns (16 / G sequences x G query heads).
+template <class ST, int D, int G>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(PCACHE_SPLIT_OCC)))
+void decode_prefix_kernel(DecodeArgs a) {
+  constexpr int NW = 4;
+  constexpr int TABLE = kPartition / kBlockTokens;
+  __shared__ UnitLds<NW, D, 16, TABLE> sm;
+  int64_t id = blockIdx.x;
+  const int kvh = (int)(id % a.num_kv_heads);
+  id /= a.num_kv_heads;
+  const int groups = (a.num_seqs + 16 / G - 1) / (16 / G);
+  const int grp = (int)(id % groups);
+  const int part = (int)(id / groups);
+  decode_unit<ST, D, G, NW, PCACHE_SPLIT_STAGES, TABLE, true, false, kBlockTokens, 16, false, true>(a, sm, grp, kvh,
+                                                                                                    part);
 }
 
 // One-pass path for many short units: one workgroup of PCACHE_GRID_WAVES waves per
@@ -943,6 +1007,39 @@ hipError_t launch_decode_multitoken(const VarlenArgs& v, int dtype, int head_siz
     case 1128: return launch_multitoken_group<F16, 128>(a, stream);
     case 2064: return launch_multitoken_group<BF16, 64>(a, stream);
     case 2128: return launch_multitoken_group<BF16, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class ST, int D, int G>
+hipError_t launch_prefix_typed(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t pp = (int64_t)a.prefix_blocks * kBlockTokens / kPartition;  // partitions the prefix fills
+  const int64_t parts = pp < a.max_partitions ? pp : a.max_partitions;
+  const int64_t groups = (a.num_seqs + 16 / G - 1) / (16 / G);
+  const int64_t wgs = (int64_t)a.num_kv_heads * groups * parts;
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_prefix_kernel<ST, D, G>), dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class ST, int D>
+hipError_t launch_prefix_group(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_prefix_typed<ST, D, 1>(a, stream);
+    case 2: return launch_prefix_typed<ST, D, 2>(a, stream);
+    case 4: return launch_prefix_typed<ST, D, 4>(a, stream);
+    case 8: return launch_prefix_typed<ST, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_prefix(const DecodeArgs& a, int dtype, int head_size, hipStream_t stream) {
+  if (a.block_size != kBlockTokens || a.kv8 || a.pair) return hipErrorInvalidValue;
+  switch (dtype * 1000 + head_size) {
+    case 1064: return launch_prefix_group<F16, 64>(a, stream);
+    case 1128: return launch_prefix_group<F16, 128>(a, stream);
+    case 2064: return launch_prefix_group<BF16, 64>(a, stream);
+    case 2128: return launch_prefix_group<BF16, 128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -66,6 +66,13 @@ struct DecodeArgs {
   // heads each; num_kv_heads and head_stride then count pairs, q / out / partials keep
   // head size 64 (decode_mfma.hip).  0: off.
   int pair;
+  // split path with a common prefix (pc_paged_attention_decode_prefix): tokens [0,
+  // shared_lens[s]) of sequence s lie in the blocks prefix_table[0 .. prefix_blocks).
+  // The partitions those tokens cover completely are computed by the prefix kernel,
+  // several sequences per read of each tile, and skipped by the split kernel.  NULL: none.
+  const int32_t* prefix_table;
+  int prefix_blocks;
+  const int32_t* shared_lens;
 };
 
 struct VarlenArgs {
@@ -102,6 +109,9 @@ hipError_t launch_write(const WriteArgs& a, int dtype, bool vec16, hipStream_t s
 hipError_t launch_write_fp8(const WriteArgs& a, int dtype, hipStream_t stream);
 // Returns hipErrorInvalidValue for a (dtype, head_size, group) the library has no kernel for.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
+// The common-prefix units of pc_paged_attention_decode_prefix (fp16 / bf16, 16-token
+// blocks).
+hipError_t launch_decode_prefix(const DecodeArgs& a, int dtype, int head_size, hipStream_t stream);
 // 16-bit storage: q.k on the matrix cores (decode_mfma.hip).
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool split, hipStream_t stream);
 // the one-pass decode over several query tokens per request (at most 16 (token, head)

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert pc.abi_version() == 8
+    assert pc.abi_version() == 9
     assert pc.status_string(0) == "ok"
     assert "invalid" in pc.status_string(-1)
     assert "unsupported" in pc.status_string(-2)

@@ -217,6 +217,14 @@ class Workload:
         sh = np.minimum(self.prefix_blocks, np.maximum(nb - 1, 0)) * self.block_size
         return np.minimum(sh, self.seq_lens).astype(np.int32)
 
+    def prefix_table(self) -> np.ndarray:
+        """The shared prefix's physical blocks in token order (empty without a prefix): the
+        first prefix_blocks entries of a sequence that shares them all."""
+        if not self.prefix_blocks:
+            return np.zeros(0, np.int32)
+        owner = int(np.argmax(self.shared_lens()))
+        return np.ascontiguousarray(self.block_tables[owner, :self.prefix_blocks], np.int32)
+
     # ----- memory images ---------------------------------------------------------
     def nan_pool(self) -> np.ndarray:
         """One pool buffer (element bits) filled with the quiet-NaN pattern (0x7F for E4M3)."""
