@@ -776,10 +776,19 @@ def bench_plan_grid(args):
                     def single(i):
                         pc.paged_attention_decode(out, q, k_pool, v_pool, tables[i % sets], sl, max_len, **lay)
 
+                    if args.grid_prefix:  # the split path given the sharing: each shared tile read once
+                        shl = torch.from_numpy(grid_shared_lens(L, args.grid_prefix, B)).cuda()
+                        pts = [t[int(np.argmax(shb)), :int(shb.max())].contiguous() for t in tables]
+
                     def split(i):
-                        pc.paged_attention_decode(None, q, k_pool, v_pool, tables[i % sets], sl, max_len,
-                                                  partition_size=pc.PARTITION_SIZE, exp_sums=es, max_logits=ml,
-                                                  tmp_out=tmp, **lay)
+                        if args.grid_prefix:
+                            pc.paged_attention_decode_prefix(q, k_pool, v_pool, tables[i % sets], sl, max_len,
+                                                             exp_sums=es, max_logits=ml, tmp_out=tmp,
+                                                             prefix_table=pts[i % sets], shared_lens=shl, **lay)
+                        else:
+                            pc.paged_attention_decode(None, q, k_pool, v_pool, tables[i % sets], sl, max_len,
+                                                      partition_size=pc.PARTITION_SIZE, exp_sums=es, max_logits=ml,
+                                                      tmp_out=tmp, **lay)
                         pc.paged_attention_reduce(out, es, ml, tmp, sl)
 
                     n = max(3, min(30, int(5000 // max(1, kv >> 20))))  # about 5 GB read per path

@@ -188,8 +188,9 @@ bool onepass_grid(int64_t units, int max_seq_len, int compute_units) {
 namespace {
 
 // Estimated launch time (us) of each decode path for a batch, from a model fitted to
-// measurements of the three kernels on MI355X: 194 batch shapes, GQA 32/8 and MHA
-// 32/32, head size 128, bf16, 16-token blocks.
+// measurements of the three kernels on MI355X: 218 batch shapes (24 of them with a
+// shared 1024-token prefix), GQA 32/8 and MHA 32/32, head size 128, bf16, 16-token
+// blocks; the split path's constants apart for MHA (its 2-wave workgroups) and GQA.
 //   * persistent one pass: each workgroup's units under the kernel's own deal (turn 0
 //     in index order, then sequences ranked longest first and dealt in snake order),
 //     each unit costing its bytes plus a fixed equivalent; the workgroups stream
@@ -201,9 +202,10 @@ namespace {
 //     number of busy workgroups; the split path adds its reduce.
 // Tokens in blocks that several sequences of the batch read (a shared prefix) come
 // partly from cache: each counts as a fraction of a token read from HBM, fitted per
-// kernel on batches with a shared 1024-token prefix (24 more measured shapes; the grid
-// kernel's on those the one-pass rule gives it): 0.60 persistent, 0.52 grid, 0.46 split
-// (which runs every sequence's first partitions side by side).
+// kernel on batches with a shared 1024-token prefix (24 more measured shapes, each
+// kernel's on the shapes it runs): 0.60 persistent, 0.54 grid.  Given the sharing, the
+// split path runs pc_paged_attention_decode_prefix; its model is in
+// est_per_unit_workgroups.
 struct Batch {
   const int32_t* lens;
   const int32_t* shared;     // per sequence: leading tokens in blocks other sequences also read (or NULL)
@@ -218,7 +220,7 @@ double unit_bytes(const Batch& b, int s, int t0, int t1, double lam) {  // token
 }
 
 double est_persistent(const Batch& b) {
-  constexpr double R0 = 54.58e3, Bw = 12812e3, o1 = 71.2e3, c1 = 3.21;  // bytes/us, bytes, us
+  constexpr double R0 = 54.75e3, Bw = 12557e3, o1 = 69.2e3, c1 = 3.39;  // bytes/us, bytes, us
   const int H = b.units_per_seq, S = b.S;
   const int64_t U = (int64_t)S * H, W = (int64_t)b.cus * b.wgs_per_cu;
   std::vector<double> load((size_t)W, 0.0);
@@ -269,18 +271,29 @@ double est_persistent(const Batch& b) {
   return t + c1;
 }
 
-// grid one pass (split = false) or split (split = true)
+// grid one pass (split = false) or split (split = true).  On the split path a batch with
+// shared prefix tokens is taken to run pc_paged_attention_decode_prefix: the partitions
+// its shared tokens cover completely leave the split kernel for the prefix kernel.
 double est_per_unit_workgroups(const Batch& b, bool split) {
-  const double BW = split ? 6345e3 : 5840e3, R = split ? 1304e3 : 831e3, t0 = split ? 1.82 : 0.0,
-               c = split ? 9.40 : 3.99, R1 = split ? 44.65e3 : 50.84e3, B1 = split ? 1e12 : 42445e3;
-  const double lam = split ? 0.46 : 0.52;
+  const bool mha = b.Hq == b.units_per_seq;  // one query head per kv head: 2-wave split workgroups
+  struct K { double BW, R, t0, c, R1, B1, rr; };
+  constexpr K kGrid{5792e3, 764.2e3, 0.0, 4.10, 50.98e3, 43898e3, 0.0};
+  constexpr K kSplitMha{6233e3, 5734e3, 4.87, 9.75, 117.3e3, 1e13, 0.557e-3};
+  constexpr K kSplitGqa{6235e3, 5883e3, 3.25, 11.16, 100.1e3, 1e13, 0.416e-3};
+  const K& k = !split ? kGrid : mha ? kSplitMha : kSplitGqa;
+  const bool pfx = split && b.shared != nullptr;
+  // shared tokens: in a partition they cover completely, the prefix kernel's (pfx);
+  // elsewhere a fraction of an HBM token
+  const double lam = !split ? 0.54 : !pfx ? 0.46 : mha ? 0.55 : 1.0;
   double total = 0.0, bmax = 0.0;
   int64_t n = 0;
-  int lmax = 0;
+  int lmax = 0, shmax = 0;
   for (int s = 0; s < b.S; ++s) {
     const int L = std::max(b.lens[s], 0);
+    const int sh = b.shared ? b.shared[s] : 0;
     const int step = split ? PC_PARTITION_SIZE : std::max(L, 1);
     for (int t0 = 0; t0 < L; t0 += step) {  // the sequence's units (its partitions on the split path)
+      if (pfx && sh >= t0 + PC_PARTITION_SIZE) continue;
       const double x = unit_bytes(b, s, t0, std::min(L, t0 + step), lam);
       total += x * b.units_per_seq;
       bmax = std::max(bmax, x);
@@ -288,11 +301,19 @@ double est_per_unit_workgroups(const Batch& b, bool split) {
     }
     if (!split && L == 0) n += b.units_per_seq;
     lmax = std::max(lmax, L);
+    shmax = std::max(shmax, sh);
   }
-  const double slots = 3.0 * b.cus;
-  const double r1 = 1.0 / (1.0 / R1 + std::min((double)n, slots) / B1);
-  double t = std::max({total / BW, (n * t0 + total / R) / slots, bmax / r1 + t0}) + c;
-  if (split) t += 0.63e-3 * b.S * b.Hq * ((lmax + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE);
+  const double slots = (split && mha ? 6.0 : 3.0) * b.cus;
+  const double r1 = 1.0 / (1.0 / k.R1 + std::min((double)n, slots) / k.B1);
+  double t = std::max({total / k.BW, (n * k.t0 + total / k.R) / slots, bmax / r1 + k.t0}) + k.c;
+  const int parts = (lmax + PC_PARTITION_SIZE - 1) / PC_PARTITION_SIZE;
+  if (split) t += k.rr * b.S * b.Hq * parts;
+  if (pfx) {  // the prefix kernel: one workgroup per (kv head, 16 / G sequences, covered partition)
+    const int G = b.Hq / b.units_per_seq;
+    const int64_t units = (int64_t)b.units_per_seq * ((b.S + 16 / G - 1) / (16 / G)) *
+                          std::min(shmax / PC_PARTITION_SIZE, parts);
+    if (units > 0) t += (mha ? 0.0 : 0.287) * units * PC_PARTITION_SIZE * b.tok_bytes / k.BW + (mha ? 15.2 : 3.91);
+  }
   return t;
 }
 
