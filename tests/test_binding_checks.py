@@ -91,3 +91,37 @@ def test_public_calls_refuse_mismatched_shapes():
     with pytest.raises(ValueError):  # the reduce's out must match the partials
         pc.paged_attention_reduce(out[:1], es, es, tmp, sl)
     torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_prefix_and_noalloc_calls_refuse_mismatched_shapes():
+    import paged_kv_cache_reshape_amd as pc
+    dev = "cuda"
+    S, Hq, Hkv, D, nb = 2, 8, 2, 64, 40
+    lay = dict(num_blocks=nb, block_stride=Hkv * 16 * D, token_stride=D, head_stride=16 * D, block_size=16)
+    pool = torch.zeros(nb * Hkv * 16 * D, dtype=torch.bfloat16, device=dev)
+    q = torch.zeros(S, Hq, D, dtype=torch.bfloat16, device=dev)
+    bt = torch.arange(S * 20, dtype=torch.int32, device=dev).reshape(S, 20) % nb
+    bt[1, :16] = bt[0, :16]  # the first 16 blocks shared
+    sl = torch.full((S,), 300, dtype=torch.int32, device=dev)
+    P = 1
+    es, ml, tmp = (torch.empty(S, Hq, P, device=dev), torch.empty(S, Hq, P, device=dev),
+                   torch.empty(S, Hq, P, D, device=dev))
+    pt = bt[0, :16].contiguous()
+    shared = torch.full((S,), 256, dtype=torch.int32, device=dev)
+    kw = dict(num_kv_heads=Hkv, scale=0.125, exp_sums=es, max_logits=ml, tmp_out=tmp, **lay)
+    pc.paged_attention_decode_prefix(q, pool, pool, bt, sl, 300, prefix_table=pt, shared_lens=shared, **kw)  # runs
+    with pytest.raises(ValueError):  # one shared count per sequence
+        pc.paged_attention_decode_prefix(q, pool, pool, bt, sl, 300, prefix_table=pt, shared_lens=shared[:1], **kw)
+    with pytest.raises(ValueError):  # block ids are int32
+        pc.paged_attention_decode_prefix(q, pool, pool, bt, sl, 300, prefix_table=pt.long(), shared_lens=shared, **kw)
+    with pytest.raises(ValueError):  # partials sized for the decode's partitions
+        pc.paged_attention_decode_prefix(q, pool, pool, bt, sl, 600, prefix_table=pt, shared_lens=shared, **kw)
+    out = torch.empty_like(q)
+    nkw = dict(num_kv_heads=Hkv, scale=0.125, **lay)
+    pc.paged_attention_split_noalloc(out, q, pool, pool, bt, sl, 300, **nkw)  # runs
+    with pytest.raises(ValueError):
+        pc.paged_attention_split_noalloc(out[:1], q, pool, pool, bt, sl, 300, **nkw)
+    with pytest.raises(ValueError):
+        pc.paged_attention_split_noalloc(out, q, pool[:-8], pool, bt, sl, 300, **nkw)
+    torch.cuda.synchronize()
