@@ -412,9 +412,11 @@ int pc_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int
  *                       (a shared prefix, "PagedAttention kernel: paged KV cache & block
  *                       tables", section Interviewer follow-ups: sequences sharing a
  *                       prefix point at the same physical blocks); 0 <= shared_lens[s] <=
- *                       seq_lens[s].  Shared tokens come partly from cache, the more so on
- *                       the split path, which reads every sequence's first partitions side
- *                       by side.
+ *                       seq_lens[s].  Shared tokens come partly from cache on the one-pass
+ *                       path; given them, the split estimate is for
+ *                       pc_paged_attention_decode_prefix (the partitions they cover
+ *                       completely read once for many sequences), the path a caller that
+ *                       knows its sharing runs.
  *   head_stride         the pool's head_stride in elements (the decode computes pairs of
  *                       kv heads together when head_size is 64 and the heads of a token
  *                       are adjacent; the plan accounts for it)
