@@ -254,3 +254,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _native.abi_version()
+
+
+def prototypes():
+    """{name: number of parameters} of every function prototype in include/pc.h."""
+    text = open(os.path.join(REPO, "include", "pc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)  # comments
+    out = {}
+    for m in re.finditer(r"\b(?:int|const char\s*\*)\s*(pc_[a-z_0-9]+)\s*\(([^)]*)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(1)] = len(params)
+    return out
+
+
+def test_binding_argtypes_match_the_header(lib):
+    """Each prototype's parameter count equals the binding's ctypes argtypes: a signature
+    change in the header cannot leave the binding passing the old argument list."""
+    protos = prototypes()
+    assert set(protos) == set(declared_symbols())
+    for name, n in protos.items():
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None, f"{name}: no argtypes in the binding"
+        assert len(fn.argtypes) == n, f"{name}: header {n} parameters, binding {len(fn.argtypes)}"
