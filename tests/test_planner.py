@@ -7,6 +7,7 @@ that batch, or the split path with its reduce.  CPU only: the planner is host co
 import os
 import re
 
+import pytest
 import torch
 
 import bench
@@ -91,3 +92,14 @@ def test_planner_on_the_five_workloads():
                                                  wl.head_stride, dt[wl.dtype], shared_lens=wl.shared_lens())
         faster_split = t_split < t_one
         assert bool(ps) == faster_split, (name, ps, t_one, t_split)
+
+
+def test_plan_lens_refuses_inconsistent_shared_counts():
+    lens = [600, 1100]
+    with pytest.raises(pc.PagedCacheError):  # more shared tokens than the sequence has
+        pc.paged_attention_plan_lens(lens, 32, 8, 128, 16 * 128, torch.bfloat16, shared_lens=[700, 1024])
+    with pytest.raises(pc.PagedCacheError):
+        pc.paged_attention_plan_lens(lens, 32, 8, 128, 16 * 128, torch.bfloat16, shared_lens=[-16, 0])
+    with pytest.raises(ValueError):  # one entry per sequence
+        pc.paged_attention_plan_lens(lens, 32, 8, 128, 16 * 128, torch.bfloat16, shared_lens=[0])
+    pc.paged_attention_plan_lens(lens, 32, 8, 128, 16 * 128, torch.bfloat16, shared_lens=[592, 1024])

@@ -143,3 +143,35 @@ def test_noalloc_refuses_what_does_not_fit():
     pc.paged_attention_split_noalloc(out, q, pool, pool, tables, lens, 60 * 512, **lay)
     torch.cuda.synchronize()
     assert torch.equal(out, torch.zeros_like(out))  # q = 0 and K = V = 0 everywhere: zeros
+
+
+def test_noalloc_under_graph_capture():
+    """The entry point's reason to exist: it can be recorded into a HIP graph (it allocates
+    nothing and enqueues only kernels).  The graph is replayed several times with eager
+    work and synchronisations between the replays; every replay equals the eager call."""
+    wl = custom(75, "bf16", 16, 4, 128, [1, 300, 513, 1400, 2000], layout="hnd")
+    pool, inp = gh.filled_pool(wl), gh.DecodeInputs(wl)
+    ref = noalloc(pool, inp)  # eager (also the device's first call, outside the capture)
+    torch.cuda.synchronize()
+    out = torch.full_like(inp.q, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the capture stream outside the graph
+        pc.paged_attention_split_noalloc(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens,
+                                         inp.max_seq_len, num_kv_heads=wl.num_kv_heads, scale=float(wl.scale),
+                                         **pool.layout_kwargs())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pc.paged_attention_split_noalloc(out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens,
+                                         inp.max_seq_len, num_kv_heads=wl.num_kv_heads, scale=float(wl.scale),
+                                         **pool.layout_kwargs())
+    for r in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_same_bits(out, ref, f"graph replay {r}")
+        noalloc(pool, inp)  # eager work on the same buffer between replays
+        torch.cuda.synchronize()
