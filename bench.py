@@ -27,6 +27,11 @@ stream over a run of back-to-back decode launches (rotating over the pool copies
 one event pair around the run, so the events' own dispatch cost is spread over the
 run); the per-launch event pairs inside the timed steps are reported beside it
 (``decode_kernel_us``, with median and p10/p90), and include one dispatch each.
+
+Beside the headline step the same line carries, each timed the same way:
+``other_configs`` (the other decode workloads on their planned paths) and
+``other_paths`` (decode over an 8-bit cache on the headline and long-context
+workloads, a speculative-decode step and a chunked-prefill step).
 """
 
 from __future__ import annotations
@@ -70,6 +75,10 @@ def parse():
     ap.add_argument("--other-configs", default="2,3,4",
                     help="workloads also timed on their planned path and reported under other_configs "
                          "(comma list; '' for none)")
+    ap.add_argument("--other-paths", default="fp8:1,fp8:3,spec,prefill",
+                    help="other paths also timed and reported under other_paths (comma list; '' for none): "
+                         "fp8:N = workload N over an E4M3 cache, spec = speculative decode (4 query tokens per "
+                         "request), prefill = chunked prefill (512-token chunks)")
     ap.add_argument("--read-peak-gib", type=int, default=4,
                     help="GiB read by the streaming-read yardstick (0: skip it)")
     ap.add_argument("--plan-grid", action="store_true",
@@ -192,17 +201,21 @@ def measure_read_peak(torch, pc, gib: int, reps: int = 10):
             "kernel": "stream_read_kernel (pc_stream_read)"}
 
 
-def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = False):
+def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = False, kv: str = "native"):
     """One workload on the path the planner picks: the whole step (write, plan, decode
     and, on the split path, the reduce) by wall clock, and the decode, the reduce and the
-    two together by HIP events around back-to-back launches (pool copies rotating)."""
+    two together by HIP events around back-to-back launches (pool copies rotating).
+    ``kv="fp8"``: the same workload over an E4M3 cache with per-kv-head scales."""
     import torch
     import gpu_harness as gh
     import paged_kv_cache_reshape_amd as pc
-    from workloads import make_config
+    from workloads import fp8_variant, make_config
 
-    print(f"[bench] other workload {idx}: generating", file=sys.stderr, flush=True)
+    print(f"[bench] other workload {idx} ({kv} cache): generating", file=sys.stderr, flush=True)
     wl = make_config(idx)
+    fp8 = kv == "fp8"
+    if fp8:
+        wl = fp8_variant(wl)
     S, Hq, D = wl.q.shape
     per_copy = (2 if wl.layout != "combined" else 1) * wl.pool_elems * wl.kv_esize
     copies = max(1, min(8, -(-(1 << 30) // max(1, wl.kv_bytes())) + 1))
@@ -215,13 +228,13 @@ def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = Fal
     msl = inp.max_seq_len
     dt = gh.TORCH_DT[wl.dtype]
     ps, P, _ = pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, dt,
-                                    shared_lens=wl.shared_lens())
+                                            kv_fp8=fp8, shared_lens=wl.shared_lens())
     kw = {}
     if ps:
         kw = dict(partition_size=ps, exp_sums=torch.empty((S, Hq, P), device="cuda"),
                   max_logits=torch.empty((S, Hq, P), device="cuda"), tmp_out=torch.empty((S, Hq, P, D), device="cuda"))
     stream = torch.cuda.current_stream()
-    use_prefix = bool(ps and wl.prefix_blocks and not no_prefix_path)
+    use_prefix = bool(ps and wl.prefix_blocks and not fp8 and not no_prefix_path)
     if use_prefix:
         pkw = dict(exp_sums=kw["exp_sums"], max_logits=kw["max_logits"], tmp_out=kw["tmp_out"],
                    prefix_table=torch.from_numpy(wl.prefix_table()).cuda(),
@@ -229,6 +242,11 @@ def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = Fal
 
     def decode(i):
         pool = pools[i % copies]
+        if fp8:
+            pc.paged_attention_decode_fp8(None if ps else out, inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens,
+                                          msl, pool.k_scale, pool.v_scale, num_kv_heads=wl.num_kv_heads,
+                                          scale=float(wl.scale), **pool.layout_kwargs(), **pool.scale_kwargs(), **kw)
+            return
         if use_prefix:
             pc.paged_attention_decode_prefix(inp.q, pool.k, pool.v, inp.block_tables, inp.seq_lens, msl,
                                              num_kv_heads=wl.num_kv_heads, scale=float(wl.scale), **pkw,
@@ -247,9 +265,13 @@ def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = Fal
 
     def step(i):
         pool = pools[i % copies]
-        pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **pool.layout_kwargs())
+        if fp8:
+            pc.reshape_and_cache_fp8(key, value, pool.k, pool.v, slots, pool.k_scale, pool.v_scale,
+                                     **pool.layout_kwargs(), **pool.scale_kwargs())
+        else:
+            pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **pool.layout_kwargs())
         pc.paged_attention_plan_lens(wl.seq_lens, Hq, wl.num_kv_heads, D, wl.head_stride, dt,
-                                    shared_lens=wl.shared_lens())
+                                     kv_fp8=fp8, shared_lens=wl.shared_lens())
         call(i)
 
     def batched(fn, n):
@@ -278,6 +300,7 @@ def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = Fal
     rec = {"workload": wl.name, "path": ("split (shared prefix)" if use_prefix else "split") if ps else "single",
            "num_seqs": S, "num_q_heads": Hq,
            "num_kv_heads": wl.num_kv_heads, "head_size": D, "dtype": wl.dtype, "layout": wl.layout,
+           "kv_cache": "fp8_e4m3 (per-kv-head scales)" if fp8 else wl.dtype,
            "effective_bytes_per_step": eff, "us_per_step": round(step_us, 2),
            "tokens_per_s": round(S / (step_us * 1e-6), 1),
            "decode_us": round(dec_us, 2), "reduce_us": round(red_us, 2) if ps else None,
@@ -549,6 +572,16 @@ def main():
     if others:
         res["other_configs"] = {str(i): measure_config(i, args.steps, args.warmup, args.no_prefix_path)
                                 for i in others if i != args.config}
+    paths = [x.strip() for x in args.other_paths.split(",") if x.strip()]
+    if paths:
+        res["other_paths"] = {}
+        for p in paths:
+            if p.startswith("fp8:"):
+                res["other_paths"][p] = measure_config(int(p[4:]), args.steps, args.warmup, kv="fp8")
+            elif p in ("spec", "prefill"):
+                res["other_paths"][p] = varlen_record(p, args.steps, args.warmup)
+            else:
+                raise SystemExit(f"--other-paths: unknown path {p!r}")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
@@ -567,9 +600,12 @@ def varlen_flops(wl, vq) -> int:
     return total * wl.num_q_heads * wl.head_size * 4
 
 
-def bench_varlen(args):
-    """Multi-token step: the write of every request's new rows, then the causal
-    attention of those rows over the whole paged history."""
+def measure_varlen(kind: str, steps: int, warmup: int, copies: int = 0):
+    """A multi-token step (``kind`` 'prefill' or 'spec'): the write of every request's new
+    rows, then the causal attention of those rows over the whole paged history; the
+    step by wall clock, the attention alone by HIP events around back-to-back launches
+    (pool copies rotating).  Returns (workload, step, seconds per step, ms per launch,
+    pool copies)."""
     import torch
     import gpu_harness as gh
     import paged_kv_cache_reshape_amd as pc
@@ -577,10 +613,10 @@ def bench_varlen(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] generating varlen workload {args.varlen}", file=sys.stderr, flush=True)
-    wl, vq = varlen_config(args.varlen)
+    print(f"[bench] generating varlen workload {kind}", file=sys.stderr, flush=True)
+    wl, vq = varlen_config(kind)
     per_copy = 2 * wl.pool_elems * wl.esize
-    copies = args.copies or max(1, min(8, -(-(1 << 30) // max(1, wl.kv_bytes())) + 1))
+    copies = copies or max(1, min(8, -(-(1 << 30) // max(1, wl.kv_bytes())) + 1))
     copies = max(1, min(copies, int(64e9 // per_copy)))
     pools = [gh.filled_pool(wl) for _ in range(copies)]
     q = gh.to_dev(vq.q, wl.dtype)
@@ -603,27 +639,55 @@ def bench_varlen(args):
         pc.reshape_and_cache(key, value, pool.k, pool.v, slots, **pool.layout_kwargs())
         attend(i)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         attend(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    kern_ms = e0.elapsed_time(e1) / args.steps
+    kern_ms = e0.elapsed_time(e1) / steps
+    del pools
+    torch.cuda.empty_cache()
+    return wl, vq, el / steps, kern_ms, copies
 
+
+def varlen_record(kind: str, steps: int, warmup: int):
+    """The compact record of a multi-token step reported beside the headline line."""
+    wl, vq, step_s, kern_ms, copies = measure_varlen(kind, steps, warmup)
+    kv = wl.kv_bytes()
+    qo = vq.total_q * wl.num_q_heads * wl.head_size * 2 * wl.esize
+    rec = {"workload": wl.name, "kernel": "varlen_lds_kernel" if kind == "prefill" else
+           "decode_onepass_kernel (16 query columns)", "query_tokens": vq.total_q,
+           "us_per_step": round(step_s * 1e6, 2), "tokens_per_s": round(vq.total_q / step_s, 1),
+           "attention_us": round(kern_ms * 1e3, 2), "pool_copies": copies,
+           "timing": "attention_us: HIP events around back-to-back launches on the launch stream; "
+                     "step = wall clock of write + attention"}
+    if kind == "prefill":
+        tf = varlen_flops(wl, vq) / (kern_ms * 1e-3) / 1e12
+        rec.update(bound="mfma", tflops=round(tf, 2), frac=round(tf / 2500.0, 4))
+    else:
+        gbs = (kv + qo) / (kern_ms * 1e-3) / 1e9
+        rec.update(bound="hbm", gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
+    return rec
+
+
+def bench_varlen(args):
+    """Multi-token step: the write of every request's new rows, then the causal
+    attention of those rows over the whole paged history."""
+    wl, vq, step_s, kern_ms, copies = measure_varlen(args.varlen, args.steps, args.warmup, args.copies)
     flops = varlen_flops(wl, vq)
     kv = wl.kv_bytes()
     qo = vq.total_q * wl.num_q_heads * wl.head_size * 2 * wl.esize
-    ms = el / args.steps * 1e3
+    ms = step_s * 1e3
     toks = vq.total_q / (ms * 1e-3)
     if args.varlen == "prefill":
         metric, unit, value = "varlen chunked-prefill attention query tokens/s", "tokens/s", toks
