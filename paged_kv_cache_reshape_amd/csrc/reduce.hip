@@ -10,8 +10,10 @@
 // m_p, l_p and 16-byte pieces of o_p for each partition p < n -- is issued at once.
 // * Many partitions per row (long sequences, few rows): reduce_kernel, a 256-thread
 //   workgroup per (sequence, query head, 32-dim slice of the output); its threads
-//   take partitions g, g + 32, ... side by side, then a block-wide max, the weights,
-//   the weighted sums and one LDS reduction over the 32 partition groups.
+//   take partitions g, g + 32, ... side by side.  Each wave keeps its own running
+//   maximum and sums (folded across its 8 partition groups with lane shuffles); the
+//   four wave states are rescaled to the common maximum once, through LDS, behind a
+//   single barrier.
 // * Few partitions per row (at most kRowsMaxParts, i.e. sequences up to 8192 tokens,
 //   typically many rows): reduce_rows_kernel, one wave per (sequence, query head).
 //   The wave's lanes form 64 / (D/4) partition groups of D/4 lanes (a float4 of the
@@ -30,19 +32,22 @@ constexpr int kReduceThreads = 256;
 constexpr int kSlice = 32;                        // output dims per workgroup
 constexpr int kCols = kSlice / 4;                 // float4 columns of a slice
 constexpr int kGroups = kReduceThreads / kCols;   // partitions summed side by side
+constexpr int kWaves = kReduceThreads / kWave;
 constexpr int kPerThread = 8;                     // partitions a thread keeps in flight at once
 
 template <class ST>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
-  __shared__ float red[kReduceThreads / kWave];
-  __shared__ __align__(16) float4 part_o[kGroups][kCols];
-  __shared__ float part_w[kGroups];
+  __shared__ __align__(16) float4 wave_o[kWaves][kCols];
+  __shared__ float wave_m[kWaves];
+  __shared__ float wave_w[kWaves];
 
   const int D = a.head_size;
   const int slices = D / kSlice;
   const int slice = blockIdx.x % slices;
   const int64_t sh = blockIdx.x / slices;  // s * num_q_heads + h
   const int s = (int)(sh / a.num_q_heads);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
   const int c = threadIdx.x % kCols;
   const int grp = threadIdx.x / kCols;
   const int L = a.seq_lens[s];
@@ -54,6 +59,8 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
   const float4* rows = reinterpret_cast<const float4*>(a.tmp_out + sh * a.max_partitions * D + slice * kSlice) + c;
   const int row4 = D / 4;
 
+  // this wave's state: M over its partitions so far (the same in every lane), and the
+  // lane's weighted sums relative to M
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.f;
   float M = -INFINITY;
@@ -70,25 +77,20 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
       l[i] = in ? es[p] : 0.f;
       t[i] = in ? rows[(int64_t)p * row4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    // the batch's max over every thread's partitions
-    float bm = -INFINITY;
+    // the batch's max over the wave's partition groups (lanes of one group hold the same m)
+    float bm = M;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) bm = fmaxf(bm, m[i]);
-    for (int off = 32; off > 0; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
-    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = bm;
-    __syncthreads();
-    float nm = M;
 #pragma unroll
-    for (int i = 0; i < kReduceThreads / kWave; ++i) nm = fmaxf(nm, red[i]);
-    __syncthreads();
+    for (int off = kCols; off < kWave; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
     // rescale what earlier batches summed to the new maximum, then add this batch
-    const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((M - nm) * kLog2e);
+    const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((M - bm) * kLog2e);
     o.x *= f;
     o.y *= f;
     o.z *= f;
     o.w *= f;
     wsum *= f;
-    M = nm;
+    M = bm;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const float wp = m[i] == -INFINITY ? 0.f : l[i] * __builtin_amdgcn_exp2f((m[i] - M) * kLog2e);
@@ -99,20 +101,39 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
       o.w = fmaf(wp, t[i].w, o.w);
     }
   }
-  part_o[grp][c] = o;
-  if (c == 0) part_w[grp] = wsum;
+  // fold the wave's partition groups (all relative to the wave's M)
+#pragma unroll
+  for (int off = kCols; off < kWave; off <<= 1) {
+    wsum += __shfl_xor(wsum, off);
+    o.x += __shfl_xor(o.x, off);
+    o.y += __shfl_xor(o.y, off);
+    o.z += __shfl_xor(o.z, off);
+    o.w += __shfl_xor(o.w, off);
+  }
+  if (lane < kCols) wave_o[wave][lane] = o;
+  if (lane == 0) {
+    wave_m[wave] = M;
+    wave_w[wave] = wsum;
+  }
   __syncthreads();
   if (threadIdx.x < kCols) {
+    float gm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) gm = fmaxf(gm, wave_m[w]);
     float4 to = make_float4(0.f, 0.f, 0.f, 0.f);
     float tw = 0.f;
-#pragma unroll 8
-    for (int g = 0; g < kGroups; ++g) {
-      const float4 v = part_o[g][threadIdx.x];
-      to.x += v.x;
-      to.y += v.y;
-      to.z += v.z;
-      to.w += v.w;
-      tw += part_w[g];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      // a wave that saw no partition (or only -inf maxima) holds zeros, or NaN sums
+      // that must still reach the output
+      const float wm = wave_m[w];
+      const float f = wm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((wm - gm) * kLog2e);
+      const float4 v = wave_o[w][threadIdx.x];
+      to.x = fmaf(f, v.x, to.x);
+      to.y = fmaf(f, v.y, to.y);
+      to.z = fmaf(f, v.z, to.z);
+      to.w = fmaf(f, v.w, to.w);
+      tw = fmaf(f, wave_w[w], tw);
     }
     const float inv = 1.f / tw;
     float r[4] = {to.x * inv, to.y * inv, to.z * inv, to.w * inv};

@@ -233,6 +233,53 @@ def test_reduce_alone(dt):
     check_attention(gh.out_f64(out), ref, dt, f"reduce alone {dt}")
 
 
+def synthetic_partials(rng, S, Hq, P, D):
+    """Seeded fp32 partials: maxima spread over about +-12 (weights from e^-24 to 1), sums
+    in [0.5, 200), outputs N(0, 1)."""
+    ml = (rng.standard_normal((S, Hq, P)) * 4.0).astype(np.float32)
+    es = rng.uniform(0.5, 200.0, (S, Hq, P)).astype(np.float32)
+    tmp = rng.standard_normal((S, Hq, P, D)).astype(np.float32)
+    return tmp, ml, es
+
+
+def reduce_on_gpu(tmp, ml, es, lens, dt):
+    S, Hq, _, D = tmp.shape
+    out = torch.empty((S, Hq, D), dtype=gh.TORCH_DT[dt], device="cuda")
+    pc.paged_attention_reduce(out, torch.from_numpy(es).cuda(), torch.from_numpy(ml).cuda(),
+                              torch.from_numpy(tmp).cuda(), torch.from_numpy(np.asarray(lens, np.int32)).cuda())
+    torch.cuda.synchronize()
+    return gh.out_f64(out)
+
+
+@pytest.mark.parametrize("dt,D,P", [("f32", 128, 40), ("bf16", 64, 300), ("f16", 96, 17)])
+def test_reduce_many_partitions(dt, D, P):
+    """More partitions per row than the one-wave rows kernel takes (and, at 300, more than
+    one 256-partition batch): rows of 0, 1, 2, about P/2 and P partitions, against the
+    oracle's merge of the same fp32 values."""
+    lens = np.array([0, 1, 512, 513, 512 * (P // 2) + 7, 512 * P, 512 * (P - 1) + 1], np.int32)
+    tmp, ml, es = synthetic_partials(np.random.default_rng(1000 + P), len(lens), 3, P, D)
+    ref = oracle.merge(tmp.astype(np.float64), ml.astype(np.float64), es.astype(np.float64), lens, 512)
+    check_attention(reduce_on_gpu(tmp, ml, es, lens, dt), ref, dt, f"reduce of {P} partitions, {dt}, D {D}")
+
+
+def test_reduce_many_partitions_nan_and_empty_partitions():
+    """A NaN element of one partial reaches only that output element; a NaN maximum, the
+    whole row; a partition with maximum -inf and sum 0 weighs nothing.  As the oracle."""
+    P, D = 40, 64
+    lens = np.array([512 * 40, 512 * 40, 512 * 39 + 100], np.int32)
+    tmp, ml, es = synthetic_partials(np.random.default_rng(77), 3, 2, P, D)
+    tmp[1, 0, 33, 5] = np.nan
+    ml[2, 1, 7] = np.nan
+    ml[0, 1, 12], es[0, 1, 12] = -np.inf, 0.0
+    ml[0, 0, 3], es[0, 0, 3] = -np.inf, 0.0
+    ref = oracle.merge(tmp.astype(np.float64), ml.astype(np.float64), es.astype(np.float64), lens, 512)
+    got = reduce_on_gpu(tmp, ml, es, lens, "f32")
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(got[1, 0, 5]) and np.isfinite(np.delete(got[1, 0], 5)).all() and np.isnan(got[2, 1]).all()
+    fin = np.isfinite(ref)
+    assert np.abs(got[fin] - ref[fin]).max() <= TOL["f32"]
+
+
 # ---------------------------------------------------------------------------------
 # invalid data: kernels turn it into NaN or a skipped write, never an out-of-range access
 # ---------------------------------------------------------------------------------
