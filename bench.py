@@ -28,10 +28,11 @@ one event pair around the run, so the events' own dispatch cost is spread over t
 run); the per-launch event pairs inside the timed steps are reported beside it
 (``decode_kernel_us``, with median and p10/p90), and include one dispatch each.
 
-Beside the headline step the same line carries, each timed the same way:
-``other_configs`` (the other decode workloads on their planned paths) and
-``other_paths`` (decode over an 8-bit cache on the headline and long-context
-workloads, a speculative-decode step and a chunked-prefill step).
+Beside the headline step the same line carries ``other_configs`` (the other decode
+workloads on their planned paths) and ``other_paths`` (decode over an 8-bit cache on
+the headline and long-context workloads, a speculative-decode step and a
+chunked-prefill step), each with its launches timed by HIP events around back-to-back
+runs; the long-context workload's records are taken first.
 """
 
 from __future__ import annotations
@@ -203,8 +204,9 @@ def measure_read_peak(torch, pc, gib: int, reps: int = 10):
 
 def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = False, kv: str = "native"):
     """One workload on the path the planner picks: the whole step (write, plan, decode
-    and, on the split path, the reduce) by wall clock, and the decode, the reduce and the
-    two together by HIP events around back-to-back launches (pool copies rotating).
+    and, on the split path, the reduce) by wall clock, and the decode alone and the call
+    (decode and reduce) by HIP events around back-to-back launches (pool copies rotating,
+    three alternating rounds of each).
     ``kv="fp8"``: the same workload over an E4M3 cache with per-kv-head scales."""
     import torch
     import gpu_harness as gh
