@@ -21,7 +21,8 @@
 //   v_mfma_f32_16x16x16_{bf16,f16}: the B operand P^T (16 tokens x 16 heads) is the
 //   score tile's own register layout after the exponential (lane l holds tokens
 //   4*(l/16) .. +3 of head l % 16), rounded to the storage type, so probabilities
-//   never move between lanes.  The A operand of tile j holds dims
+//   never move between lanes.  For bf16 a second product adds the part of each
+//   probability that rounding drops (kSplitP).  The A operand of tile j holds dims
 //   (D/16)*m + j (m < 16) of the same four tokens: lane (r, c) loads 16 (head_size
 //   128) or 8 (64) contiguous bytes of each of its four V rows (dims (D/16)*c ..)
 //   and picks element j of each with v_perm_b32.  Lane (r, c) accumulates, for
@@ -438,6 +439,9 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
     _Pragma("unroll") for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(fmaf(c[e], cs, -ref));          \
     lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);                                                       \
     const uint2 pb = make_uint2(pack2<ST>(pr[0], pr[1]), pack2<ST>(pr[2], pr[3]));                   \
+    /* bf16: the probabilities' rounding residuals, a second P^T operand */                          \
+    const uint2 pl = kSplitP<ST> ? make_uint2(residual2(pb.x, pr[0], pr[1]), residual2(pb.y, pr[2], pr[3])) \
+                                 : make_uint2(0u, 0u);                                               \
     if constexpr (KV8) {                                                                             \
       /* tiles j, j+1 (j even): bytes j, j+1 of the four rows gathered pairwise into two */         \
       /* dwords of codes, each widened into one operand dword of either tile */                      \
@@ -448,6 +452,10 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
         const uint2 xw_ = widen4<ST>(x_), yw_ = widen4<ST>(y_);                                      \
         acc[j] = mfma_pv<ST>(make_uint2(xw_.x, yw_.x), pb, acc[j]);                                  \
         acc[j + 1] = mfma_pv<ST>(make_uint2(xw_.y, yw_.y), pb, acc[j + 1]);                          \
+        if constexpr (kSplitP<ST>) {                                                                 \
+          acc[j] = mfma_pv<ST>(make_uint2(xw_.x, yw_.x), pl, acc[j]);                                \
+          acc[j + 1] = mfma_pv<ST>(make_uint2(xw_.y, yw_.y), pl, acc[j + 1]);                        \
+        }                                                                                            \
       }                                                                                              \
     } else {                                                                                         \
       _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                              \
@@ -456,6 +464,7 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs& a, UnitLds<NW, D, 
         const uint2 va = make_uint2(__builtin_amdgcn_perm(vword(vb[SL][1], j >> 1), vword(vb[SL][0], j >> 1), sel), \
                                     __builtin_amdgcn_perm(vword(vb[SL][3], j >> 1), vword(vb[SL][2], j >> 1), sel)); \
         acc[j] = mfma_pv<ST>(va, pb, acc[j]);                                                        \
+        if constexpr (kSplitP<ST>) acc[j] = mfma_pv<ST>(va, pl, acc[j]);                             \
       }                                                                                              \
     }                                                                                                \
   } while (0)

@@ -65,6 +65,24 @@ __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// bf16 probabilities enter P.V as two operands, the value rounded to bf16 and the part
+// that rounding drops (rounded to bf16 in turn), so that P.V sees each probability to
+// about 2^-16 of its size rather than bf16's 2^-8: at outputs of 2 to 4, where rounding
+// the output to bf16 already costs up to 2^-7, one rounding of the probabilities could take
+// the result past 1e-2 of the exact value.  fp16 (2^-11) keeps a single operand.
+template <class ST>
+constexpr bool kSplitP = false;
+template <>
+constexpr bool kSplitP<BF16> = true;
+
+// the residuals a - bf16(a), b - bf16(b) of a dword packed by pack2<BF16>(a, b), each
+// exact in fp32 and rounded to bf16
+__device__ __forceinline__ uint32_t residual2(uint32_t packed, float a, float b) {
+  const float ha = __builtin_bit_cast(float, packed << 16);
+  const float hb = __builtin_bit_cast(float, packed & 0xffff0000u);
+  return pack2<BF16>(a - ha, b - hb);
+}
+
 // four E4M3 codes (one dword) widened exactly to two dwords of the 16-bit type
 template <class ST>
 __device__ __forceinline__ uint2 widen4(uint32_t codes);

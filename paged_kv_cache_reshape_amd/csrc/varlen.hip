@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2
     if (vis_end - (TOK0) < kTok) { /* rows past the unit's last visible position: stale V */          \
       _Pragma("unroll") for (int e = 0; e < 4; ++e) vb[SL][e] = t0_ + e < vis_end ? vb[SL][e] : VRow{}; \
     }                                                                                                 \
-    uint2 pb[NQ];                                                                                     \
+    uint2 pb[NQ], pl[NQ];                                                                             \
     _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                  \
       f32x4_t c = {0.f, 0.f, 0.f, 0.f};                                                               \
       _Pragma("unroll") for (int k = 0; k < KS; ++k) c = mfma16<ST>(kb[SL][k], qb[q][k], c);          \
@@ -184,12 +184,17 @@ __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(2
       _Pragma("unroll") for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(fmaf(c[e], cs, -ref));         \
       lsum[q] += (pr[0] + pr[1]) + (pr[2] + pr[3]);                                                   \
       pb[q] = make_uint2(pack2<ST>(pr[0], pr[1]), pack2<ST>(pr[2], pr[3]));                           \
+      if constexpr (kSplitP<ST>)                                                                      \
+        pl[q] = make_uint2(residual2(pb[q].x, pr[0], pr[1]), residual2(pb[q].y, pr[2], pr[3]));       \
     }                                                                                                 \
     _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                  \
       const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;                                       \
       const uint2 va = make_uint2(__builtin_amdgcn_perm(vword(vb[SL][1], j >> 1), vword(vb[SL][0], j >> 1), sel), \
                                   __builtin_amdgcn_perm(vword(vb[SL][3], j >> 1), vword(vb[SL][2], j >> 1), sel)); \
-      _Pragma("unroll") for (int q = 0; q < NQ; ++q) acc[q][j] = mfma_pv<ST>(va, pb[q], acc[q][j]);   \
+      _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                \
+        acc[q][j] = mfma_pv<ST>(va, pb[q], acc[q][j]);                                                \
+        if constexpr (kSplitP<ST>) acc[q][j] = mfma_pv<ST>(va, pl[q], acc[q][j]);                     \
+      }                                                                                               \
     }                                                                                                 \
   } while (0)
 
@@ -589,7 +594,7 @@ void varlen_lds_kernel(VarlenArgs a) {
                 for (int i = 0; i < 8; ++i)
                   xs[q][i] = tA + (i < 4 ? i : kTok + i - 4) <= lim[q] ? xs[q][i] : -INFINITY;
             }
-            uint4 pb[NQ];
+            uint4 pb[NQ], pl[NQ];
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
               const float* x = xs[q];
@@ -616,6 +621,9 @@ void varlen_lds_kernel(VarlenArgs a) {
               lsum[q] += ((pr8[0] + pr8[1]) + (pr8[2] + pr8[3])) + ((pr8[4] + pr8[5]) + (pr8[6] + pr8[7]));
               pb[q] = make_uint4(pack2<ST>(pr8[0], pr8[1]), pack2<ST>(pr8[2], pr8[3]), pack2<ST>(pr8[4], pr8[5]),
                                  pack2<ST>(pr8[6], pr8[7]));
+              if constexpr (kSplitP<ST>)
+                pl[q] = make_uint4(residual2(pb[q].x, pr8[0], pr8[1]), residual2(pb[q].y, pr8[2], pr8[3]),
+                                   residual2(pb[q].z, pr8[4], pr8[5]), residual2(pb[q].w, pr8[6], pr8[7]));
             }
             // output tile j = dims 16 j .. 16 j + 15; its V^T operand (k = 8 rg + 0..3 from
             // the first tile, + 4..7 from the second) comes straight from LDS, transposed
@@ -626,7 +634,10 @@ void varlen_lds_kernel(VarlenArgs a) {
               const uint2 hi = lds_read_tr16(sb + 2 * TCH * 16 + v_rd[j]);
               const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
-              for (int q = 0; q < NQ; ++q) acc[q][j] = mfma16<ST>(va, pb[q], acc[q][j]);
+              for (int q = 0; q < NQ; ++q) {
+                acc[q][j] = mfma16<ST>(va, pb[q], acc[q][j]);
+                if constexpr (kSplitP<ST>) acc[q][j] = mfma16<ST>(va, pl[q], acc[q][j]);
+              }
             }
           }
         }

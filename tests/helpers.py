@@ -109,5 +109,7 @@ def with_abs_values(wl):
     return dataclasses.replace(wl, pre_value=wl.pre_value & ~sign, value=wl.value & ~sign)
 
 
-# unit roundoff of the 16-bit types a probability may be rounded to before P.V
-PROB_ROUNDOFF = {"bf16": 2.0 ** -9, "f16": 2.0 ** -11, "f32": 0.0}
+# relative error of a probability as P.V sees it: fp16 rounds it once (unit roundoff
+# 2^-11, an 11-bit significand); bf16 (8-bit significand, unit roundoff 2^-8) carries it
+# as the rounded value plus the rounded residual, 2^-8 of a residual of at most 2^-8
+PROB_ROUNDOFF = {"bf16": 2.0 ** -16, "f16": 2.0 ** -11, "f32": 0.0}
