@@ -202,6 +202,41 @@ def measure_read_peak(torch, pc, gib: int, reps: int = 10):
             "kernel": "stream_read_kernel (pc_stream_read)"}
 
 
+def measure_gather(torch, pc, wl, pools, inp, steps: int):
+    """The gather yardstick (pc_gather_read) over the workload's own pools and tables:
+    every K/V tile its decode reads, loads only, for both cache policies of the V loads;
+    microseconds per launch from HIP events around ``steps`` back-to-back launches
+    (pool copies rotating as for the decode)."""
+    if wl.block_size != 16:
+        return None
+    sink = torch.zeros(pc.GATHER_SINK_WORDS, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    copies = len(pools)
+
+    def one(i, pol):
+        pool = pools[i % copies]
+        kw = pool.layout_kwargs()
+        pc.gather_read(pool.k, pool.v, inp.block_tables, inp.seq_lens, inp.max_seq_len, sink,
+                       num_kv_heads=wl.num_kv_heads, head_size=wl.head_size, num_blocks=kw["num_blocks"],
+                       block_stride=kw["block_stride"], token_stride=kw["token_stride"],
+                       head_stride=kw["head_stride"], v_offset=kw.get("v_offset", 0), v_cache_policy=pol)
+
+    us = {}
+    for pol in (0, 2):
+        for i in range(3):
+            one(i, pol)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            one(i, pol)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us["nt" if pol else "default"] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+    return {"us_by_v_cache_policy": us, "us": min(us.values()), "kernel": "gather_read_kernel (pc_gather_read)",
+            "timing": "HIP events around back-to-back launches on the launch stream, pool copies rotating"}
+
+
 def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = False, kv: str = "native"):
     """One workload on the path the planner picks: the whole step (write, plan, decode
     and, on the split path, the reduce) by wall clock, and the decode alone and the call
@@ -323,6 +358,12 @@ def measure_config(idx: int, steps: int, warmup: int, no_prefix_path: bool = Fal
         uniq = wl.unique_kv_bytes() + wl.qo_bytes()
         rec.update(unique_bytes_per_step=uniq, unique_call_gbs=round(uniq / (call_us * 1e-6) / 1e9, 1),
                    unique_call_frac=round(uniq / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    g = measure_gather(torch, pc, wl, pools, inp, steps)
+    if g is not None:
+        # a plain gather of the tiles the decode reads (a shared block once per sequence
+        # that addresses it, where the shared-prefix path reads it once per group)
+        g["decode_us_over_gather_us"] = round(dec_us / g["us"], 3)
+        rec["gather"] = g
     del pools
     torch.cuda.empty_cache()
     return rec
@@ -569,6 +610,14 @@ def main():
                                "gbs_decode_launch": round(uniq / (dec_b * 1e-3) / 1e9, 2),
                                "frac_decode_launch": round(uniq / (dec_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                "note": "distinct physical K/V rows read (the shared prefix once) plus q and out"}
+    print("[bench] gather yardstick", file=sys.stderr, flush=True)
+    g = measure_gather(torch, pc, wl, pools, inp, args.steps)
+    if g is not None:
+        # the same algorithmic bytes over a plain gather's launch time: above 1 in
+        # frac_of_measured_gather, the decode reads its tiles faster than a loads-only gather
+        res["gather_read"] = g
+        res["roofline"]["measured_gather"] = round(launch_bytes / (g["us"] * 1e-6) / 1e9, 1)
+        res["roofline"]["frac_of_measured_gather"] = round(g["us"] / (dec_b * 1e3), 4)
     del pools
     torch.cuda.empty_cache()
     if args.read_peak_gib > 0:

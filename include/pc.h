@@ -450,6 +450,36 @@ int pc_paged_attention_plan_lens(const int32_t *seq_lens, const int32_t *shared_
 int pc_stream_read(const void *src, int64_t bytes, uint32_t *sink, int num_workgroups, int cache_policy,
                    void *stream);
 
+/*
+ * pc_gather_read -- measurement aid: read the K and V tiles a decode of this batch reads,
+ * and nothing else.
+ *
+ * Not a step of the path.  The decode's HBM stream ("vLLM 源码完全拆解（七）", section
+ * 性能模型) is not one contiguous read but a gather through the block table ("How vLLM
+ * CUDA Kernels Write and Read the Paged KV Cache", section "Reading logical blocks
+ * during attention"): for every sequence s, kv head h and block j < ceil(seq_lens[s] /
+ * 16), the 16 token rows of head h in block block_tables[s, j], from the K pool and from
+ * the V pool.  This call loads exactly those tiles (16-byte loads, workgroups dealt as
+ * the split decode deals its partitions) and folds the words with XOR, so a decode's
+ * rate can be set against a plain gather of its own bytes.  With sink zeroed first,
+ * the XOR of sink's 4096 entries afterwards is the XOR of every 32-bit word read.
+ *
+ *   k_pool, v_pool, num_blocks, block_stride, token_stride, head_stride, block_tables,
+ *   max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_kv_heads, head_size:
+ *                   as for pc_paged_attention_decode (16-token blocks; element strides)
+ *   element_bytes   1, 2 or 4 (the pool's element size); head_size * element_bytes must
+ *                   be 128, 256 or 512
+ *   sink            device uint32 [4096]
+ *   v_cache_policy  0 (default) or 2 (non-temporal hint on the V loads, as the decode's)
+ * A sequence whose length exceeds its table row or max_seq_len, and a block id outside
+ * [0, num_blocks), read nothing.  Returns PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED
+ * or PC_ERR_LAUNCH.
+ */
+int pc_gather_read(const void *k_pool, const void *v_pool, int64_t num_blocks, int64_t block_stride,
+                   int64_t token_stride, int64_t head_stride, const int32_t *block_tables, int max_blocks_per_seq,
+                   const int32_t *seq_lens, int num_seqs, int max_seq_len, int num_kv_heads, int head_size,
+                   int element_bytes, uint32_t *sink, int v_cache_policy, void *stream);
+
 /* Bytes of the device buffer behind pc_paged_attention_split_noalloc, per GPU. */
 #define PC_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 

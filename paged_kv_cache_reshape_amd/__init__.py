@@ -18,15 +18,19 @@ The compute lives in ``libpcache.so`` (hand-written HIP for gfx950, C ABI in
 * ``paged_attention_split_noalloc`` -- the split decode and its reduce with the
   partials in the library's own device buffer, for callers that cannot allocate;
 * ``stream_read``              -- measurement aid: one plain read of a buffer (the
-  yardstick the benchmark quotes the decode's HBM rate against).
+  yardstick the benchmark quotes the decode's HBM rate against);
+* ``gather_read``              -- measurement aid: the K/V tiles a decode of a batch
+  reads, loads only.
 """
 
 from ._native import (  # noqa: F401
+    GATHER_SINK_WORDS,
     LIB_PATH,
     NOALLOC_SCRATCH_BYTES,
     PARTITION_SIZE,
     PagedCacheError,
     abi_version,
+    gather_read,
     library,
     paged_attention_decode,
     paged_attention_decode_prefix,

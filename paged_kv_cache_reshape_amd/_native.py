@@ -76,6 +76,8 @@ def _load():
                                                          i32, i32, i32, i32, f32, vp, i32, vp]
         lib.pc_stream_read.restype = i32
         lib.pc_stream_read.argtypes = [vp, i64, vp, i32, i32, vp]
+        lib.pc_gather_read.restype = i32
+        lib.pc_gather_read.argtypes = [vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, i32, i32, i32, i32, vp, i32, vp]
         _lib = lib
     return _lib
 
@@ -550,3 +552,35 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, *, cache_policy: int = 0,
     st = _load().pc_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), sink.numel(),
                                 cache_policy, _stream(src, stream))
     _check("pc_stream_read", st)
+
+
+GATHER_SINK_WORDS = 4096
+
+
+def gather_read(k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                max_seq_len: int, sink: torch.Tensor, *, num_kv_heads: int, head_size: int, num_blocks: int,
+                block_stride: int, token_stride: int, head_stride: int, block_size: int = 16, v_offset: int = 0,
+                v_cache_policy: int = 0, stream=None) -> None:
+    """Measurement aid: read every K/V tile a decode of this batch reads, loads only
+    (pc_gather_read).  ``sink``: a zeroed 32-bit integer tensor of 4096 entries; the XOR of
+    its entries afterwards is the XOR of every 32-bit word read."""
+    _same_device(k_pool, v_pool, block_tables, seq_lens, sink)
+    if block_size != 16:
+        raise ValueError("pc_gather_read reads 16-token blocks")
+    if sink.dtype not in (torch.int32, torch.uint32) or not sink.is_contiguous() or sink.numel() != GATHER_SINK_WORDS:
+        raise ValueError(f"sink must be a contiguous 32-bit integer tensor of {GATHER_SINK_WORDS} entries")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous int32 [S, max_blocks_per_seq]")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [S]")
+    if k_pool.dtype != v_pool.dtype:
+        raise ValueError("k_pool and v_pool must share one element type")
+    S = block_tables.shape[0]
+    _check_seq_inputs(S, block_tables, seq_lens)
+    _check_pool(k_pool, v_pool, v_offset, num_blocks, block_stride, token_stride, head_stride, block_size,
+                num_kv_heads, head_size)
+    st = _load().pc_gather_read(_ptr(k_pool), _ptr(v_pool, v_offset), num_blocks, block_stride, token_stride,
+                                head_stride, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S,
+                                max_seq_len, num_kv_heads, head_size, k_pool.element_size(), _ptr(sink),
+                                v_cache_policy, _stream(k_pool, stream))
+    _check("pc_gather_read", st)

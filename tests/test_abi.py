@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert pc.abi_version() == 9
+    assert pc.abi_version() == 10
     assert pc.status_string(0) == "ok"
     assert "invalid" in pc.status_string(-1)
     assert "unsupported" in pc.status_string(-2)
@@ -225,6 +225,26 @@ def test_stream_read_validation(lib):
     assert f(FAKE, 1 << 20, FAKE, 64, 1, None) == -1  # cache policy is 0 or 2
     assert f(FAKE, (1 << 20) + 8, FAKE, 64, 0, None) == -2  # not whole 16-byte vectors
     assert f(FAKE, 1 << 40, FAKE, 1, 0, None) == -2  # a chunk past 32-bit offsets
+
+
+def _gather(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, nb=64, bs=8 * 16 * 128, ts=128, hs=16 * 128, bt=FAKE, W=4, sl=FAKE, S=2, msl=64, Hkv=8,
+             D=128, eb=2, sink=FAKE, pol=0)
+    a.update(kw)
+    return lib.pc_gather_read(a["k"], a["v"], a["nb"], a["bs"], a["ts"], a["hs"], a["bt"], a["W"], a["sl"], a["S"],
+                              a["msl"], a["Hkv"], a["D"], a["eb"], a["sink"], a["pol"], None)
+
+
+def test_gather_read_validation(lib):
+    assert _gather(lib, S=0) == 0 and _gather(lib, msl=0) == 0  # nothing to read: no launch
+    assert _gather(lib, eb=3) == -1  # element size 1, 2 or 4
+    assert _gather(lib, pol=1) == -1  # cache policy 0 or 2
+    assert _gather(lib, msl=65) == -1  # longer than a table row holds
+    assert _gather(lib, sink=None) == -1
+    assert _gather(lib, nb=0) == -1
+    assert _gather(lib, D=96) == -2  # a row of 192 bytes
+    assert _gather(lib, ts=127, hs=16 * 127) == -2  # strides not whole 16-byte vectors
+    assert _gather(lib, ts=1 << 27) == -2  # a tile past 32-bit offsets
 
 
 def test_plan_choices():
