@@ -27,6 +27,11 @@ stream over a run of back-to-back decode launches (rotating over the pool copies
 one event pair around the run, so the events' own dispatch cost is spread over the
 run); the per-launch event pairs inside the timed steps are reported beside it
 (``decode_kernel_us``, with median and p10/p90), and include one dispatch each.
+Two yardsticks sit beside it: ``read_peak`` (pc_stream_read, one plain read of a 4 GiB
+buffer; ``roofline.measured_read_peak``) and ``gather_read`` (pc_gather_read, a
+loads-only gather of exactly the decode's K/V tiles from the same pools;
+``roofline.measured_gather``, and ``frac_of_measured_gather`` = the gather's launch time
+over the decode's).
 
 Beside the headline step the same line carries ``other_configs`` (the other decode
 workloads on their planned paths) and ``other_paths`` (decode over an 8-bit cache on
